@@ -1,0 +1,83 @@
+"""Pure-Python scalar-loop MLA layer for tiny dimensions. TEST INFRASTRUCTURE ONLY.
+
+An independent restatement of the same equations as `oracle.mla` (no numpy, no shared code),
+used to pin the vectorised oracle by brute force on tiny shapes (hidden 8, ranks 4-6, 2 heads,
+head widths 2-4, a handful of tokens). Every loop follows one equation of the pages:
+
+  "Key-value latent" page, mla-init / mla-kv / rmsnorm excerpts;
+  "Key content up-projection" page, code excerpt (assembly, scores, mask, softmax, P.V);
+  dense-block attention page, mla-output excerpt (flatten heads, o_proj).
+"""
+from __future__ import annotations
+
+import math
+
+
+def _matvec(w, x):
+    """y[o] = sum_i w[o][i] * x[i]  (nn.Linear, [out, in] weight, no bias)."""
+    return [sum(w[o][i] * x[i] for i in range(len(x))) for o in range(len(w))]
+
+
+def _rms(x, g, eps):
+    ms = sum(v * v for v in x) / len(x)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [g[i] * x[i] * r for i in range(len(x))]
+
+
+def _rotate(v, p, theta):
+    """Pairs (2i, 2i+1) rotated by angle p * theta^(-2i/len(v))."""
+    out = list(v)
+    n = len(v)
+    for i in range(n // 2):
+        ang = p * theta ** (-2.0 * i / n)
+        c, s = math.cos(ang), math.sin(ang)
+        a, b = v[2 * i], v[2 * i + 1]
+        out[2 * i] = a * c - b * s
+        out[2 * i + 1] = a * s + b * c
+    return out
+
+
+def forward(x, w, dims, eps, theta, sigma, cache_entries=None):
+    """x: list of T token vectors; w: dict of nested lists; dims: dict with keys
+    q_lora, kv_lora, heads, nope, rope, v. cache_entries: list of (c_hat, k_pe) for positions
+    0..L0-1. Returns (y rows, new entries)."""
+    heads, nope, rope, vd = dims["heads"], dims["nope"], dims["rope"], dims["v"]
+    kv_lora = dims["kv_lora"]
+    entries = list(cache_entries or [])
+    l0 = len(entries)
+    # keys and values: every token of this call is appended first
+    for t, xt in enumerate(x):
+        p = l0 + t
+        ckv = _matvec(w["kv_a"], xt)
+        c_hat = _rms(ckv[:kv_lora], w["kv_a_norm"], eps)
+        k_pe = _rotate(ckv[kv_lora:], p, theta)
+        entries.append((c_hat, k_pe))
+    keys, vals = [], []
+    for c_hat, k_pe in entries:
+        kv = _matvec(w["kv_b"], c_hat)
+        kh, vh = [], []
+        for h in range(heads):
+            base = h * (nope + vd)
+            kh.append(kv[base: base + nope] + list(k_pe))
+            vh.append(kv[base + nope: base + nope + vd])
+        keys.append(kh)
+        vals.append(vh)
+    ys = []
+    for t, xt in enumerate(x):
+        p = l0 + t
+        q_hat = _rms(_matvec(w["q_a"], xt), w["q_a_norm"], eps)
+        q = _matvec(w["q_b"], q_hat)
+        o_flat = []
+        for h in range(heads):
+            base = h * (nope + rope)
+            qh = q[base: base + nope] + _rotate(q[base + nope: base + nope + rope], p, theta)
+            scores = []
+            for j in range(p + 1):  # causal: keys at positions 0..p
+                scores.append(sigma * sum(qh[d] * keys[j][h][d] for d in range(nope + rope)))
+            m = max(scores)
+            e = [math.exp(s - m) for s in scores]
+            z = sum(e)
+            o_h = [sum(e[j] / z * vals[j][h][d] for j in range(p + 1)) for d in range(vd)]
+            o_flat.extend(o_h)
+        ys.append(_matvec(w["o"], o_flat))
+    return ys, entries[l0:]

@@ -1,0 +1,336 @@
+"""Pins of the float64 oracle against facts fixed by the pages and by mathematics (CPU only).
+
+Each test ties one part of the oracle to something other than itself: numbers printed on the
+pages (tests/golden/page_facts.json), closed forms, invariants, library routines and a
+pure-Python brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute, fp8, mla
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+
+TINY = mla.Config(hidden=8, q_lora=6, kv_lora=4, heads=2, nope=3, rope=4, v=2, eps=1e-6, theta=50000.0)
+
+
+def tiny_weights(cfg: mla.Config, seed=3, zero=()):
+    rng = np.random.default_rng(seed)
+    w = {}
+    for name, shape in mla.weight_shapes(cfg).items():
+        if name.endswith("norm"):
+            w[name] = 1.0 + 0.1 * rng.standard_normal(shape)
+        else:
+            w[name] = 0.5 * rng.standard_normal(shape)
+        if name in zero:
+            w[name] = np.zeros(shape)
+    return w
+
+
+def to_lists(w):
+    return {k: v.tolist() for k, v in w.items()}
+
+
+# ------------------------------------------------------------------------------------ P1, P2, P3
+def test_parameter_counts_match_pages():
+    g = GOLD["param_counts"]
+    n = {k: int(np.prod(s)) for k, s in mla.weight_shapes().items()}
+    cfg = mla.KIMI_K2
+    kva_latent_rows = cfg.kv_lora * cfg.hidden
+    kva_rope_rows = cfg.rope * cfg.hidden
+    w_uk = cfg.heads * cfg.nope * cfg.kv_lora
+    w_uv = cfg.heads * cfg.v * cfg.kv_lora
+    assert n["q_a"] + n["q_a_norm"] == g["query_compression"]
+    assert kva_latent_rows + n["kv_a_norm"] == g["kv_compression"]
+    assert n["q_b"] == g["query_heads"]
+    assert w_uk + kva_rope_rows == g["key_heads"]
+    assert w_uv == g["value_heads"]
+    assert n["o"] == g["causal_attention_out"]
+    assert sum(n.values()) == g["per_instance_total"]
+    assert n["kv_b"] == w_uk + w_uv
+    assert w_uk == g["w_uk"] and 60 * w_uk == g["w_uk_times_60_moe_blocks"]
+
+
+def test_cache_bytes_match_pages():
+    g = GOLD["cache_bytes_per_token_61_layers"]
+    b = mla.cache_bytes_per_position()
+    assert b["rebuilt"] * g["layers"] == g["rebuilt_bf16"]
+    assert b["latent"] * g["layers"] == g["latent_bf16"]
+    assert b["flash_padded"] * g["layers"] == g["flash_padded_bf16"]
+    assert round(b["rebuilt"] / b["latent"]) == g["ratio_rounded"]
+    vp = GOLD["values_per_position"]
+    assert b["rebuilt"] // 2 == vp["rebuilt"] and b["latent"] // 2 == vp["latent"]
+
+
+def test_decode_shapes_at_position_1000():
+    """1000 cached + 1 new token: rebuilt keys/values cover 1,001 positions ('KV cache' page)."""
+    cfg = mla.KIMI_K2
+    rng = np.random.default_rng(0)
+    c_hat = rng.standard_normal((1001, cfg.kv_lora))
+    k_pe = rng.standard_normal((1001, cfg.rope))
+    w_kvb = 0.02 * rng.standard_normal(mla.weight_shapes()["kv_b"])
+    k, v = mla.rebuild_kv(c_hat, k_pe, w_kvb)
+    gk, gv = GOLD["decode_shapes_at_p1000"]["k"], GOLD["decode_shapes_at_p1000"]["v"]
+    # the pages' layout is [B, heads, positions, features]; the oracle keeps [positions, heads, features]
+    assert (k.shape[1], k.shape[0], k.shape[2]) == tuple(gk[1:])
+    assert (v.shape[1], v.shape[0], v.shape[2]) == tuple(gv[1:])
+    assert cfg.kv_lora == GOLD["tensor_shapes"]["latent"]
+    assert cfg.heads * cfg.nope == GOLD["tensor_shapes"]["k_content_flat"]
+    assert cfg.rope // 2 == GOLD["tensor_shapes"]["rope_pairs"]
+    # the shared rotary key is the same in every head
+    assert np.array_equal(k[:, 0, cfg.nope:], k[:, 63, cfg.nope:])
+
+
+def test_kv_b_head_split_is_content_then_value():
+    """W_UK is output features 0..127 of each head's 256 ('Key content up-projection', Explanation)."""
+    cfg = mla.KIMI_K2
+    rng = np.random.default_rng(1)
+    c = rng.standard_normal((2, cfg.kv_lora))
+    w_kvb = rng.standard_normal(mla.weight_shapes()["kv_b"])
+    k, v = mla.rebuild_kv(c, np.zeros((2, cfg.rope)), w_kvb)
+    h = 37
+    assert np.allclose(k[:, h, :cfg.nope], c @ w_kvb[h * 256: h * 256 + 128].T, rtol=0, atol=1e-10)
+    assert np.allclose(v[:, h], c @ w_kvb[h * 256 + 128: h * 256 + 256].T, rtol=0, atol=1e-10)
+
+
+# ------------------------------------------------------------------------------------ P4 RMSNorm
+def test_rmsnorm_identities():
+    rng = np.random.default_rng(2)
+    m, eps = 512, 1e-6
+    x = rng.standard_normal((5, m))
+    ones = np.ones(m)
+    y = mla.rmsnorm(x, ones, eps)
+    ms_x = np.mean(x * x, axis=1)
+    # with unit gain, mean(y^2) = ms / (ms + eps)
+    assert np.allclose(np.mean(y * y, axis=1), ms_x / (ms_x + eps), rtol=1e-13, atol=0)
+    # odd symmetry, and scale invariance as eps -> 0
+    assert np.array_equal(mla.rmsnorm(-x, ones, eps), -y)
+    assert np.allclose(mla.rmsnorm(1000 * x, ones, 0.0), mla.rmsnorm(x, ones, 0.0), rtol=1e-13)
+    # constant vector a*1 maps to g * a / sqrt(a^2 + eps)
+    a = 0.003
+    g = 1.0 + 0.1 * rng.standard_normal(m)
+    assert np.allclose(mla.rmsnorm(np.full(m, a), g, eps), g * a / math.sqrt(a * a + eps), rtol=1e-14)
+    # eps inside the root: for a tiny input the output is x / sqrt(eps), not x / (rms + eps)
+    t = np.full(m, 1e-9)
+    assert np.allclose(mla.rmsnorm(t, ones, eps), t / math.sqrt(1e-18 + eps), rtol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P7 RoPE
+def test_rope_matches_complex_rotation():
+    cfg = mla.KIMI_K2
+    rng = np.random.default_rng(4)
+    pos = np.array([0, 1, 7, 1000, 131071])
+    v = rng.standard_normal((len(pos), 3, cfg.rope))
+    cos, sin = mla.rope_cos_sin(pos, cfg.rope, cfg.theta)
+    r = mla.rope_rotate(v, cos, sin)
+    z = v[..., 0::2] + 1j * v[..., 1::2]
+    freq = np.array([cfg.theta ** (-(2 * i) / cfg.rope) for i in range(cfg.rope // 2)])
+    rot = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    assert np.allclose(r[..., 0::2], rot.real, atol=1e-12) and np.allclose(r[..., 1::2], rot.imag, atol=1e-12)
+    # position 0 is the identity; pair 0 turns by exactly p radians; pair 16 by p / sqrt(50000)
+    assert np.array_equal(r[0], v[0])
+    assert np.isclose(cos[3, 0], math.cos(1000.0)) and np.isclose(sin[3, 16], math.sin(1000.0 / math.sqrt(50000.0)))
+
+
+def test_rope_relative_position_invariance():
+    cfg = mla.KIMI_K2
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, cfg.rope))
+    k = rng.standard_normal((1, cfg.rope))
+    def score(pq, pk):
+        cq, sq = mla.rope_cos_sin(np.array([pq]), cfg.rope, cfg.theta)
+        ck, sk = mla.rope_cos_sin(np.array([pk]), cfg.rope, cfg.theta)
+        return float((mla.rope_rotate(q, cq, sq) @ mla.rope_rotate(k, ck, sk).T)[0, 0])
+    base = score(17, 5)
+    for delta in (1, 100, 10000):
+        assert abs(score(17 + delta, 5 + delta) - base) < 1e-9 * (1 + abs(base))
+    # norms of pairs are preserved
+    c, s = mla.rope_cos_sin(np.array([12345]), cfg.rope, cfg.theta)
+    r = mla.rope_rotate(q, c, s)
+    assert np.allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, q[:, 0::2] ** 2 + q[:, 1::2] ** 2, rtol=1e-13)
+
+
+# ------------------------------------------------------------------------------------ P6 brute force
+@pytest.mark.parametrize("t_new,l0", [(1, 0), (5, 0), (1, 4), (3, 2)])
+def test_brute_force_tiny(t_new, l0):
+    cfg = TINY
+    w = tiny_weights(cfg)
+    rng = np.random.default_rng(10 + t_new + 7 * l0)
+    x_prev = rng.standard_normal((l0, cfg.hidden))
+    x = rng.standard_normal((t_new, cfg.hidden))
+    cache = mla.kv_entries(x_prev, w, 0, cfg) if l0 else None
+    out = mla.forward(x, w, cfg, cache=cache)
+    dims = dict(q_lora=cfg.q_lora, kv_lora=cfg.kv_lora, heads=cfg.heads, nope=cfg.nope, rope=cfg.rope, v=cfg.v)
+    bcache = None
+    if l0:
+        bcache = [(list(cache[0][i]), list(cache[1][i])) for i in range(l0)]
+    ys, ents = brute.forward(x.tolist(), to_lists(w), dims, cfg.eps, cfg.theta, 1 / math.sqrt(cfg.qk), bcache)
+    assert np.allclose(out["y"], np.array(ys), rtol=0, atol=1e-12)
+    assert np.allclose(out["c_hat"], np.array([e[0] for e in ents]), rtol=0, atol=1e-12)
+    assert np.allclose(out["k_pe"], np.array([e[1] for e in ents]), rtol=0, atol=1e-12)
+
+
+def test_brute_force_tiny_softmax_scale_default():
+    assert mla.KIMI_K2.sigma == pytest.approx(1 / math.sqrt(192), rel=1e-15)
+
+
+# ------------------------------------------------------------------------------------ P5 T = 1
+def test_single_token_closed_form():
+    """One token, empty cache: softmax over one key is 1, so o = W_UV,h c_hat for each head."""
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=11)
+    x = np.random.default_rng(12).standard_normal((1, cfg.hidden))
+    out = mla.forward(x, w, cfg)
+    ckv = x[0] @ w["kv_a"].T
+    c = ckv[: cfg.kv_lora]
+    c_hat = w["kv_a_norm"] * c / math.sqrt(np.mean(c ** 2) + cfg.eps)
+    kv = w["kv_b"] @ c_hat
+    o = np.concatenate([kv[h * (cfg.nope + cfg.v) + cfg.nope:(h + 1) * (cfg.nope + cfg.v)] for h in range(cfg.heads)])
+    assert np.allclose(out["y"][0], w["o"] @ o, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P12 uniform
+def test_uniform_attention_when_queries_vanish():
+    """Zero q_b: every score is 0, so each query averages the values of positions 0..t."""
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=13, zero=("q_b",))
+    x = np.random.default_rng(14).standard_normal((6, cfg.hidden))
+    out = mla.forward(x, w, cfg)
+    _, v = mla.rebuild_kv(out["c_hat"], out["k_pe"], w["kv_b"], cfg)
+    for t in range(6):
+        o = v[: t + 1].mean(axis=0).reshape(-1)
+        assert np.allclose(out["y"][t], w["o"] @ o, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P8 absorption
+def test_absorbed_form_equals_rebuilt_form():
+    cfg = mla.Config(hidden=96, q_lora=48, kv_lora=32, heads=4, nope=16, rope=8, v=12)
+    w = tiny_weights(cfg, seed=15)
+    x = np.random.default_rng(16).standard_normal((7, cfg.hidden))
+    out = mla.forward(x, w, cfg)
+    pos = np.arange(7)
+    o_abs = mla.attend_absorbed(out["q_nope"], out["q_pe"], out["c_hat"], out["k_pe"], w["kv_b"], pos, cfg)
+    assert np.allclose(o_abs.reshape(7, -1), out["o"], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P9, P11
+def test_prefill_equals_prefill_then_decode():
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=17)
+    x = np.random.default_rng(18).standard_normal((9, cfg.hidden))
+    full = mla.forward(x, w, cfg)
+    first = mla.forward(x[:8], w, cfg)
+    step = mla.forward(x[8:], w, cfg, cache=(first["c_hat"], first["k_pe"]))
+    assert np.allclose(step["y"][0], full["y"][8], rtol=0, atol=1e-12)
+    assert np.allclose(first["y"], full["y"][:8], rtol=0, atol=1e-12)
+
+
+def test_causality_later_tokens_do_not_change_earlier_outputs():
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=19)
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((8, cfg.hidden))
+    x2 = x.copy()
+    x2[5:] = rng.standard_normal((3, cfg.hidden))
+    a = mla.forward(x, w, cfg)["y"]
+    b = mla.forward(x2, w, cfg)["y"]
+    assert np.array_equal(a[:5], b[:5])
+    assert not np.allclose(a[5:], b[5:])
+
+
+def test_rows_subset_matches_full():
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=21)
+    x = np.random.default_rng(22).standard_normal((10, cfg.hidden))
+    full = mla.forward(x, w, cfg)
+    sub = mla.forward(x, w, cfg, rows=np.array([0, 4, 9]))
+    assert np.allclose(sub["y"], full["y"][[0, 4, 9]], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------ P13, P14 FP8
+def test_e4m3_decode_matches_torch_for_all_codes():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = fp8.e4m3_value(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_rne_with_saturation():
+    import torch
+
+    rng = np.random.default_rng(23)
+    vals = fp8.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2  # exact ties
+    x = np.concatenate([
+        rng.standard_normal(200000) * 50, rng.standard_normal(20000) * 1e-3, mids, -mids, vals, -vals,
+        np.array([448.0, 449.0, 464.0, 1000.0, -500.0, 0.0, 1e-30]),
+    ]).astype(np.float32)
+    mine = fp8.e4m3_encode(x)
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # compare values (a negative number rounding to zero may give +0 or -0)
+    assert np.array_equal(fp8.e4m3_value(mine), fp8.e4m3_value(ref))
+    assert not np.any((mine & 0x7F) == 0x7F)
+
+
+def test_activation_quantiser_worked_cases():
+    # a group whose amax is 448 * 2^-5 gets scale exactly 2^-5; exact e4m3 multiples round-trip
+    g = np.zeros((1, 128))
+    g[0, 0] = 448 * 2.0 ** -5
+    g[0, 1] = -1.5 * 2.0 ** -5
+    g[0, 2] = 0.65625 * 2.0 ** -5  # halfway between 0.625 (m=2) and 0.6875 (m=3): tie -> even m
+    codes, s = fp8.quantize_1x128(g)
+    assert s[0, 0] == np.float32(2.0 ** -5)
+    dq = fp8.dequant_1x128(codes, s)
+    assert dq[0, 0] == g[0, 0] and dq[0, 1] == g[0, 1]
+    assert fp8.e4m3_value(codes[0, 2:3])[0] == 0.625
+    # zero group -> scale 1, codes 0; groups are independent
+    z = np.zeros((2, 256))
+    z[1, 128:] = np.linspace(-3, 3, 128)
+    c2, s2 = fp8.quantize_1x128(z)
+    assert s2[0, 0] == 1.0 and s2[0, 1] == 1.0 and s2[1, 0] == 1.0 and np.all(c2[0] == 0)
+    assert s2[1, 1] == np.float32(np.float32(3.0) / np.float32(448.0))
+    # the largest element quantises to +-448 (possibly by saturation)
+    assert np.max(np.abs(fp8.e4m3_value(c2[1, 128:]))) == 448.0
+    # per-token groups: quantising rows one by one equals quantising the matrix
+    m = np.random.default_rng(24).standard_normal((5, 384))
+    cm, sm = fp8.quantize_1x128(m)
+    for r in range(5):
+        cr, sr = fp8.quantize_1x128(m[r:r + 1])
+        assert np.array_equal(cr[0], cm[r]) and np.array_equal(sr[0], sm[r])
+
+
+def test_weight_dequant_blocks_and_ragged_rows():
+    rng = np.random.default_rng(25)
+    codes = rng.integers(0, 0x7E, size=(576, 256)).astype(np.uint8)
+    s = rng.uniform(0.001, 0.01, size=(5, 2)).astype(np.float32)
+    w = fp8.dequant_weight(codes, s)
+    v = fp8.e4m3_value(codes)
+    assert w[0, 0] == v[0, 0] * float(s[0, 0])
+    assert w[575, 255] == v[575, 255] * float(s[4, 1])  # ragged last block row (rows 512..575)
+    assert w[511, 128] == v[511, 128] * float(s[3, 1])
+    # exact: a 4-bit significand times a 24-bit significand fits in float64
+    assert np.array_equal(w / np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:576, :256], v)
+
+
+def test_w8a8_forward_quantises_projection_inputs():
+    """W8A8 mode differs from plain mode only through the quantiser; with inputs that are
+    already exact e4m3 multiples of a power-of-two group scale the quantiser is the identity
+    on x, so q_a/kv_a outputs agree exactly."""
+    cfg = mla.Config(hidden=128, q_lora=128, kv_lora=128, heads=2, nope=64, rope=64, v=64)
+    w = tiny_weights(cfg, seed=26)
+    x = np.zeros((1, 128))
+    x[0, :4] = [448.0, -2.0, 1.0, 0.5]
+    a = mla.latent_path(x, w, np.array([0]), cfg, w8a8=False)
+    b = mla.latent_path(x, w, np.array([0]), cfg, w8a8=True)
+    assert np.array_equal(a["ckv"], b["ckv"])
+    # c_hat in W8A8 is the quantise-dequantise image of the RMSNorm output
+    assert np.array_equal(b["c_hat"], fp8.fake_quant_1x128(a["c_hat"]))
