@@ -1,0 +1,263 @@
+"""Thin ctypes binding over libmla.so (include/mla.h). Argument marshalling only.
+
+torch provides device memory and the stream; every step of the layer runs in the library's HIP
+kernels. Loading fails loudly if the library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+MLA_OK = 0
+STATUS_NAMES = {0: "MLA_OK", 1: "MLA_E_ARG", 2: "MLA_E_SHAPE", 3: "MLA_E_CAPACITY", 4: "MLA_E_UNSUPPORTED",
+                5: "MLA_E_WORKSPACE", 6: "MLA_E_HIP", 7: "MLA_E_ALIGN"}
+WDTYPE_BF16 = 0
+WDTYPE_FP8 = 1
+
+EXPORTED = (
+    "mla_packed_weight_bytes", "mla_cache_entry_bytes", "mla_prefill_workspace_bytes",
+    "mla_decode_workspace_bytes", "mla_workspace_init", "mla_init_weights", "mla_prefill", "mla_decode",
+    "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
+)
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("q_lora", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("qk_nope", ctypes.c_int32), ("qk_rope", ctypes.c_int32),
+                ("v_head", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float), ("max_positions", ctypes.c_int32), ("wdtype", ctypes.c_int32)]
+
+
+class MlaWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q_a", "q_a_norm", "q_b", "kv_a", "kv_a_norm", "kv_b", "o")] + \
+               [(n, ctypes.c_void_p) for n in ("q_a_s", "q_b_s", "kv_a_s", "kv_b_s", "o_s")]
+
+
+class MlaCacheDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("offset_h", ctypes.c_void_p), ("offset_d", ctypes.c_void_p),
+                ("len_h", ctypes.c_void_p), ("len_d", ctypes.c_void_p), ("cap_h", ctypes.c_void_p),
+                ("n_seqs", ctypes.c_int32), ("total_slots", ctypes.c_int64)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so (built by head_latent_attention_proj_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m head_latent_attention_proj_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.mla_packed_weight_bytes.argtypes = [ctypes.POINTER(MlaConfig)]
+    L.mla_packed_weight_bytes.restype = sz
+    L.mla_cache_entry_bytes.argtypes = [ctypes.POINTER(MlaConfig)]
+    L.mla_cache_entry_bytes.restype = sz
+    L.mla_prefill_workspace_bytes.argtypes = [vp, i32, i32, i64]
+    L.mla_prefill_workspace_bytes.restype = sz
+    L.mla_decode_workspace_bytes.argtypes = [vp, i32, i64]
+    L.mla_decode_workspace_bytes.restype = sz
+    L.mla_workspace_init.argtypes = [vp, sz, vp]
+    L.mla_workspace_init.restype = ctypes.c_int
+    L.mla_init_weights.argtypes = [ctypes.POINTER(MlaConfig), ctypes.POINTER(MlaWeights), vp, sz, vp,
+                                   ctypes.POINTER(vp)]
+    L.mla_init_weights.restype = ctypes.c_int
+    L.mla_prefill.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.mla_prefill.restype = ctypes.c_int
+    L.mla_decode.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp, sz, vp]
+    L.mla_decode.restype = ctypes.c_int
+    L.mla_cache_append.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), i32, vp, i32, vp]
+    L.mla_cache_append.restype = ctypes.c_int
+    L.mla_destroy.argtypes = [vp]
+    L.mla_destroy.restype = None
+    L.mla_status_str.argtypes = [ctypes.c_int]
+    L.mla_status_str.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != MLA_OK:
+        raise MlaError(status, lib().mla_last_error().decode())
+
+
+def make_config(max_positions: int = 131072, wdtype: int = WDTYPE_BF16, softmax_scale: float = 0.0,
+                eps: float = 1e-6, theta: float = 50000.0) -> MlaConfig:
+    return MlaConfig(7168, 1536, 512, 64, 128, 64, 128, eps, theta, softmax_scale, max_positions, wdtype)
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Cache:
+    """Caller-owned latent cache: device slots plus host/device offset and length arrays."""
+
+    def __init__(self, layer: "Layer", caps, device="cuda", fill_byte: int | None = None, align: int = 16):
+        import torch
+
+        caps = np.asarray(caps, dtype=np.int64)
+        rounded = ((caps + align - 1) // align) * align
+        self.offset_h = np.zeros(len(caps), dtype=np.int64)
+        if len(caps) > 1:
+            self.offset_h[1:] = np.cumsum(rounded)[:-1]
+        self.cap_h = caps.astype(np.int32)
+        self.len_h = np.zeros(len(caps), dtype=np.int32)
+        self.total_slots = int(rounded.sum())
+        self.entry_bytes = layer.entry_bytes
+        self.data = torch.empty(self.total_slots * self.entry_bytes, dtype=torch.uint8, device=device)
+        if fill_byte is not None:
+            self.data.fill_(fill_byte)
+        self.offset_d = torch.from_numpy(self.offset_h).to(device)
+        self.len_d = torch.zeros(len(caps), dtype=torch.int32, device=device)
+        self._desc = MlaCacheDesc(self.data.data_ptr(), self.offset_h.ctypes.data, self.offset_d.data_ptr(),
+                                  self.len_h.ctypes.data, self.len_d.data_ptr(), self.cap_h.ctypes.data,
+                                  len(caps), self.total_slots)
+
+    @property
+    def desc(self) -> MlaCacheDesc:
+        return self._desc
+
+    def slots(self, seq: int):
+        """View of sequence `seq`'s used slots as [len, entry_bytes] uint8."""
+        o, n = int(self.offset_h[seq]), int(self.len_h[seq])
+        return self.data.view(-1, self.entry_bytes)[o:o + n]
+
+
+class Layer:
+    """One MLA layer: a library context over caller-owned (torch) weights."""
+
+    def __init__(self, weights: dict, max_positions: int = 131072, wdtype: int = WDTYPE_BF16, stream=None):
+        import torch
+
+        L = lib()
+        self.cfg = make_config(max_positions, wdtype)
+        self.weights = weights  # keep the referenced tensors alive
+        w = MlaWeights()
+        for name in ("q_a", "q_a_norm", "q_b", "kv_a", "kv_a_norm", "kv_b", "o"):
+            setattr(w, name, weights[name].data_ptr())
+        if wdtype == WDTYPE_FP8:
+            for name in ("q_a", "q_b", "kv_a", "kv_b", "o"):
+                setattr(w, name + "_s", weights[name + "_s"].data_ptr())
+        nbytes = L.mla_packed_weight_bytes(ctypes.byref(self.cfg))
+        if nbytes == 0:
+            raise MlaError(1, L.mla_last_error().decode())
+        self.packed = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ctx = ctypes.c_void_p()
+        check(L.mla_init_weights(ctypes.byref(self.cfg), ctypes.byref(w), _ptr(self.packed), nbytes,
+                                 _stream(stream), ctypes.byref(ctx)))
+        self.ctx = ctx
+        self.entry_bytes = L.mla_cache_entry_bytes(ctypes.byref(self.cfg))
+        self._ws = None
+
+    def close(self):
+        if self.ctx:
+            lib().mla_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, nbytes: int, stream=None):
+        import torch
+
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            check(lib().mla_workspace_init(_ptr(self._ws), self._ws.numel(), _stream(stream)))
+        return self._ws
+
+    def prefill_workspace_bytes(self, max_tokens: int, max_batch: int, max_keys: int) -> int:
+        return lib().mla_prefill_workspace_bytes(self.ctx, max_tokens, max_batch, max_keys)
+
+    def decode_workspace_bytes(self, max_batch: int, max_keys: int) -> int:
+        return lib().mla_decode_workspace_bytes(self.ctx, max_batch, max_keys)
+
+    def prefill(self, cache: Cache, seq_ids, q_start, x, y=None, stream=None):
+        """x: [sum T, 7168] bf16 cuda; q_start: B+1 row offsets. Returns y [sum T, 7168] bf16."""
+        import torch
+
+        seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        q_start = np.ascontiguousarray(q_start, dtype=np.int32)
+        B = len(seq_ids)
+        keys = int(sum(int(cache.len_h[s]) + int(q_start[b + 1] - q_start[b]) for b, s in enumerate(seq_ids)))
+        ws = self.workspace(self.prefill_workspace_bytes(int(q_start[-1]), B, keys), stream)
+        if y is None:
+            y = torch.empty_like(x)
+        sid_d = torch.from_numpy(seq_ids).to(x.device)
+        qs_d = torch.from_numpy(q_start).to(x.device)
+        check(lib().mla_prefill(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(sid_d),
+                                q_start.ctypes.data, _ptr(qs_d), B, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+        self._keep = (sid_d, qs_d)  # device copies stay alive until the next call
+        return y
+
+    def decode(self, cache: Cache, seq_ids, x, y=None, seq_ids_d=None, stream=None):
+        """One new token per sequence: x [B, 7168] bf16 cuda. Returns y [B, 7168] bf16."""
+        import torch
+
+        seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        B = len(seq_ids)
+        keys = int(sum(int(cache.len_h[s]) + 1 for s in seq_ids))
+        ws = self.workspace(self.decode_workspace_bytes(B, keys), stream)
+        if y is None:
+            y = torch.empty_like(x)
+        if seq_ids_d is None:
+            seq_ids_d = torch.from_numpy(seq_ids).to(x.device)
+        check(lib().mla_decode(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(seq_ids_d), B,
+                               _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+        self._keep = (seq_ids_d,)
+        return y
+
+    def cache_append(self, cache: Cache, seq: int, entries, stream=None):
+        """entries: cuda tensor holding n * entry_bytes bytes in the slot format."""
+        n = entries.numel() * entries.element_size() // self.entry_bytes
+        check(lib().mla_cache_append(self.ctx, ctypes.byref(cache.desc), seq, _ptr(entries), n, _stream(stream)))
+
+
+def weights_to_device(wbits: dict, device="cuda") -> dict:
+    """numpy bf16 bits / e4m3 codes / float32 scales -> torch tensors on the device."""
+    import torch
+
+    out = {}
+    for k, v in wbits.items():
+        if v.dtype == np.uint16:
+            out[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    return out
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def tensor_to_bf16_bits(t) -> np.ndarray:
+    import torch
+
+    return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)

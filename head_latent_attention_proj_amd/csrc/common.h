@@ -1,0 +1,72 @@
+// Shared device helpers for the gfx950 MLA kernels: bf16 handling, MFMA wrappers, launch structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define MLA_DEV __device__ __forceinline__
+
+// Kimi-K2 dimensions the kernels are specialised for.
+namespace mla_dims {
+constexpr int HIDDEN = 7168;
+constexpr int Q_LORA = 1536;
+constexpr int KV_LORA = 512;
+constexpr int HEADS = 64;
+constexpr int NOPE = 128;
+constexpr int ROPE = 64;
+constexpr int VD = 128;
+constexpr int QK = NOPE + ROPE;          // 192
+constexpr int ENTRY = KV_LORA + ROPE;    // 576 features per cached position
+constexpr int QKVA_N = Q_LORA + ENTRY;   // 2112: fused q_a | kv_a output width
+constexpr int KVB_N = HEADS * (NOPE + VD);  // 16384
+constexpr int QB_N = HEADS * QK;         // 12288
+constexpr int O_IN = HEADS * VD;         // 8192
+constexpr int BF16_ENTRY_BYTES = ENTRY * 2;                 // 1152
+constexpr int FP8_ENTRY_BYTES = KV_LORA + 16 + ROPE * 2;    // 656: codes | 4 scales | k_pe
+}  // namespace mla_dims
+
+MLA_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+MLA_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+MLA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// bf16 pair (packed in a uint32) -> two floats
+MLA_DEV float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+MLA_DEV float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// D = A(16x32) * B(32x16) + C on one wave. Lane l holds row (A) / column (B) l%16 and eight
+// consecutive k of group l/16; the result holds column l%16, rows 4*(l/16) .. +3. Any
+// permutation of k applied identically to A and B leaves the product unchanged.
+MLA_DEV f32x4_t mfma_bf16_16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+MLA_DEV bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+MLA_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+MLA_DEV void st16(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+template <typename T>
+MLA_DEV T wave_max(T v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename T>
+MLA_DEV T wave_sum(T v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -1,0 +1,154 @@
+// Host-side launch interfaces of the gfx950 MLA kernels (implemented in the *.hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla_k {
+
+// ---------------------------------------------------------------------------------------------
+// GEMM  C[b] = A[b] (M x K) * B[b]^T (B is N x K): both operands K-contiguous ("NT"), which is
+// how nn.Linear stores its [out, in] weight. bf16 operands, fp32 accumulation.
+// ---------------------------------------------------------------------------------------------
+enum Epilogue : int {
+  EPI_F32 = 0,   // C float32
+  EPI_BF16 = 1,  // C bf16
+  EPI_KVB = 2,   // kv_b output split per head: content keys -> knope[key][h*128+d] (bf16),
+                 // values -> vt[(h*128+d) * vt_ld + key] (bf16, key-contiguous for P.V)
+};
+
+struct GemmArgs {
+  const void* A = nullptr;  int64_t lda = 0, sA = 0;  // elements; sA = batch stride
+  const void* B = nullptr;  int64_t ldb = 0, sB = 0;
+  void* C = nullptr;        int64_t ldc = 0, sC = 0;
+  int M = 0, N = 0, K = 0, batch = 1;
+  int epi = EPI_F32;
+  // EPI_KVB destinations
+  uint16_t* knope = nullptr;
+  uint16_t* vt = nullptr;
+  int64_t vt_ld = 0;
+  int64_t key_base = 0;
+  // FP8 (E4M3FN codes) operands: A scales per (row, 128-group) with row stride as_ld floats;
+  // B scales per (128-row block, 128-group) with row stride bs_ld floats.
+  const float* a_scale = nullptr; int64_t as_ld = 0;
+  const float* b_scale = nullptr; int64_t bs_ld = 0;
+  // split-K scratch (workspace): fp32 partials and per-tile arrival counters (kept zeroed)
+  float* part = nullptr;
+  int* counters = nullptr;
+  int64_t part_cap = 0;     // floats available in `part`
+  int counter_cap = 0;      // counters available
+};
+
+// Chooses a tile kernel (large M) or a split-K skinny kernel (small M). Returns a hipError_t.
+hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s);
+// Bytes of split-K partials / counters the skinny path may need for an (M, N, K, batch) GEMM.
+int64_t gemm_part_floats(int M, int N, int K, int batch);
+int gemm_counters(int M, int N, int K, int batch);
+
+// ---------------------------------------------------------------------------------------------
+// Per-call sequence metadata (device, filled by plan_kernel at the start of a prefill)
+// ---------------------------------------------------------------------------------------------
+struct SeqMeta {
+  int64_t slot0;   // first cache slot of the sequence
+  int32_t l0;      // positions held before this call
+  int32_t t;       // new tokens in this call
+  int32_t q0;      // first row of this call's tokens in x / y
+  int32_t kbase;   // first row of this sequence's rebuilt keys in the prefill workspace
+  int32_t seq;     // sequence id
+  int32_t pad;
+};
+
+hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const int64_t* offset_d,
+                        const int32_t* len_d, int B, SeqMeta* meta, hipStream_t s);
+hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, int32_t* len_d, int B,
+                          hipStream_t s);
+
+// RMSNorm of the fused q_a | kv_a output (fp32 [n, 2112]): q_hat (bf16 [n, 1536]) and the cache
+// entry [c_hat | rotated k_pe] of each token written to its slot. Prefill: token -> sequence
+// through `meta`; decode (meta == nullptr): token b is sequence seq_ids[b] at position len[seq],
+// and len[seq] is advanced by one after the entry is written.
+struct NormArgs {
+  const float* cqkv;
+  const uint16_t* g_q;
+  const uint16_t* g_kv;
+  float eps;
+  uint16_t* q_hat;
+  const float* rope_cs;  // [max_pos][32] cos, then [max_pos][32] sin (float32)
+  int max_pos;
+  uint8_t* cache;
+  int entry_bytes;
+  int fp8;               // cache / q_hat in FP8 form
+  uint8_t* q_hat_codes;  // FP8: q_hat codes [n, 1536] and scales [n, 12]
+  float* q_hat_scales;
+  int n_tokens;
+  // prefill
+  const SeqMeta* meta;
+  int B;
+  // decode
+  const int32_t* seq_ids;
+  const int64_t* offset;
+  int32_t* len;
+};
+hipError_t norm_rope_append(const NormArgs& a, hipStream_t s);
+
+// Byte copy of n ready-made entries to dst (the slot of position len[seq]); len[seq] += n.
+hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_bytes, int n, int seq, int32_t* len_d,
+                                hipStream_t s);
+
+// ---------------------------------------------------------------------------------------------
+// Prefill attention (rebuilt keys/values, causal): o[row][h*128+d] bf16
+// ---------------------------------------------------------------------------------------------
+struct PrefillAttnArgs {
+  const uint16_t* q;       // [n_tok][64][192] bf16, rotary part not yet rotated
+  const uint16_t* knope;   // [keys][64][128] bf16
+  const uint16_t* vt;      // [64*128][vt_ld] bf16
+  int64_t vt_ld;
+  const uint8_t* cache;    // for the rotated shared key k_pe of each position
+  int entry_bytes;
+  int kpe_off;             // byte offset of k_pe inside an entry
+  const float* rope_cs;
+  int max_pos;
+  const SeqMeta* meta;
+  int B;
+  int max_t;               // largest T_b (grid sizing)
+  float scale;             // softmax scale
+  uint16_t* o;             // [n_tok][8192] bf16 (when o_f32 is null)
+  float* o_f32;            // optional fp32 output [n_tok][8192]
+};
+hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------------
+// Decode attention in the latent space, split over positions, then merged
+// ---------------------------------------------------------------------------------------------
+struct DecodeAttnArgs {
+  const uint16_t* q_lat;   // [B][64][512] bf16 (q_nope absorbed through W_UK)
+  const uint16_t* q;       // [B][64][192] bf16: rotary part read from here, rotated on load
+  const uint8_t* cache;
+  int entry_bytes;
+  int fp8;
+  const float* rope_cs;
+  int max_pos;
+  const int32_t* seq_ids;
+  const int64_t* offset;
+  const int32_t* len;      // positions held INCLUDING this step's entry
+  int B;
+  int chunk;               // positions per split
+  int max_splits;          // splits per sequence in the grid
+  float scale;
+  float* part_o;           // [B][max_splits][64][512] fp32
+  float* part_ml;          // [B][max_splits][64][2] (running max, sum)
+  uint16_t* o_lat;         // merged [B][64][512] bf16
+};
+hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s);
+
+// FP8 activation quantiser for a bf16/fp32 matrix [rows, K] (K multiple of 128).
+hipError_t quantize_rows_f32(const float* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
+                             hipStream_t s);
+hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
+                              hipStream_t s);
+
+// Fill kernel for small control blocks (used instead of memset so callers may capture graphs).
+hipError_t fill_zero_i32(int* p, int64_t n, hipStream_t s);
+
+}  // namespace mla_k

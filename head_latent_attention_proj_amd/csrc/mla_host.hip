@@ -1,0 +1,508 @@
+// Host side of the C ABI in include/mla.h: validation, weight packing, workspace planning and the
+// launch sequences of prefill and decode. Nothing here allocates device memory; every device
+// buffer is the caller's. All validation happens before the first enqueue of a call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace mla_dims;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(MLA_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// ---- W_UK^T per head: ukT[h][c][d] = kv_b[h*256 + d][c]  (d < 128, c < 512), bf16
+__global__ void transpose_uk_kernel(const uint16_t* kvb, uint16_t* ukT) {
+  const int h = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // over 512*128
+  if (idx >= KV_LORA * NOPE) return;
+  const int c = idx / NOPE, d = idx % NOPE;
+  ukT[((int64_t)h * KV_LORA + c) * NOPE + d] = kvb[((int64_t)h * 256 + d) * KV_LORA + c];
+}
+
+}  // namespace
+
+struct mla_ctx {
+  mla_config cfg;
+  float scale;
+  const uint16_t* g_q;
+  const uint16_t* g_kv;
+  const void* w_qkva;  // packed [2112, 7168]
+  const void* w_qb;
+  const void* w_kvb;
+  const void* w_ukT;   // packed [64][512][128]
+  const void* w_o;
+  const float* rope_cs;
+};
+
+namespace {
+
+mla_status check_config(const mla_config* c) {
+  if (!c) return fail(MLA_E_ARG, "config is NULL");
+  if (c->hidden != HIDDEN || c->q_lora != Q_LORA || c->kv_lora != KV_LORA || c->heads != HEADS ||
+      c->qk_nope != NOPE || c->qk_rope != ROPE || c->v_head != VD)
+    return fail(MLA_E_UNSUPPORTED,
+                "kernels are built for hidden 7168, q_lora 1536, kv_lora 512, 64 heads, 128/64/128 head widths");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f) || c->softmax_scale < 0.f || !std::isfinite(c->softmax_scale))
+    return fail(MLA_E_ARG, "rms_eps, rope_theta or softmax_scale out of range");
+  if (c->max_positions < 1 || c->max_positions > 131072)
+    return fail(MLA_E_ARG, "max_positions must be in [1, 131072]");
+  if (c->wdtype != MLA_WDTYPE_BF16 && c->wdtype != MLA_WDTYPE_FP8_E4M3_B128)
+    return fail(MLA_E_ARG, "unknown weight format %d", c->wdtype);
+  return MLA_OK;
+}
+
+struct PackedLayout {
+  size_t qkva, ukT, g_q, g_kv, rope, total;
+};
+
+PackedLayout packed_layout(const mla_config* c) {
+  PackedLayout L{};
+  const size_t eb = c->wdtype == MLA_WDTYPE_BF16 ? 2 : 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L.qkva = take((size_t)QKVA_N * HIDDEN * eb);
+  L.ukT = take((size_t)HEADS * KV_LORA * NOPE * eb);
+  L.g_q = take(Q_LORA * 2);
+  L.g_kv = take(KV_LORA * 2);
+  L.rope = take((size_t)c->max_positions * 32 * 2 * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// ---- workspace planning ----------------------------------------------------------------------
+constexpr int N_COUNTERS = 16384;
+constexpr int DECODE_MAX_WG = 2048;
+
+struct DecodePlan {
+  int chunk = 64, max_splits = 1;
+};
+
+DecodePlan plan_decode(int B, const int* lens_after, int n) {
+  int64_t total = 0;
+  int max_len = 1;
+  for (int i = 0; i < n; ++i) {
+    total += lens_after[i];
+    max_len = std::max(max_len, lens_after[i]);
+  }
+  DecodePlan p;
+  p.chunk = (int)std::max<int64_t>(64, round_up((total + 511) / 512, 64));
+  p.max_splits = (max_len + p.chunk - 1) / p.chunk;
+  while ((int64_t)B * p.max_splits > DECODE_MAX_WG) {
+    p.chunk *= 2;
+    p.max_splits = (max_len + p.chunk - 1) / p.chunk;
+  }
+  return p;
+}
+
+struct WsLayout {
+  size_t counters, cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, o_lat, gpart, total;
+  int64_t gpart_floats;
+  int64_t vt_ld;
+};
+
+// GEMM shapes a call may run, for split-K scratch sizing: (M, N, K, batch).
+int64_t max_gemm_part(int ntok, int nkeys_seq, bool decode) {
+  int64_t mx = 0;
+  auto upd = [&](int M, int N, int K, int batch) {
+    if (M > 0) mx = std::max(mx, mla_k::gemm_part_floats(M, N, K, batch));
+  };
+  upd(ntok, QKVA_N, HIDDEN, 1);
+  upd(ntok, QB_N, Q_LORA, 1);
+  upd(ntok, HIDDEN, O_IN, 1);
+  if (decode) {
+    upd(ntok, KV_LORA, NOPE, HEADS);
+    upd(ntok, VD, KV_LORA, HEADS);
+  } else {
+    upd(nkeys_seq, KVB_N, KV_LORA, 1);
+  }
+  return mx;
+}
+
+WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64_t gpart_floats) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L.counters = take(N_COUNTERS * sizeof(int));
+  L.cqkv = take((size_t)ntok * QKVA_N * 4);
+  L.q_hat = take((size_t)ntok * Q_LORA * 2);
+  L.q = take((size_t)ntok * QB_N * 2);
+  L.o = take((size_t)ntok * O_IN * 2);
+  L.meta = take((size_t)nbatch * sizeof(mla_k::SeqMeta));
+  L.vt_ld = round_up(nkeys, 64);
+  L.knope = take((size_t)L.vt_ld * HEADS * NOPE * 2);
+  L.vt = take((size_t)L.vt_ld * HEADS * VD * 2);
+  L.q_lat = take((size_t)nbatch * HEADS * KV_LORA * 2);
+  L.part_o = take((size_t)decode_splits * HEADS * KV_LORA * 4);
+  L.part_ml = take((size_t)decode_splits * HEADS * 2 * 4);
+  L.o_lat = take((size_t)nbatch * HEADS * KV_LORA * 2);
+  L.gpart_floats = gpart_floats;
+  L.gpart = take((size_t)gpart_floats * 4);
+  L.total = off;
+  return L;
+}
+
+mla_k::GemmArgs gemm_common(uint8_t* ws, const WsLayout& L) {
+  mla_k::GemmArgs g;
+  g.part = (float*)(ws + L.gpart);
+  g.part_cap = L.gpart_floats;
+  g.counters = (int*)(ws + L.counters);
+  g.counter_cap = N_COUNTERS;
+  return g;
+}
+
+mla_status check_cache(const mla_ctx* ctx, const mla_cache* c) {
+  if (!c) return fail(MLA_E_ARG, "cache is NULL");
+  if (!c->data || !c->offset_h || !c->offset_d || !c->len_h || !c->len_d || !c->cap_h)
+    return fail(MLA_E_ARG, "cache has a NULL pointer");
+  if (c->n_seqs <= 0 || c->total_slots <= 0) return fail(MLA_E_ARG, "cache has no sequences or slots");
+  if (!aligned16(c->data)) return fail(MLA_E_ALIGN, "cache data is not 16-byte aligned");
+  (void)ctx;
+  return MLA_OK;
+}
+
+mla_status check_seq(const mla_ctx* ctx, const mla_cache* c, int s, int64_t add) {
+  if (s < 0 || s >= c->n_seqs) return fail(MLA_E_ARG, "sequence id %d outside [0, %d)", s, c->n_seqs);
+  const int64_t len = c->len_h[s];
+  if (len < 0 || c->cap_h[s] < 0 || c->offset_h[s] < 0 || c->offset_h[s] + c->cap_h[s] > c->total_slots)
+    return fail(MLA_E_ARG, "sequence %d has an inconsistent offset/cap/len", s);
+  if (len + add > c->cap_h[s])
+    return fail(MLA_E_CAPACITY, "sequence %d: %lld positions + %lld new exceed its %d slots", s, (long long)len,
+                (long long)add, c->cap_h[s]);
+  if (len + add > ctx->cfg.max_positions)
+    return fail(MLA_E_CAPACITY, "sequence %d: %lld positions exceed max_positions %d", s, (long long)(len + add),
+                ctx->cfg.max_positions);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_E_ARG: return "invalid argument";
+    case MLA_E_SHAPE: return "inconsistent shapes";
+    case MLA_E_CAPACITY: return "cache capacity exceeded";
+    case MLA_E_UNSUPPORTED: return "unsupported configuration";
+    case MLA_E_WORKSPACE: return "workspace too small";
+    case MLA_E_HIP: return "HIP runtime error";
+    case MLA_E_ALIGN: return "misaligned device pointer";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+size_t mla_packed_weight_bytes(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return packed_layout(cfg).total;
+}
+
+size_t mla_cache_entry_bytes(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return cfg->wdtype == MLA_WDTYPE_BF16 ? BF16_ENTRY_BYTES : FP8_ENTRY_BYTES;
+}
+
+size_t mla_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32_t max_batch, int64_t max_keys) {
+  if (!ctx || max_tokens <= 0 || max_batch <= 0 || max_keys < max_tokens) return 0;
+  // rebuilt keys: each sequence's rows are padded to a multiple of 64
+  const int64_t keys = max_keys + 63LL * max_batch;
+  int64_t gp = 0;
+  for (int m = 1; m <= std::min(max_tokens, 4096); ++m) gp = std::max(gp, max_gemm_part(m, 0, false));
+  const int64_t kmax = std::min<int64_t>(max_keys, 4096);
+  for (int64_t k = 1; k <= kmax; ++k) gp = std::max(gp, mla_k::gemm_part_floats((int)k, KVB_N, KV_LORA, 1));
+  return ws_layout(max_tokens, max_batch, keys, 0, gp).total;
+}
+
+size_t mla_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t max_keys) {
+  if (!ctx || max_batch <= 0 || max_keys < max_batch) return 0;
+  int64_t gp = 0;
+  for (int m = 1; m <= max_batch; ++m) gp = std::max(gp, max_gemm_part(m, 0, true));
+  const int64_t splits = std::min<int64_t>((int64_t)max_batch * ((max_keys + 63) / 64), DECODE_MAX_WG);
+  return ws_layout(max_batch, max_batch, 0, (int)std::max<int64_t>(splits, max_batch), gp).total;
+}
+
+mla_status mla_workspace_init(void* ws, size_t ws_bytes, mla_stream stream) {
+  if (!ws) return fail(MLA_E_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MLA_E_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < N_COUNTERS * sizeof(int)) return fail(MLA_E_WORKSPACE, "workspace smaller than its control block");
+  HIP_TRY(mla_k::fill_zero_i32((int*)ws, N_COUNTERS, (hipStream_t)stream));
+  return MLA_OK;
+}
+
+mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* packed, size_t packed_bytes,
+                            mla_stream stream, mla_ctx** out) {
+  if (!out) return fail(MLA_E_ARG, "out is NULL");
+  *out = nullptr;
+  mla_status st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  if (!w || !packed) return fail(MLA_E_ARG, "weights or packed buffer is NULL");
+  const void* ptrs[] = {w->q_a, w->q_a_norm, w->q_b, w->kv_a, w->kv_a_norm, w->kv_b, w->o};
+  for (const void* p : ptrs) {
+    if (!p) return fail(MLA_E_ARG, "a weight pointer is NULL");
+    if (!aligned16(p)) return fail(MLA_E_ALIGN, "a weight pointer is not 16-byte aligned");
+  }
+  if (cfg->wdtype == MLA_WDTYPE_FP8_E4M3_B128)
+    return fail(MLA_E_UNSUPPORTED, "FP8 block-scaled weights are not enabled in this build");
+  const PackedLayout L = packed_layout(cfg);
+  if (packed_bytes < L.total) return fail(MLA_E_WORKSPACE, "packed buffer has %zu bytes, needs %zu", packed_bytes, L.total);
+  if (!aligned16(packed)) return fail(MLA_E_ALIGN, "packed buffer is not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* pk = (uint8_t*)packed;
+  const size_t eb = 2;
+  HIP_TRY(hipMemcpyAsync(pk + L.qkva, w->q_a, (size_t)Q_LORA * HIDDEN * eb, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(pk + L.qkva + (size_t)Q_LORA * HIDDEN * eb, w->kv_a, (size_t)ENTRY * HIDDEN * eb,
+                         hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(pk + L.g_q, w->q_a_norm, Q_LORA * 2, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(pk + L.g_kv, w->kv_a_norm, KV_LORA * 2, hipMemcpyDeviceToDevice, s));
+  hipLaunchKernelGGL(transpose_uk_kernel, dim3(KV_LORA * NOPE / 256, HEADS), dim3(256), 0, s,
+                     (const uint16_t*)w->kv_b, (uint16_t*)(pk + L.ukT));
+  HIP_TRY(hipGetLastError());
+  // RoPE table: angle = position * theta^(-2i/64), computed in double, stored float32
+  const int P = cfg->max_positions;
+  std::vector<float> cs((size_t)P * 64);
+  for (int i = 0; i < 32; ++i) {
+    const double freq = std::pow((double)cfg->rope_theta, -2.0 * i / 64.0);
+    for (int p = 0; p < P; ++p) {
+      const double ang = (double)p * freq;
+      cs[(size_t)p * 32 + i] = (float)std::cos(ang);
+      cs[(size_t)P * 32 + (size_t)p * 32 + i] = (float)std::sin(ang);
+    }
+  }
+  HIP_TRY(hipMemcpyAsync(pk + L.rope, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+
+  mla_ctx* c = new mla_ctx;
+  c->cfg = *cfg;
+  c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(1.0 / std::sqrt((double)QK));
+  c->g_q = (const uint16_t*)(pk + L.g_q);
+  c->g_kv = (const uint16_t*)(pk + L.g_kv);
+  c->w_qkva = pk + L.qkva;
+  c->w_qb = w->q_b;
+  c->w_kvb = w->kv_b;
+  c->w_ukT = pk + L.ukT;
+  c->w_o = w->o;
+  c->rope_cs = (const float*)(pk + L.rope);
+  *out = c;
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+void mla_destroy(mla_ctx* ctx) { delete ctx; }
+
+mla_status mla_cache_append(mla_ctx* ctx, mla_cache* cache, int32_t seq_id, const void* entries, int32_t n,
+                            mla_stream stream) {
+  if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
+  mla_status st = check_cache(ctx, cache);
+  if (st != MLA_OK) return st;
+  if (!entries) return fail(MLA_E_ARG, "entries is NULL");
+  if (n <= 0) return fail(MLA_E_ARG, "n must be positive");
+  if (!aligned16(entries)) return fail(MLA_E_ALIGN, "entries are not 16-byte aligned");
+  st = check_seq(ctx, cache, seq_id, n);
+  if (st != MLA_OK) return st;
+  const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
+  uint8_t* dst = (uint8_t*)cache->data + (cache->offset_h[seq_id] + cache->len_h[seq_id]) * (int64_t)eb;
+  HIP_TRY(mla_k::cache_copy_append_at(dst, (const uint8_t*)entries, eb, n, seq_id, cache->len_d,
+                                      (hipStream_t)stream));
+  cache->len_h[seq_id] += n;
+  return MLA_OK;
+}
+
+mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                       const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
+                       void* ws, size_t ws_bytes, mla_stream stream) {
+  if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
+  mla_status st = check_cache(ctx, cache);
+  if (st != MLA_OK) return st;
+  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
+  if (!seq_ids_h || !seq_ids_d || !q_start_h || !q_start_d || !x || !y || !ws)
+    return fail(MLA_E_ARG, "a pointer argument is NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MLA_E_ALIGN, "x, y or ws is not 16-byte aligned");
+  if (q_start_h[0] != 0) return fail(MLA_E_SHAPE, "q_start[0] must be 0");
+  std::vector<int64_t> kbase(B);
+  int64_t nkeys = 0;
+  int max_t = 0;
+  for (int b = 0; b < B; ++b) {
+    const int t = q_start_h[b + 1] - q_start_h[b];
+    if (t <= 0) return fail(MLA_E_SHAPE, "sequence %d of the batch has %d new tokens", b, t);
+    for (int c = 0; c < b; ++c)
+      if (seq_ids_h[c] == seq_ids_h[b]) return fail(MLA_E_ARG, "sequence id %d appears twice", seq_ids_h[b]);
+    st = check_seq(ctx, cache, seq_ids_h[b], t);
+    if (st != MLA_OK) return st;
+    kbase[b] = nkeys;
+    nkeys += round_up(cache->len_h[seq_ids_h[b]] + t, 64);
+    max_t = std::max(max_t, t);
+  }
+  const int ntok = q_start_h[B];
+  int max_keys_seq = 0;
+  for (int b = 0; b < B; ++b)
+    max_keys_seq = std::max(max_keys_seq, cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b]);
+  int64_t gp = max_gemm_part(ntok, 0, false);
+  for (int b = 0; b < B; ++b)
+    gp = std::max(gp, mla_k::gemm_part_floats(cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b],
+                                              KVB_N, KV_LORA, 1));
+  const WsLayout L = ws_layout(ntok, B, nkeys, 0, gp);
+  if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
+  auto* meta = (mla_k::SeqMeta*)(w + L.meta);
+  HIP_TRY(mla_k::prefill_plan(seq_ids_d, q_start_d, cache->offset_d, cache->len_d, B, meta, s));
+
+  // 1. fused q_a | kv_a projection (fp32 out)
+  mla_k::GemmArgs g = gemm_common(w, L);
+  g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
+  g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 2. RMSNorms, RoPE of the shared key, latent entries into the cache
+  mla_k::NormArgs na{};
+  na.cqkv = (const float*)(w + L.cqkv); na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
+  na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
+  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = ntok; na.meta = meta; na.B = B;
+  HIP_TRY(mla_k::norm_rope_append(na, s));
+  // 3. q_b
+  g = gemm_common(w, L);
+  g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
+  g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values
+  for (int b = 0; b < B; ++b) {
+    const int sid = seq_ids_h[b];
+    const int n = cache->len_h[sid] + q_start_h[b + 1] - q_start_h[b];
+    g = gemm_common(w, L);
+    g.A = (const uint8_t*)cache->data + cache->offset_h[sid] * (int64_t)eb; g.lda = eb / 2;
+    g.B = ctx->w_kvb; g.ldb = KV_LORA; g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB;
+    g.knope = (uint16_t*)(w + L.knope); g.vt = (uint16_t*)(w + L.vt); g.vt_ld = L.vt_ld; g.key_base = kbase[b];
+    HIP_TRY(mla_k::gemm_bf16(g, s));
+  }
+  // 5. causal attention
+  mla_k::PrefillAttnArgs pa{};
+  pa.q = (const uint16_t*)(w + L.q); pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
+  pa.vt_ld = L.vt_ld; pa.cache = (const uint8_t*)cache->data; pa.entry_bytes = eb; pa.kpe_off = KV_LORA * 2;
+  pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
+  pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o);
+  HIP_TRY(mla_k::prefill_attention(pa, s));
+  // 6. o_proj
+  g = gemm_common(w, L);
+  g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
+  g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 7. lengths
+  HIP_TRY(mla_k::commit_lengths(seq_ids_d, q_start_d, cache->len_d, B, s));
+  for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += q_start_h[b + 1] - q_start_h[b];
+  return MLA_OK;
+}
+
+mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
+                      const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream) {
+  if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
+  mla_status st = check_cache(ctx, cache);
+  if (st != MLA_OK) return st;
+  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
+  if (!seq_ids_h || !seq_ids_d || !x || !y || !ws) return fail(MLA_E_ARG, "a pointer argument is NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MLA_E_ALIGN, "x, y or ws is not 16-byte aligned");
+  std::vector<int> lens(B);
+  for (int b = 0; b < B; ++b) {
+    for (int c = 0; c < b; ++c)
+      if (seq_ids_h[c] == seq_ids_h[b]) return fail(MLA_E_ARG, "sequence id %d appears twice", seq_ids_h[b]);
+    st = check_seq(ctx, cache, seq_ids_h[b], 1);
+    if (st != MLA_OK) return st;
+    lens[b] = cache->len_h[seq_ids_h[b]] + 1;
+  }
+  const DecodePlan dp = plan_decode(B, lens.data(), B);
+  const int64_t gp = max_gemm_part(B, 0, true);
+  const WsLayout L = ws_layout(B, B, 0, B * dp.max_splits, gp);
+  if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
+  // 1. fused q_a | kv_a
+  mla_k::GemmArgs g = gemm_common(w, L);
+  g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
+  g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 2. norms + shared-key RoPE + append at position len; len_d advances by one here
+  mla_k::NormArgs na{};
+  na.cqkv = (const float*)(w + L.cqkv); na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
+  na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
+  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = B; na.meta = nullptr;
+  na.seq_ids = seq_ids_d; na.offset = cache->offset_d; na.len = cache->len_d;
+  HIP_TRY(mla_k::norm_rope_append(na, s));
+  // 3. q_b
+  g = gemm_common(w, L);
+  g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
+  g.M = B; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched GEMM)
+  g = gemm_common(w, L);
+  g.A = w + L.q; g.lda = QB_N; g.sA = QK; g.B = ctx->w_ukT; g.ldb = NOPE; g.sB = (int64_t)KV_LORA * NOPE;
+  g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.M = B; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
+  g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 5. split attention over the latent cache + merge
+  mla_k::DecodeAttnArgs da{};
+  da.q_lat = (const uint16_t*)(w + L.q_lat); da.q = (const uint16_t*)(w + L.q); da.cache = (const uint8_t*)cache->data;
+  da.entry_bytes = eb; da.fp8 = 0; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
+  da.seq_ids = seq_ids_d; da.offset = cache->offset_d; da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
+  da.max_splits = dp.max_splits; da.scale = ctx->scale; da.part_o = (float*)(w + L.part_o);
+  da.part_ml = (float*)(w + L.part_ml); da.o_lat = (uint16_t*)(w + L.o_lat);
+  HIP_TRY(mla_k::decode_attention(da, s));
+  // 6. W_UV per head: o[b, h*128 + d] = o_lat[b,h,:] . W_UV,h[d,:]
+  g = gemm_common(w, L);
+  g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
+  g.B = (const uint16_t*)ctx->w_kvb + (int64_t)NOPE * KV_LORA; g.ldb = KV_LORA; g.sB = 256 * KV_LORA;
+  g.C = w + L.o; g.ldc = O_IN; g.sC = VD; g.M = B; g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 7. o_proj
+  g = gemm_common(w, L);
+  g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
+  g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16;
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
+  return MLA_OK;
+}
+
+}  // extern "C"

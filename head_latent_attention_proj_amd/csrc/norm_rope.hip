@@ -1,0 +1,266 @@
+// RMSNorm + RoPE + latent cache append, per-call sequence planning, length commits, FP8
+// activation quantisation.
+//
+// RMSNorm follows the rmsnorm excerpt on the "Key-value latent" page: float32,
+// y = g * x / sqrt(mean(x^2) + eps). The normalised value is rounded once (to bf16, or to an
+// E4M3FN code with its group scale in FP8 mode); the excerpt's intermediate cast to the input
+// dtype before the gain is not reproduced.
+// RoPE: pairs (2i, 2i+1) of the 64 rotary features turn by position * theta^(-2i/64)
+// (cos/sin from a float32 table built on the host in double precision).
+// The cache entry of a position is [c_hat (512) | rotated k_pe (64)] ("Key-value latent" page,
+// mla-kv excerpt: the 512 + 64 split of kv_a_proj_with_mqa; the latent RMSNorm output is the
+// input of kv_b, so it is what the keys and values are rebuilt from).
+#include "common.h"
+#include "kernels.h"
+
+namespace mla_k {
+
+namespace {
+
+// OCP E4M3FN encode of a float32, round to nearest even, saturating at +-448.
+MLA_DEV uint32_t e4m3_rne_sat(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  if (!(a < 448.f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (m = 8 is the smallest normal)
+    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.f);
+    return sign | m;
+  }
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+  const uint32_t e = (r >> 3) - 127u + 7u;
+  return sign | (e << 3) | (r & 7u);
+}
+
+// Block-wide sum over 256 threads (4 waves).
+MLA_DEV float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+__global__ void plan_kernel(const int32_t* seq_ids, const int32_t* q_start, const int64_t* offset,
+                            const int32_t* len, int B, SeqMeta* meta) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int kbase = 0;
+  for (int b = 0; b < B; ++b) {
+    const int s = seq_ids[b];
+    SeqMeta m;
+    m.slot0 = offset[s];
+    m.l0 = len[s];
+    m.q0 = q_start[b];
+    m.t = q_start[b + 1] - q_start[b];
+    m.kbase = kbase;
+    m.seq = s;
+    m.pad = 0;
+    meta[b] = m;
+    kbase += (m.l0 + m.t + 63) & ~63;  // rows of one sequence padded to the 64-key block
+  }
+}
+
+__global__ void commit_kernel(const int32_t* seq_ids, const int32_t* q_start, int32_t* len, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) len[seq_ids[b]] += q_start[b + 1] - q_start[b];
+}
+
+// One workgroup (256 threads) per token.
+__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
+  using namespace mla_dims;
+  __shared__ float red[4];
+  __shared__ float vals[KV_LORA];
+  const int tok = blockIdx.x;
+  const int tid = threadIdx.x;
+
+  int64_t slot;
+  int pos;
+  int seq = -1;
+  if (a.meta) {
+    int lo = 0, hi = a.B - 1;  // last sequence whose first row is <= tok
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.meta[mid].q0 <= tok) lo = mid; else hi = mid - 1;
+    }
+    const SeqMeta m = a.meta[lo];
+    pos = m.l0 + (tok - m.q0);
+    slot = m.slot0 + pos;
+  } else {
+    seq = a.seq_ids[tok];
+    pos = a.len[seq];
+    slot = a.offset[seq] + pos;
+  }
+
+  const float* row = a.cqkv + (int64_t)tok * QKVA_N;
+  // ---- query latent RMSNorm (1536 = 6 per thread)
+  float xq[6];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    xq[i] = row[tid + i * 256];
+    ss += xq[i] * xq[i];
+  }
+  const float rq = 1.0f / sqrtf(block_sum256(ss, red) / (float)Q_LORA + a.eps);
+  // ---- kv latent RMSNorm (512 = 2 per thread)
+  float xc[2];
+  ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xc[i] = row[Q_LORA + tid + i * 256];
+    ss += xc[i] * xc[i];
+  }
+  const float rc = 1.0f / sqrtf(block_sum256(ss, red) / (float)KV_LORA + a.eps);
+
+  uint8_t* entry = a.cache + slot * a.entry_bytes;
+  if (!a.fp8) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + i * 256;
+      a.q_hat[(int64_t)tok * Q_LORA + c] = f2bf(bf2f(a.g_q[c]) * (xq[i] * rq));
+    }
+    uint16_t* e16 = (uint16_t*)entry;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      e16[c] = f2bf(bf2f(a.g_kv[c]) * (xc[i] * rc));
+    }
+  } else {
+    // q_hat: 12 groups of 128; c_hat: 4 groups. Values go through LDS so one wave owns a group.
+    __shared__ float qv[Q_LORA];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + i * 256;
+      qv[c] = bf2f(a.g_q[c]) * (xq[i] * rq);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      vals[c] = bf2f(a.g_kv[c]) * (xc[i] * rc);
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int grp = wave; grp < 16; grp += 4) {
+      const float* src = grp < 12 ? qv + grp * 128 : vals + (grp - 12) * 128;
+      const float v0 = src[lane], v1 = src[lane + 64];
+      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+      const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
+      const uint32_t c0 = e4m3_rne_sat(v0 / sc), c1 = e4m3_rne_sat(v1 / sc);
+      if (grp < 12) {
+        uint8_t* dst = a.q_hat_codes + (int64_t)tok * Q_LORA + grp * 128;
+        dst[lane] = (uint8_t)c0;
+        dst[lane + 64] = (uint8_t)c1;
+        if (lane == 0) a.q_hat_scales[(int64_t)tok * (Q_LORA / 128) + grp] = sc;
+      } else {
+        uint8_t* dst = entry + (grp - 12) * 128;
+        dst[lane] = (uint8_t)c0;
+        dst[lane + 64] = (uint8_t)c1;
+        if (lane == 0) ((float*)(entry + KV_LORA))[grp - 12] = sc;
+      }
+    }
+  }
+  // ---- shared rotary key: 32 pairs, rotated by this token's position
+  if (tid < ROPE / 2) {
+    const float k0 = row[Q_LORA + KV_LORA + 2 * tid];
+    const float k1 = row[Q_LORA + KV_LORA + 2 * tid + 1];
+    const float c = a.rope_cs[(int64_t)pos * 32 + tid];
+    const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + tid];
+    uint16_t* kpe = (uint16_t*)(entry + (a.fp8 ? KV_LORA + 16 : KV_LORA * 2));
+    *(uint32_t*)(kpe + 2 * tid) = pack_bf16x2(k0 * c - k1 * s, k0 * s + k1 * c);
+  }
+  if (!a.meta) {
+    __syncthreads();
+    if (tid == 0) a.len[seq] = pos + 1;
+  }
+}
+
+__global__ void copy_append_kernel(uint8_t* dst, const uint8_t* src, int64_t nvec, int32_t* len, int seq, int n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nvec) st16(dst + i * 16, ld16(src + i * 16));
+  if (i == 0) len[seq] += n;
+}
+
+// One wave per 128-feature group of one row.
+template <typename T>
+__global__ void quantize_rows_kernel(const T* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int groups = K / 128;
+  if (gid >= (int64_t)rows * groups) return;
+  const int r = (int)(gid / groups), gi = (int)(gid % groups);
+  const T* src = x + r * ldx + gi * 128;
+  float v0, v1;
+  if constexpr (sizeof(T) == 2) {
+    v0 = bf2f(src[lane]);
+    v1 = bf2f(src[lane + 64]);
+  } else {
+    v0 = src[lane];
+    v1 = src[lane + 64];
+  }
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
+  uint8_t* dst = codes + (int64_t)r * K + gi * 128;
+  dst[lane] = (uint8_t)e4m3_rne_sat(v0 / sc);
+  dst[lane + 64] = (uint8_t)e4m3_rne_sat(v1 / sc);
+  if (lane == 0) scales[(int64_t)r * groups + gi] = sc;
+}
+
+__global__ void fill_zero_kernel(int* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const int64_t* offset_d,
+                        const int32_t* len_d, int B, SeqMeta* meta, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, seq_ids_d, q_start_d, offset_d, len_d, B, meta);
+  return hipGetLastError();
+}
+
+hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, int32_t* len_d, int B,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3(cdiv(B, 256)), dim3(256), 0, s, seq_ids_d, q_start_d, len_d, B);
+  return hipGetLastError();
+}
+
+hipError_t norm_rope_append(const NormArgs& a, hipStream_t s) {
+  if (a.n_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_rope_append_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_bytes, int n, int seq, int32_t* len_d,
+                                hipStream_t s) {
+  const int64_t nvec = (int64_t)n * entry_bytes / 16;
+  hipLaunchKernelGGL(copy_append_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s, dst, src, nvec,
+                     len_d, seq, n);
+  return hipGetLastError();
+}
+
+hipError_t quantize_rows_f32(const float* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
+                             hipStream_t s) {
+  const int64_t waves = (int64_t)rows * (K / 128);
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, ldx, rows,
+                     K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
+                              hipStream_t s) {
+  const int64_t waves = (int64_t)rows * (K / 128);
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, ldx,
+                     rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t fill_zero_i32(int* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace mla_k

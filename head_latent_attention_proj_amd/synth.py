@@ -168,3 +168,18 @@ def packed_offsets(caps: np.ndarray, align: int = 16) -> tuple[np.ndarray, np.nd
     if caps.size > 1:
         offs[1:] = np.cumsum(caps)[:-1]
     return offs, caps.astype(np.int32), int(caps.sum())
+
+
+def make_cache_entries(n: int, d: Dims = KIMI_K2, seed: int = 2000, latent_std: float = 1.0,
+                       kpe_std: float = 1.7) -> np.ndarray:
+    """Synthetic latent cache entries [n, kv_lora + rope] in bf16 bits.
+
+    The latent part stands for RMSNorm outputs (unit RMS times gains near 1: N(0, latent_std));
+    the rotary part for the shared key of a 7168-wide N(0,1) input through N(0, 0.02) weights
+    (std sqrt(7168) * 0.02 = 1.7; a rotation keeps it). Used where filling a long cache through
+    the kv path would cost more than the test itself.
+    """
+    rng = np.random.default_rng(seed)
+    lat = rng.normal(0.0, latent_std, size=(n, d.kv_lora))
+    kpe = rng.normal(0.0, kpe_std, size=(n, d.rope))
+    return f32_to_bf16_bits(np.concatenate([lat, kpe], axis=1).astype(np.float32))

@@ -1,0 +1,84 @@
+"""The C-ABI library loads on a machine without a GPU, exports every declared symbol, and
+rejects invalid arguments before touching HIP (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_latent_attention_proj_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libmla.so not built")
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_symbols()
+    assert names, "no declarations found"
+    assert set(binding.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(8):
+        assert L.mla_status_str(code)
+    assert L.mla_status_str(0) == b"ok"
+
+
+def test_config_validation_without_gpu(L):
+    cfg = binding.make_config(max_positions=4096)
+    assert L.mla_cache_entry_bytes(ctypes.byref(cfg)) == 1152
+    assert L.mla_packed_weight_bytes(ctypes.byref(cfg)) > (2112 * 7168 + 64 * 512 * 128) * 2
+    fp8 = binding.make_config(max_positions=4096, wdtype=binding.WDTYPE_FP8)
+    assert L.mla_cache_entry_bytes(ctypes.byref(fp8)) == 656
+    bad = binding.make_config()
+    bad.heads = 32
+    assert L.mla_packed_weight_bytes(ctypes.byref(bad)) == 0
+    assert b"built for" in L.mla_last_error()
+    bad = binding.make_config(max_positions=131073)
+    assert L.mla_cache_entry_bytes(ctypes.byref(bad)) == 0
+    bad = binding.make_config(wdtype=7)
+    assert L.mla_cache_entry_bytes(ctypes.byref(bad)) == 0
+
+
+def test_init_rejects_null_and_unsupported_before_any_hip_call(L):
+    ctx = ctypes.c_void_p()
+    w = binding.MlaWeights()
+    cfg = binding.make_config(max_positions=64)
+    assert L.mla_init_weights(ctypes.byref(cfg), ctypes.byref(w), None, 0, None, ctypes.byref(ctx)) == 1
+    assert not ctx.value
+    bad = binding.make_config()
+    bad.hidden = 4096
+    assert L.mla_init_weights(ctypes.byref(bad), ctypes.byref(w), None, 0, None, ctypes.byref(ctx)) == 4
+    # misaligned weight pointers are rejected before use (the addresses are never dereferenced)
+    for i, name in enumerate(("q_a", "q_a_norm", "q_b", "kv_a", "kv_a_norm", "kv_b", "o")):
+        setattr(w, name, 0x1000 * (i + 1) + 2)
+    assert L.mla_init_weights(ctypes.byref(cfg), ctypes.byref(w), 0x100000, 1 << 30, None, ctypes.byref(ctx)) == 7
+
+
+def test_calls_reject_null_context(L):
+    desc = binding.MlaCacheDesc()
+    assert L.mla_prefill(None, ctypes.byref(desc), None, None, None, None, 1, None, None, None, 0, None) == 1
+    assert L.mla_decode(None, ctypes.byref(desc), None, None, 1, None, None, None, 0, None) == 1
+    assert L.mla_cache_append(None, ctypes.byref(desc), 0, None, 1, None) == 1
+    assert L.mla_prefill_workspace_bytes(None, 1, 1, 1) == 0
+    assert L.mla_decode_workspace_bytes(None, 1, 1) == 0
+    assert L.mla_workspace_init(None, 0, None) == 1
+    L.mla_destroy(None)
