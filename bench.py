@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of one Kimi-K2 MLA layer on one MI355X, through the C ABI (libmla.so).
+
+Headline workload: decode, batch 1, one new token at position 1000 over 1000 cached positions
+(bf16 weights N(0, 0.02), gains 1 + N(0, 0.1), hidden states N(0, 1); the cache is filled by an
+untimed GPU prefill of 1000 tokens). A step is one decode call, i.e. every stage of the decode
+path: fused q_a|kv_a projection, both RMSNorms, RoPE and the latent-cache append, q_b, the W_UK
+absorption, split attention over the latent cache with its merge, W_UV and o_proj.
+
+Three copies of the layer (own weights, own cache) are stepped in turn, as consecutive layers of
+a model are: the 202 MB of weights per layer then cannot sit in the 256 MB Infinity Cache
+between its steps, so the step reads them from HBM.
+
+Also reported (same process, same JSON line, under "extra"): prefill of 64 and 8192 tokens
+(tokens/s, MFMA fraction) and batched decode of 64 sequences with cached lengths uniform in
+[1024, 8192] (µs/step, HBM fraction). `roofline` is the o_proj kernel of the headline step timed
+on its own with HIP events on its stream; `cpu_baseline` is the float64 oracle's decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12       # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15      # flop/s, dense bf16 MFMA
+
+WEIGHT_BYTES = 2 * (1536 * 7168 + 1536 + 12288 * 1536 + 576 * 7168 + 512 + 16384 * 512 + 7168 * 8192)
+OPROJ_BYTES = 2 * 7168 * 8192
+
+
+def decode_step_bytes(lens_after, B):
+    """Algorithmic bytes of one decode step: weights once, 1,152 B per cached position read,
+    the new entry written, x read and y written."""
+    return WEIGHT_BYTES + 1152 * int(np.sum(lens_after)) + 1152 * B + 2 * 2 * 7168 * B
+
+
+def prefill_flops(T):
+    """Projections (2 * MACs) plus causal attention: 640 flop per head per causal pair."""
+    proj = 2 * T * (7168 * 2112 + 1536 * 12288 + 512 * 16384 + 8192 * 7168)
+    att = 640 * 64 * T * (T + 1) // 2
+    return proj + att
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_loop(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=3, help="layer copies stepped in turn")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer is not sharded across GPUs.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from head_latent_attention_proj_amd import binding, synth
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    log("generating weights")
+    bits = synth.make_weights_bf16(seed=0)
+    base = binding.weights_to_device(bits)
+    layers = []
+    for c in range(args.copies):
+        w = base if c == 0 else {k: v.clone() for k, v in base.items()}
+        layers.append(binding.Layer(w, max_positions=16384))
+
+    # ---------------- headline: decode B=1 at position 1000 over 1000 cached positions
+    P0 = 1000
+    total_steps = args.steps + args.warmup
+    caps = P0 + total_steps // args.copies + 2
+    caches, xs = [], []
+    x_fill = binding.bf16_tensor(synth.make_hidden(P0, seed=1001))
+    for c, L in enumerate(layers):
+        cache = binding.Cache(L, [caps])
+        L.prefill(cache, [0], [0, P0], x_fill)
+        caches.append(cache)
+    x_new = binding.bf16_tensor(synth.make_hidden(1, seed=1002))
+    y_new = torch.empty_like(x_new)
+    sid_h = np.zeros(1, dtype=np.int32)
+    sid_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def decode_step(i):
+        c = i % args.copies
+        layers[c].decode(caches[c], sid_h, x_new, y=y_new, seq_ids_d=sid_d)
+
+    log("timing decode B=1")
+    t_dec = timed_loop(torch, decode_step, args.steps, args.warmup)
+    us_per_step = t_dec * 1e6
+    lens_after = np.array([P0 + 1])
+    dec_bytes = decode_step_bytes(lens_after, 1)
+
+    # ---------------- roofline: o_proj kernel of that step, HIP events on its stream
+    log("timing o_proj kernel")
+    gemm = binding.Gemm()
+    xo = binding.bf16_tensor(synth.make_activations(1, 8192, seed=7))
+    yo = torch.empty((1, 7168), dtype=torch.bfloat16, device="cuda")
+    n_ev = max(args.steps, 30)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i in range(10):
+        gemm(xo, layers[i % args.copies].weights["o"], yo, 1, 7168, 8192, stage="oproj")
+    for i in range(n_ev):
+        evs[i][0].record(stream)
+        gemm(xo, layers[i % args.copies].weights["o"], yo, 1, 7168, 8192, stage="oproj")
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    oproj_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    oproj_bytes = OPROJ_BYTES + 2 * 8192 + 2 * 7168
+    achieved = oproj_bytes / (oproj_ms * 1e-3) / 1e9
+
+    extra = {}
+    if not args.no_extra:
+        # ---------------- prefill T=64 and T=8192
+        for T, steps in ((64, 30), (8192, 5)):
+            log(f"timing prefill T={T}")
+            xb = binding.bf16_tensor(synth.make_hidden(T, seed=1003))
+            pc = [binding.Cache(L, [T]) for L in layers]
+            yb = torch.empty_like(xb)
+            sid = np.zeros(1, dtype=np.int32)
+            qs = np.array([0, T], dtype=np.int32)
+
+            def prefill_step(i, T=T, xb=xb, pc=pc, yb=yb, sid=sid, qs=qs):
+                c = i % args.copies
+                pc[c].len_h[0] = 0
+                pc[c].len_d.zero_()
+                layers[c].prefill(pc[c], sid, qs, xb, y=yb)
+
+            t = timed_loop(torch, prefill_step, steps, 2)
+            fl = prefill_flops(T)
+            extra[f"prefill_T{T}"] = {
+                "ms": round(t * 1e3, 4), "tokens_per_s": round(T / t, 1),
+                "tflops": round(fl / t / 1e12, 2), "mfma_frac": round(fl / t / BF16_PEAK, 4),
+                "note": "includes one zero-fill of the device length per step",
+            }
+            del pc, xb, yb
+        # ---------------- decode B=64, lengths U[1024, 8192]
+        log("timing decode B=64 varlen")
+        B = 64
+        lens = synth.make_lengths(B, 1024, 8192, seed=1002)
+        L0 = layers[0]
+        vc = binding.Cache(L0, lens + 8)
+        ents = synth.make_cache_entries(int(lens.max()), seed=2002)
+        ent_t = binding.bf16_tensor(ents)
+        for s in range(B):
+            L0.cache_append(vc, s, ent_t[: int(lens[s])])
+        xb = binding.bf16_tensor(synth.make_hidden(B, seed=1004))
+        yb = torch.empty_like(xb)
+        sid_h64 = np.arange(B, dtype=np.int32)
+        sid_d64 = torch.arange(B, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+        def dec64(i):
+            # every step sees the same state: rewind the lengths by one after each step
+            L0.decode(vc, sid_h64, xb, y=yb, seq_ids_d=sid_d64)
+            vc.len_h[:] = lens
+            vc.len_d.sub_(1)
+
+        t = timed_loop(torch, dec64, 10, 3)
+        byts = decode_step_bytes(lens + 1, B)
+        extra["decode_B64_varlen"] = {
+            "us_per_step": round(t * 1e6, 2), "bytes": int(byts),
+            "hbm_gbs": round(byts / t / 1e9, 1), "hbm_frac": round(byts / t / HBM_PEAK, 4),
+            "sum_len": int(lens.sum()),
+            "note": "one copy of the weights (MALL may hold part of them); includes one length rewind per step",
+        }
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing CPU oracle decode step")
+        cpu = cpu_baseline(bits, args.cpu_seconds)
+
+    line = {
+        "metric": "MLA layer prefill tokens/s + decode µs/step; % of HBM / MFMA roofline",
+        "value": round(us_per_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_dec * 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states; random-init, no checkpoint)",
+        "config": {
+            "workload": "decode B=1, one new token at position 1000 over 1000 cached positions, "
+                        "Kimi-K2 MLA layer (hidden 7168, q_lora 1536, kv_lora 512, 64 heads, 128/64/128), bf16",
+            "global_batch": 1, "seq_len": P0 + 1, "parallelism": "single GPU", "layer_copies": args.copies,
+        },
+        "step_bytes": int(dec_bytes),
+        "step_hbm_gbs": round(dec_bytes / t_dec / 1e9, 1),
+        "step_hbm_frac": round(dec_bytes / t_dec / HBM_PEAK, 4),
+        "roofline": {
+            "kernel": "o_proj GEMM (M=1, N=7168, K=8192, bf16 weights)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+            "frac": round(achieved / 8000.0, 4), "traffic": None,
+            "avg_launch_us": round(oproj_ms * 1e3, 3), "bytes_per_launch": int(oproj_bytes),
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(bits, seconds):
+    """The float64 oracle's decode step (position 1000, 1000 cached entries) on the host cores."""
+    from threadpoolctl import threadpool_info
+
+    from head_latent_attention_proj_amd import synth
+    from oracle import mla as omla
+
+    w64 = {k: synth.bf16_bits_to_f64(v) for k, v in bits.items()}
+    ents = synth.bf16_bits_to_f64(synth.make_cache_entries(1000, seed=2001))
+    x = synth.bf16_bits_to_f64(synth.make_hidden(1, seed=1002))
+    cache = (ents[:, :512], ents[:, 512:])
+    n, t0 = 0, time.perf_counter()
+    while True:
+        omla.forward(x, w64, cache=cache)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    threads = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {
+        "value": round(dt * 1e6, 1), "unit": "us/step", "cores": int(max(threads) if threads else 1),
+        "kind": "oracle",
+        "sample": f"{n} float64 decode steps (position 1000 over 1000 cached entries), {dt * n:.1f} s",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

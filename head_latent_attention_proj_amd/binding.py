@@ -22,7 +22,9 @@ EXPORTED = (
     "mla_packed_weight_bytes", "mla_cache_entry_bytes", "mla_prefill_workspace_bytes",
     "mla_decode_workspace_bytes", "mla_workspace_init", "mla_init_weights", "mla_prefill", "mla_decode",
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
+    "mla_test_gemm_workspace_bytes", "mla_test_gemm",
 )
+STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6}
 
 
 class MlaConfig(ctypes.Structure):
@@ -86,6 +88,10 @@ def lib() -> ctypes.CDLL:
     L.mla_status_str.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
     L.mla_last_error.restype = ctypes.c_char_p
+    L.mla_test_gemm_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.mla_test_gemm_workspace_bytes.restype = sz
+    L.mla_test_gemm.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32, vp, sz, vp]
+    L.mla_test_gemm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -138,6 +144,10 @@ class Cache:
     @property
     def desc(self) -> MlaCacheDesc:
         return self._desc
+
+    def held(self, seq: int) -> int:
+        """Positions held by `seq` (0 for an id outside the cache: the library rejects it)."""
+        return int(self.len_h[seq]) if 0 <= seq < len(self.len_h) else 0
 
     def slots(self, seq: int):
         """View of sequence `seq`'s used slots as [len, entry_bytes] uint8."""
@@ -203,7 +213,7 @@ class Layer:
         seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
         q_start = np.ascontiguousarray(q_start, dtype=np.int32)
         B = len(seq_ids)
-        keys = int(sum(int(cache.len_h[s]) + int(q_start[b + 1] - q_start[b]) for b, s in enumerate(seq_ids)))
+        keys = int(sum(cache.held(s) + int(q_start[b + 1] - q_start[b]) for b, s in enumerate(seq_ids)))
         ws = self.workspace(self.prefill_workspace_bytes(int(q_start[-1]), B, keys), stream)
         if y is None:
             y = torch.empty_like(x)
@@ -221,7 +231,7 @@ class Layer:
 
         seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
         B = len(seq_ids)
-        keys = int(sum(int(cache.len_h[s]) + 1 for s in seq_ids))
+        keys = int(sum(cache.held(s) + 1 for s in seq_ids))
         ws = self.workspace(self.decode_workspace_bytes(B, keys), stream)
         if y is None:
             y = torch.empty_like(x)
@@ -261,3 +271,26 @@ def tensor_to_bf16_bits(t) -> np.ndarray:
     import torch
 
     return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)
+
+
+class Gemm:
+    """The library's projection kernel on its own (mla_test_gemm): C = A B^T per batch."""
+
+    def __init__(self):
+        self._ws = None
+
+    def __call__(self, A, B, C, M, N, K, batch=1, lda=None, ldb=None, ldc=None, sA=0, sB=0, sC=0,
+                 stage="none", stream=None):
+        import torch
+
+        need = lib().mla_test_gemm_workspace_bytes(M, N, K, batch)
+        if need == 0:
+            raise MlaError(1, "invalid GEMM shape")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=A.device)
+            check(lib().mla_workspace_init(_ptr(self._ws), self._ws.numel(), _stream(stream)))
+        out_bf16 = 1 if C.dtype == torch.bfloat16 else 0
+        check(lib().mla_test_gemm(M, N, K, batch, _ptr(A), lda or K, sA, _ptr(B), ldb or K, sB, _ptr(C),
+                                  ldc or N, sC, out_bf16, STAGE[stage], _ptr(self._ws), self._ws.numel(),
+                                  _stream(stream)))
+        return C

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int64_t slot0 = a.offset[seq];
   const int nblk = cdiv(c1 - c0, DKB);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int hg = wave & 3, lh = wave >> 2;  // head group (16 heads), latent half (256 features)
   const int head = hg * 16 + l16;

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   if ((int)blockIdx.y >= nqt) return;
   const int q0 = (nqt - 1 - (int)blockIdx.y) * PQ;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave skips scalar
   const int l16 = lane & 15, g = lane >> 4;
   const int n_keys = m.l0 + m.t;
   const int q_hi = min(q0 + PQ, m.t);

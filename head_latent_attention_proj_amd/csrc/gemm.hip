@@ -8,11 +8,16 @@
 //   * gemm_tile   -- prefill-sized M: BM x BN workgroup tile staged through LDS (double
 //                    buffered, padded rows so 16-byte fragment reads are bank-conflict free),
 //                    16x16x32 bf16 MFMA, XCD-aware grouped tile order. Optional split-K.
-//   * gemm_skinny -- decode-sized M (<= 64): activations and weights go straight from global
-//                    memory into MFMA fragments (each lane streams 64 contiguous weight bytes
-//                    per 128-wide K step), K split across workgroups so that every CU streams
-//                    weights; the last workgroup of a tile reduces the fp32 partials in a fixed
-//                    order (deterministic, no float atomics).
+//   * gemm_wsplit -- decode-sized M (<= 64): operands go straight from global memory into MFMA
+//                    fragments; the K range of a 16-column tile is split across the waves of one
+//                    workgroup (each wave streams its own contiguous slice of the weight rows,
+//                    four 32-wide K steps in flight), and the waves' partial tiles are summed
+//                    through LDS in a fixed order. No cross-workgroup synchronisation, no float
+//                    atomics: the result is deterministic.
+//   Split-K of the tile kernel (few tiles, small M) writes fp32 partials and a separate
+//   reduction kernel sums them in a fixed order.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,46 +40,11 @@ MLA_DEV void epi_store(const GemmArgs& p, int b, int m, int n, float v) {
   }
 }
 
-MLA_DEV void part_store(float* ptr, float v) {
-  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-MLA_DEV float part_load(const float* ptr) {
-  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival count for split-K: returns true in the workgroup that arrives last for this tile
-// (it then owns the reduction); that workgroup also resets the counter to zero.
-MLA_DEV bool splitk_arrive(int* ctr, int splits) {
-  __shared__ int last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(ctr, 1);
-    last = (old == splits - 1);
-    if (last) atomicExch(ctr, 0);
-  }
-  __syncthreads();
-  __threadfence();
-  return last != 0;
-}
-
-// Last arrival: sum the partials of region [m0, m0+bm) x [n0, n0+bn) over splits 0..splits-1.
-MLA_DEV void splitk_reduce(const GemmArgs& p, int b, int splits, int m0, int bm, int n0, int bn) {
-  const float* base = p.part + (int64_t)b * splits * p.M * p.N;
-  const int cnt = bm * bn;
-  for (int idx = threadIdx.x; idx < cnt; idx += blockDim.x) {
-    const int m = m0 + idx / bn, n = n0 + idx % bn;
-    if (m >= p.M || n >= p.N) continue;
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += part_load(base + ((int64_t)sp * p.M + m) * p.N + n);
-    epi_store(p, b, m, n, s);
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 // Tile kernel
 // ------------------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
+// TAG only names the projection (distinct kernel symbols per stage in traces); the code is shared.
+template <int BM, int BN, int WM, int WN, int TAG>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int splits, int ksplit) {
   constexpr int NT = WM * WN * 64;
   constexpr int BK = 64;
@@ -87,7 +57,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of rows per pass");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, g = lane >> 4;
 
@@ -191,123 +162,187 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * WTM + i * 16 + g * 4 + e;
         const int n = n0 + wn * WTN + j * 16 + l16;
-        if (m < p.M && n < p.N) part_store(part + (int64_t)m * p.N + n, acc[i][j][e]);
+        if (m < p.M && n < p.N) part[(int64_t)m * p.N + n] = acc[i][j][e];
       }
-  if (splitk_arrive(p.counters + batch * ntile + tm * tiles_n + tn, splits))
-    splitk_reduce(p, batch, splits, m0, BM, n0, BN);
+}
+
+// Sum of the split-K partials in split order, then the epilogue. One thread per output.
+template <int TAG>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int splits) {
+  const int64_t mn = (int64_t)p.M * p.N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (idx >= mn) return;
+  const float* base = p.part + (int64_t)b * splits * mn + idx;
+  float s = 0.f;
+  for (int sp = 0; sp < splits; ++sp) s += base[sp * mn];
+  epi_store(p, b, (int)(idx / p.N), (int)(idx % p.N), s);
 }
 
 // ------------------------------------------------------------------------------------------
-// Skinny kernel: M <= 16*MT rows, 4 waves x TN column tiles of 16, K split over blockIdx.y
+// Decode-sized M: one workgroup per 16-column tile, K split across its KW waves
 // ------------------------------------------------------------------------------------------
-template <int MT, int TN>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p, int splits, int ksplit) {
-  constexpr int WCOLS = TN * 16, BCOLS = 4 * WCOLS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int MT, int KW, int TAG>
+__global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
+  constexpr int U = MT >= 4 ? 2 : 4;  // 32-wide K steps per pipeline stage
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
-  const int nb = blockIdx.x, split = blockIdx.y, batch = blockIdx.z;
-  const int nw = nb * BCOLS + wave * WCOLS;
-  const int kb = split * ksplit;
-  const int ke = min(p.K, kb + ksplit);
-
+  const int n0 = blockIdx.x * 16;
+  const int batch = blockIdx.z;
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
-  // lane (l16, g) owns bytes [g*64, g*64+64) of every 128-wide K step of its row
+  const int nsteps = p.K >> 5;
+  const int spw = cdiv(nsteps, KW);
+  const int s0 = wave * spw;
+  const int s1 = min(nsteps, s0 + spw);
+
+  // lane (l16, g): row l16 of the tile, features g*8 .. g*8+7 of each 32-wide step
   const uint16_t* pa[MT];
-  const uint16_t* pb[TN];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) pa[i] = A + (int64_t)min(i * 16 + l16, p.M - 1) * p.lda + g * 32;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) pb[j] = B + (int64_t)min(nw + j * 16 + l16, p.N - 1) * p.ldb + g * 32;
+  for (int i = 0; i < MT; ++i) pa[i] = A + (int64_t)min(i * 16 + l16, p.M - 1) * p.lda + g * 8;
+  const uint16_t* pb = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + g * 8;
 
-  f32x4_t acc[MT][TN];
+  f32x4_t acc[MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
-  for (int k = kb; k < ke; k += 128) {
-    u32x4_t va[MT][4], vb[TN][4];
+  if (s0 < s1) {
+    // Loads are unconditional (steps past the wave's range re-read its last step) so the
+    // next stage's loads stay in flight while the current stage multiplies; a step past the
+    // range multiplies a zero weight fragment instead of being branched around.
+    u32x4_t ca[U][MT], cb[U];
+    auto load = [&](int s, u32x4_t (&ra)[U][MT], u32x4_t (&rb)[U]) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int u = 0; u < U; ++u) {
+        const int st = min(s + u, s1 - 1) * 32;
+        rb[u] = ld16(pb + st);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) vb[j][s] = ld16(pb[j] + k + s * 8);
+        for (int i = 0; i < MT; ++i) ra[u][i] = ld16(pa[i] + st);
+      }
+    };
+    load(s0, ca, cb);
+    for (int s = s0; s < s1; s += U) {
+      u32x4_t na[U][MT], nb[U];
+      load(min(s + U, s1 - 1), na, nb);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int u = 0; u < U; ++u) {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        const u32x4_t bw = (s + u < s1) ? cb[u] : zero;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) va[i][s] = ld16(pa[i] + k + s * 8);
+        for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16_16x16x32(as_bf16x8(ca[u][i]), as_bf16x8(bw), acc[i]);
+      }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int u = 0; u < U; ++u) {
+        cb[u] = nb[u];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) ca[u][i] = na[u][i];
+      }
+    }
+  }
+
+  // fixed-order sum of the waves' partial tiles through LDS
+  if constexpr (KW > 1) {
+    __shared__ float red[(KW - 1) * MT * 4 * 64];
+    if (wave > 0) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma_bf16_16x16x32(as_bf16x8(va[i][s]), as_bf16x8(vb[j][s]), acc[i][j]);
+        for (int e = 0; e < 4; ++e) red[(((wave - 1) * MT + i) * 4 + e) * 64 + lane] = acc[i][e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] += red[((w * MT + i) * 4 + e) * 64 + lane];
   }
-
-  if (splits == 1) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = i * 16 + g * 4 + e, n = nw + j * 16 + l16;
-          if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][j][e]);
-        }
-    return;
-  }
-  float* part = p.part + ((int64_t)batch * splits + split) * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = i * 16 + g * 4 + e, n = nw + j * 16 + l16;
-        if (m < p.M && n < p.N) part_store(part + (int64_t)m * p.N + n, acc[i][j][e]);
-      }
-  if (splitk_arrive(p.counters + batch * gridDim.x + nb, splits))
-    splitk_reduce(p, batch, splits, 0, 16 * MT, nb * BCOLS, BCOLS);
+    for (int e = 0; e < 4; ++e) {
+      const int m = i * 16 + g * 4 + e, n = n0 + l16;
+      if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][e]);
+    }
 }
 
-constexpr int SKINNY_TN = 4;
-constexpr int SKINNY_COLS = 4 * SKINNY_TN * 16;  // 256 columns per workgroup
-constexpr int TARGET_WGS = 512;                  // two workgroups per CU on 256 CUs
+constexpr int TARGET_WGS = 512;  // two workgroups per CU on 256 CUs
 
 struct Plan {
-  int kind;  // 0 skinny, 1 tile128, 2 tile256
-  int mt;
+  int kind;  // 0 wsplit, 1 tile128, 2 tile256
+  int mt, kw;
   int splits, ksplit;
   int tiles;  // workgroups per (split, batch)
 };
 
+int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
 Plan plan_gemm(int M, int N, int K, int batch) {
   Plan pl{};
-  int kstep;
+  pl.splits = 1;
+  pl.ksplit = K;
   if (M <= 64) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    pl.tiles = cdiv(N, SKINNY_COLS);
-    kstep = 128;
-  } else {
-    const bool big = (M >= 1024 && N >= 1024);
-    pl.kind = big ? 2 : 1;
-    const int bm = big ? 256 : 128;
-    pl.tiles = cdiv(M, bm) * cdiv(N, bm);
-    kstep = 64;
+    pl.tiles = cdiv(N, 16);
+    // about three thousand waves in flight over the GPU; no more waves than 32-wide K steps
+    int kw = pow2_at_least(cdiv(3000, pl.tiles * batch));
+    kw = std::min(kw, pl.mt == 1 ? 16 : 8);
+    while (kw > 1 && kw > K / 32) kw >>= 1;
+    pl.kw = kw;
+    return pl;
   }
-  const int nsteps = K / kstep;
+  const bool big = (M >= 1024 && N >= 1024);
+  pl.kind = big ? 2 : 1;
+  const int bm = big ? 256 : 128;
+  pl.tiles = cdiv(M, bm) * cdiv(N, bm);
+  const int nsteps = K / 64;
   int splits = 1;
   const int wgs = pl.tiles * batch;
   if (wgs < TARGET_WGS / 2) splits = cdiv(TARGET_WGS, wgs);
-  if (splits > nsteps) splits = nsteps;
-  if (splits < 1) splits = 1;
+  splits = std::max(1, std::min(splits, nsteps));
   const int steps_per = cdiv(nsteps, splits);
-  pl.ksplit = steps_per * kstep;
+  pl.ksplit = steps_per * 64;
   pl.splits = cdiv(nsteps, steps_per);
   return pl;
+}
+
+template <int MT, int TAG>
+void launch_wsplit(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+  dim3 grid(pl.tiles, 1, a.batch);
+  switch (pl.kw) {
+    case 1: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 1, TAG>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 2, TAG>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 4, TAG>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 8, TAG>), grid, dim3(512), 0, s, a); break;
+    default:
+      if constexpr (MT == 1) hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 16, TAG>), grid, dim3(1024), 0, s, a);
+      break;
+  }
+}
+
+template <int TAG>
+void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+  if (pl.kind == 0) {
+    if (pl.mt == 1) launch_wsplit<1, TAG>(a, pl, s);
+    else if (pl.mt == 2) launch_wsplit<2, TAG>(a, pl, s);
+    else launch_wsplit<4, TAG>(a, pl, s);
+    return;
+  }
+  dim3 grid(pl.tiles, pl.splits, a.batch);
+  if (pl.kind == 1)
+    hipLaunchKernelGGL((gemm_tile_kernel<128, 128, 2, 2, TAG>), grid, dim3(256), 0, s, a, pl.splits, pl.ksplit);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4, TAG>), grid, dim3(512), 0, s, a, pl.splits, pl.ksplit);
+  if (pl.splits > 1) {
+    dim3 rgrid((unsigned)(((int64_t)a.M * a.N + 255) / 256), a.batch);
+    hipLaunchKernelGGL((splitk_reduce_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
+  }
 }
 
 }  // namespace
@@ -317,35 +352,21 @@ int64_t gemm_part_floats(int M, int N, int K, int batch) {
   return pl.splits > 1 ? (int64_t)pl.splits * batch * M * N : 0;
 }
 
-int gemm_counters(int M, int N, int K, int batch) {
-  const Plan pl = plan_gemm(M, N, K, batch);
-  return pl.splits > 1 ? pl.tiles * batch : 0;
-}
+int gemm_counters(int, int, int, int) { return 0; }
 
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 128 != 0) return hipErrorInvalidValue;
   const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch);
-  if (pl.splits > 1) {
-    if ((int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap || pl.tiles * a.batch > a.counter_cap)
-      return hipErrorInvalidValue;
-  }
-  dim3 grid(pl.tiles, pl.splits, a.batch);
-  switch (pl.kind) {
-    case 0:
-      if (pl.mt == 1)
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, SKINNY_TN>), grid, dim3(256), 0, s, a, pl.splits, pl.ksplit);
-      else if (pl.mt == 2)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, SKINNY_TN>), grid, dim3(256), 0, s, a, pl.splits, pl.ksplit);
-      else
-        hipLaunchKernelGGL((gemm_skinny_kernel<4, SKINNY_TN>), grid, dim3(256), 0, s, a, pl.splits, pl.ksplit);
-      break;
-    case 1:
-      hipLaunchKernelGGL((gemm_tile_kernel<128, 128, 2, 2>), grid, dim3(256), 0, s, a, pl.splits, pl.ksplit);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_tile_kernel<256, 256, 2, 4>), grid, dim3(512), 0, s, a, pl.splits, pl.ksplit);
-      break;
+  if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
+  switch (a.tag) {
+    case TAG_QKVA: launch_tagged<TAG_QKVA>(a, pl, s); break;
+    case TAG_QB: launch_tagged<TAG_QB>(a, pl, s); break;
+    case TAG_KVB: launch_tagged<TAG_KVB>(a, pl, s); break;
+    case TAG_OPROJ: launch_tagged<TAG_OPROJ>(a, pl, s); break;
+    case TAG_ABSORB: launch_tagged<TAG_ABSORB>(a, pl, s); break;
+    case TAG_UV: launch_tagged<TAG_UV>(a, pl, s); break;
+    default: launch_tagged<TAG_NONE>(a, pl, s); break;
   }
   return hipGetLastError();
 }

@@ -17,7 +17,11 @@ enum Epilogue : int {
                  // values -> vt[(h*128+d) * vt_ld + key] (bf16, key-contiguous for P.V)
 };
 
+// Stage tags: one kernel symbol per projection so traces attribute time per stage.
+enum GemmTag : int { TAG_NONE = 0, TAG_QKVA = 1, TAG_QB = 2, TAG_KVB = 3, TAG_OPROJ = 4, TAG_ABSORB = 5, TAG_UV = 6 };
+
 struct GemmArgs {
+  int tag = TAG_NONE;
   const void* A = nullptr;  int64_t lda = 0, sA = 0;  // elements; sA = batch stride
   const void* B = nullptr;  int64_t ldb = 0, sB = 0;
   void* C = nullptr;        int64_t ldc = 0, sC = 0;

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/mla.h"
+#include "../../include/mla_test.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -394,7 +395,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   // 1. fused q_a | kv_a projection (fp32 out)
   mla_k::GemmArgs g = gemm_common(w, L);
   g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
-  g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32; g.tag = mla_k::TAG_QKVA;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 2. RMSNorms, RoPE of the shared key, latent entries into the cache
   mla_k::NormArgs na{};
@@ -405,7 +406,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   // 3. q_b
   g = gemm_common(w, L);
   g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
-  g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16;
+  g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_QB;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values
   for (int b = 0; b < B; ++b) {
@@ -413,7 +414,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     const int n = cache->len_h[sid] + q_start_h[b + 1] - q_start_h[b];
     g = gemm_common(w, L);
     g.A = (const uint8_t*)cache->data + cache->offset_h[sid] * (int64_t)eb; g.lda = eb / 2;
-    g.B = ctx->w_kvb; g.ldb = KV_LORA; g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB;
+    g.B = ctx->w_kvb; g.ldb = KV_LORA; g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB; g.tag = mla_k::TAG_KVB;
     g.knope = (uint16_t*)(w + L.knope); g.vt = (uint16_t*)(w + L.vt); g.vt_ld = L.vt_ld; g.key_base = kbase[b];
     HIP_TRY(mla_k::gemm_bf16(g, s));
   }
@@ -427,7 +428,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   // 6. o_proj
   g = gemm_common(w, L);
   g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
-  g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16;
+  g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 7. lengths
   HIP_TRY(mla_k::commit_lengths(seq_ids_d, q_start_d, cache->len_d, B, s));
@@ -462,7 +463,7 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   // 1. fused q_a | kv_a
   mla_k::GemmArgs g = gemm_common(w, L);
   g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
-  g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32; g.tag = mla_k::TAG_QKVA;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 2. norms + shared-key RoPE + append at position len; len_d advances by one here
   mla_k::NormArgs na{};
@@ -474,13 +475,13 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   // 3. q_b
   g = gemm_common(w, L);
   g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
-  g.M = B; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16;
+  g.M = B; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_QB;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched GEMM)
   g = gemm_common(w, L);
   g.A = w + L.q; g.lda = QB_N; g.sA = QK; g.B = ctx->w_ukT; g.ldb = NOPE; g.sB = (int64_t)KV_LORA * NOPE;
   g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.M = B; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
-  g.epi = mla_k::EPI_BF16;
+  g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_ABSORB;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 5. split attention over the latent cache + merge
   mla_k::DecodeAttnArgs da{};
@@ -495,13 +496,43 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
   g.B = (const uint16_t*)ctx->w_kvb + (int64_t)NOPE * KV_LORA; g.ldb = KV_LORA; g.sB = 256 * KV_LORA;
   g.C = w + L.o; g.ldc = O_IN; g.sC = VD; g.M = B; g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.epi = mla_k::EPI_BF16;
+  g.tag = mla_k::TAG_UV;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 7. o_proj
   g = gemm_common(w, L);
   g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
-  g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16;
+  g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
   HIP_TRY(mla_k::gemm_bf16(g, s));
   for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
+  return MLA_OK;
+}
+
+size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch) {
+  if (M <= 0 || N <= 0 || K <= 0 || batch <= 0 || K % 128) return 0;
+  return round_up(N_COUNTERS * sizeof(int), 256) + (size_t)mla_k::gemm_part_floats(M, N, K, batch) * 4;
+}
+
+mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const void* A, int64_t lda, int64_t sA,
+                         const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC, int32_t out_bf16,
+                         int32_t stage, void* ws, size_t ws_bytes, mla_stream stream) {
+  if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) return fail(MLA_E_ARG, "non-positive GEMM size");
+  if (K % 128) return fail(MLA_E_UNSUPPORTED, "K must be a multiple of 128");
+  if (!A || !B || !C || !ws) return fail(MLA_E_ARG, "a pointer argument is NULL");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(ws) || lda % 8 || ldb % 8 || (batch > 1 && (sA % 8 || sB % 8)))
+    return fail(MLA_E_ALIGN, "operand rows must start on 16-byte boundaries");
+  if (lda < K || ldb < K || ldc < N) return fail(MLA_E_SHAPE, "leading dimension smaller than the row");
+  if (stage < 0 || stage > MLA_STAGE_UV) return fail(MLA_E_ARG, "unknown stage %d", stage);
+  const size_t need = mla_test_gemm_workspace_bytes(M, N, K, batch);
+  if (ws_bytes < need) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  mla_k::GemmArgs g;
+  g.tag = stage;
+  g.A = A; g.lda = lda; g.sA = sA; g.B = B; g.ldb = ldb; g.sB = sB; g.C = C; g.ldc = ldc; g.sC = sC;
+  g.M = M; g.N = N; g.K = K; g.batch = batch; g.epi = out_bf16 ? mla_k::EPI_BF16 : mla_k::EPI_F32;
+  g.counters = (int*)ws;
+  g.counter_cap = N_COUNTERS;
+  g.part = (float*)((uint8_t*)ws + round_up(N_COUNTERS * sizeof(int), 256));
+  g.part_cap = mla_k::gemm_part_floats(M, N, K, batch);
+  HIP_TRY(mla_k::gemm_bf16(g, (hipStream_t)stream));
   return MLA_OK;
 }
 

@@ -183,3 +183,9 @@ def make_cache_entries(n: int, d: Dims = KIMI_K2, seed: int = 2000, latent_std: 
     lat = rng.normal(0.0, latent_std, size=(n, d.kv_lora))
     kpe = rng.normal(0.0, kpe_std, size=(n, d.rope))
     return f32_to_bf16_bits(np.concatenate([lat, kpe], axis=1).astype(np.float32))
+
+
+def make_activations(rows: int, cols: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """A [rows, cols] N(0, std) activation matrix in bf16 bits (e.g. an o_proj input)."""
+    rng = np.random.default_rng(seed)
+    return _normal_bf16(rng, (rows, cols), 0.0, std)

@@ -1,0 +1,72 @@
+"""GPU parity of the projection kernel (mla_test_gemm) against float64 matmul of the same bf16 bits.
+
+Covers the skinny (decode-sized M) and tile (prefill-sized M) kernels, split-K with its
+last-arrival reduction, batched per-head products with strides, and ragged M/N tails.
+"""
+import numpy as np
+import pytest
+
+from head_latent_attention_proj_amd import binding, synth
+from oracle import mla as omla
+
+from gpu_common import log
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_rand(shape, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    return synth.f32_to_bf16_bits(rng.normal(0, std, size=shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 2112, 7168), (1, 7168, 8192), (3, 12288, 1536), (16, 7168, 8192), (17, 2112, 7168),
+    (33, 16384, 512), (64, 7168, 8192), (65, 2112, 7168), (100, 12288, 1536), (128, 7168, 8192),
+    (300, 16384, 512), (1000, 2112, 7168), (1024, 1100, 1536), (2048, 7168, 8192),
+])
+def test_gemm_matches_float64(M, N, K):
+    import torch
+
+    log(f"gemm M={M} N={N} K={K}")
+    a = bf16_rand((M, K), 1 + M)
+    b = bf16_rand((N, K), 2 + N, std=0.02)
+    A, B = binding.bf16_tensor(a), binding.bf16_tensor(b)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    binding.Gemm()(A, B, C, M, N, K)
+    torch.cuda.synchronize()
+    ref = omla.linear(synth.bf16_bits_to_f64(a), synth.bf16_bits_to_f64(b))
+    got = C.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    scale = np.sqrt(K) * 0.02  # typical |ref|
+    log(f"  max err {err.max():.3e} (scale {scale:.3f})")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= 2e-5 * scale * 8
+
+
+def test_gemm_bf16_output_and_batched_strides():
+    """Per-head batched product with row/batch strides (the decode absorption layout)."""
+    import torch
+
+    log("batched gemm")
+    Bt, H = 5, 64
+    q = bf16_rand((Bt, H * 192), 11)
+    w = bf16_rand((H, 512, 128), 12, std=0.05)
+    Q, W = binding.bf16_tensor(q), binding.bf16_tensor(w)
+    out = torch.empty((Bt, H, 512), dtype=torch.bfloat16, device="cuda")
+    binding.Gemm()(Q, W, out, Bt, 512, 128, batch=H, lda=H * 192, sA=192, ldb=128, sB=512 * 128,
+                   ldc=H * 512, sC=512, stage="absorb")
+    torch.cuda.synchronize()
+    got = synth.bf16_bits_to_f64(binding.tensor_to_bf16_bits(out))
+    q64 = synth.bf16_bits_to_f64(q).reshape(Bt, H, 192)[:, :, :128]
+    ref = np.einsum("bhd,hcd->bhc", q64, synth.bf16_bits_to_f64(w))
+    err = np.abs(got - ref)
+    assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-6
+
+
+def test_gemm_rejects_bad_shapes():
+    import torch
+
+    A = torch.zeros((4, 130), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.MlaError):
+        binding.Gemm()(A, A, C, 4, 4, 130)
