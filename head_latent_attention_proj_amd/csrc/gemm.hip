@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 // ------------------------------------------------------------------------------------------
 template <int MT, int KW, int TAG>
 __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
-  constexpr int U = MT >= 4 ? 2 : 4;  // 32-wide K steps per pipeline stage
+  constexpr int U = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);  // 32-wide K steps per pipeline stage
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
@@ -192,10 +192,13 @@ __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
   const int batch = blockIdx.z;
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
-  const int nsteps = p.K >> 5;
-  const int spw = cdiv(nsteps, KW);
-  const int s0 = wave * spw;
-  const int s1 = min(nsteps, s0 + spw);
+  // K steps of this workgroup (blockIdx.y of gridDim.y splits), then of this wave
+  const int ysteps = cdiv(p.K >> 5, (int)gridDim.y);
+  const int y0 = blockIdx.y * ysteps;
+  const int y1 = min(p.K >> 5, y0 + ysteps);
+  const int spw = cdiv(y1 - y0, KW);
+  const int s0 = y0 + wave * spw;
+  const int s1 = min(y1, s0 + spw);
 
   // lane (l16, g): row l16 of the tile, features g*8 .. g*8+7 of each 32-wide step
   const uint16_t* pa[MT];
@@ -258,6 +261,17 @@ __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][e] += red[((w * MT + i) * 4 + e) * 64 + lane];
   }
+  if (gridDim.y > 1) {  // partial sum of this K split (EPI_F32 only; the consumer adds the parts)
+    float* C = (float*)p.C + blockIdx.y * p.c_split_stride + batch * p.sC;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = i * 16 + g * 4 + e, n = n0 + l16;
+        if (m < p.M && n < p.N) C[(int64_t)m * p.ldc + n] = acc[i][e];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -271,7 +285,7 @@ constexpr int TARGET_WGS = 512;  // two workgroups per CU on 256 CUs
 
 struct Plan {
   int kind;  // 0 wsplit, 1 tile128, 2 tile256
-  int mt, kw;
+  int mt, kw, ysplit;
   int splits, ksplit;
   int tiles;  // workgroups per (split, batch)
 };
@@ -282,18 +296,22 @@ int pow2_at_least(int v) {
   return p;
 }
 
-Plan plan_gemm(int M, int N, int K, int batch) {
+Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1) {
   Plan pl{};
   pl.splits = 1;
   pl.ksplit = K;
+  pl.ysplit = 1;
   if (M <= 64) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     pl.tiles = cdiv(N, 16);
+    // fewer tiles than CUs: split K over workgroups too (partials summed by the consumer)
+    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 256 && K / 32 >= 32 * pl.ysplit)
+      pl.ysplit *= 2;
     // about three thousand waves in flight over the GPU; no more waves than 32-wide K steps
-    int kw = pow2_at_least(cdiv(3000, pl.tiles * batch));
+    int kw = pow2_at_least(cdiv(3000, pl.tiles * batch * pl.ysplit));
     kw = std::min(kw, pl.mt == 1 ? 16 : 8);
-    while (kw > 1 && kw > K / 32) kw >>= 1;
+    while (kw > 1 && kw > K / 32 / pl.ysplit) kw >>= 1;
     pl.kw = kw;
     return pl;
   }
@@ -314,7 +332,7 @@ Plan plan_gemm(int M, int N, int K, int batch) {
 
 template <int MT, int TAG>
 void launch_wsplit(const GemmArgs& a, const Plan& pl, hipStream_t s) {
-  dim3 grid(pl.tiles, 1, a.batch);
+  dim3 grid(pl.tiles, pl.ysplit, a.batch);
   switch (pl.kw) {
     case 1: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 1, TAG>), grid, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 2, TAG>), grid, dim3(128), 0, s, a); break;
@@ -354,10 +372,14 @@ int64_t gemm_part_floats(int M, int N, int K, int batch) {
 
 int gemm_counters(int, int, int, int) { return 0; }
 
+int gemm_ysplit(const GemmArgs& a) {
+  return plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1).ysplit;
+}
+
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 128 != 0) return hipErrorInvalidValue;
-  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch);
+  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1);
   if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
   switch (a.tag) {
     case TAG_QKVA: launch_tagged<TAG_QKVA>(a, pl, s); break;

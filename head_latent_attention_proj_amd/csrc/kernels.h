@@ -36,6 +36,10 @@ struct GemmArgs {
   // B scales per (128-row block, 128-group) with row stride bs_ld floats.
   const float* a_scale = nullptr; int64_t as_ld = 0;
   const float* b_scale = nullptr; int64_t bs_ld = 0;
+  // Decode-sized M with EPI_F32 only: the K range may be split over `ysplit_max` workgroups,
+  // split y writing its partial sum to C + y * c_split_stride (the consumer adds the parts).
+  int ysplit_max = 1;
+  int64_t c_split_stride = 0;
   // split-K scratch (workspace): fp32 partials and per-tile arrival counters (kept zeroed)
   float* part = nullptr;
   int* counters = nullptr;
@@ -43,8 +47,11 @@ struct GemmArgs {
   int counter_cap = 0;      // counters available
 };
 
-// Chooses a tile kernel (large M) or a split-K skinny kernel (small M). Returns a hipError_t.
+// Chooses a tile kernel (large M) or the in-workgroup split-K kernel (small M). Returns a
+// hipError_t. gemm_ysplit() is the number of partial outputs a call writes (1 unless the
+// caller allowed a split of K over workgroups).
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s);
+int gemm_ysplit(const GemmArgs& a);
 hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s);
 // Bytes of split-K partials / counters the skinny path may need for an (M, N, K, batch) GEMM.
 int64_t gemm_part_floats(int M, int N, int K, int batch);
@@ -73,7 +80,9 @@ hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, in
 // through `meta`; decode (meta == nullptr): token b is sequence seq_ids[b] at position len[seq],
 // and len[seq] is advanced by one after the entry is written.
 struct NormArgs {
-  const float* cqkv;
+  const float* cqkv;     // [n_part][n][2112] partial sums (added here)
+  int n_part;
+  int64_t part_stride;   // floats between parts
   const uint16_t* g_q;
   const uint16_t* g_kv;
   float eps;

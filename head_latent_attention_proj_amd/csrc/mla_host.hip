@@ -107,6 +107,7 @@ PackedLayout packed_layout(const mla_config* c) {
 
 // ---- workspace planning ----------------------------------------------------------------------
 constexpr int N_COUNTERS = 16384;
+constexpr int QKVA_PARTS = 4;  // K splits of the fused q_a|kv_a projection at decode sizes
 constexpr int DECODE_MAX_WG = 2048;
 
 struct DecodePlan {
@@ -163,7 +164,7 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
     return o;
   };
   L.counters = take(N_COUNTERS * sizeof(int));
-  L.cqkv = take((size_t)ntok * QKVA_N * 4);
+  L.cqkv = take((size_t)ntok * QKVA_N * 4 * QKVA_PARTS);
   L.q_hat = take((size_t)ntok * Q_LORA * 2);
   L.q = take((size_t)ntok * QB_N * 2);
   L.o = take((size_t)ntok * O_IN * 2);
@@ -399,7 +400,8 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 2. RMSNorms, RoPE of the shared key, latent entries into the cache
   mla_k::NormArgs na{};
-  na.cqkv = (const float*)(w + L.cqkv); na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
+  na.cqkv = (const float*)(w + L.cqkv); na.n_part = 1; na.g_q = ctx->g_q; na.g_kv = ctx->g_kv;
+  na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = ntok; na.meta = meta; na.B = B;
   HIP_TRY(mla_k::norm_rope_append(na, s));
@@ -464,10 +466,13 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   mla_k::GemmArgs g = gemm_common(w, L);
   g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
   g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32; g.tag = mla_k::TAG_QKVA;
+  g.ysplit_max = QKVA_PARTS; g.c_split_stride = (int64_t)B * QKVA_N;
+  const int qkva_parts = mla_k::gemm_ysplit(g);
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 2. norms + shared-key RoPE + append at position len; len_d advances by one here
   mla_k::NormArgs na{};
-  na.cqkv = (const float*)(w + L.cqkv); na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
+  na.cqkv = (const float*)(w + L.cqkv); na.n_part = qkva_parts; na.part_stride = (int64_t)B * QKVA_N;
+  na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = B; na.meta = nullptr;
   na.seq_ids = seq_ids_d; na.offset = cache->offset_d; na.len = cache->len_d;

@@ -94,12 +94,18 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   }
 
   const float* row = a.cqkv + (int64_t)tok * QKVA_N;
+  // partial sums of a K-split projection are added in a fixed order
+  auto cval = [&](int c) {
+    float v = row[c];
+    for (int p = 1; p < a.n_part; ++p) v += row[p * a.part_stride + c];
+    return v;
+  };
   // ---- query latent RMSNorm (1536 = 6 per thread)
   float xq[6];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 6; ++i) {
-    xq[i] = row[tid + i * 256];
+    xq[i] = cval(tid + i * 256);
     ss += xq[i] * xq[i];
   }
   const float rq = 1.0f / sqrtf(block_sum256(ss, red) / (float)Q_LORA + a.eps);
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    xc[i] = row[Q_LORA + tid + i * 256];
+    xc[i] = cval(Q_LORA + tid + i * 256);
     ss += xc[i] * xc[i];
   }
   const float rc = 1.0f / sqrtf(block_sum256(ss, red) / (float)KV_LORA + a.eps);
@@ -162,8 +168,8 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   }
   // ---- shared rotary key: 32 pairs, rotated by this token's position
   if (tid < ROPE / 2) {
-    const float k0 = row[Q_LORA + KV_LORA + 2 * tid];
-    const float k1 = row[Q_LORA + KV_LORA + 2 * tid + 1];
+    const float k0 = cval(Q_LORA + KV_LORA + 2 * tid);
+    const float k1 = cval(Q_LORA + KV_LORA + 2 * tid + 1);
     const float c = a.rope_cs[(int64_t)pos * 32 + tid];
     const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + tid];
     uint16_t* kpe = (uint16_t*)(entry + (a.fp8 ? KV_LORA + 16 : KV_LORA * 2));
