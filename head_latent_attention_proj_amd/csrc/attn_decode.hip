@@ -1,20 +1,29 @@
-// Decode attention in the 512-feature latent space, split over positions, then merged.
+// Decode attention in the 512-feature latent space, split over positions, then merged and
+// mapped to the value heads.
 //
 // For one new token of a sequence holding L positions (this step's entry included), head h:
 //   s_j = scale * ( q_lat_h . c_hat_j + RoPE(q_pe_h) . k_pe_j ),  j = 0 .. L-1
 //   o_lat_h = sum_j softmax(s)_j c_hat_j                            (512 features)
+//   o_h = W_UV,h o_lat_h                                            (128 value features)
 // with q_lat_h = W_UK,h^T q_nope_h. This equals the pages' scores q.k over 192 features and the
-// value mix sum_j a_j v_j once W_UV,h is applied to o_lat_h afterwards (W_UK / W_UV are output
-// features 0..127 / 128..255 of each head's 256 in kv_b: "Key content up-projection" page,
-// Explanation). The cache therefore streams 1,152 bytes per position for all 64 heads at once
-// instead of 64 x (192 + 128) rebuilt features ("KV cache" page: 20,480 vs 576 values).
+// value mix sum_j a_j v_j (W_UK / W_UV are output features 0..127 / 128..255 of each head's 256
+// in kv_b: "Key content up-projection" page, Explanation). The cache therefore streams one
+// 576-feature entry per position for all 64 heads at once instead of 64 x (192 + 128) rebuilt
+// features ("KV cache" page: 20,480 vs 576 values per position).
+//
+// FP8 cache entries hold the latent as E4M3FN codes with one float32 scale per 128 features
+// (the quantised RMSNorm output, which is exactly what kv_b consumes). Codes are widened to bf16
+// exactly while staging; the group scales are applied per position to the partial scores of
+// each group and to the probabilities of the value mix, so no product is rounded before its
+// scale is applied.
 //
 // Work layout: one workgroup = (sequence, split of `chunk` positions), 8 waves = 4 head groups of
 // 16 x 2 feature halves. Heads are the MFMA column dimension, so one 32-position block staged in
 // LDS feeds every head: S^T = C Q^T (A = cache rows, B = queries held in registers), then
 // O^T = C^T P^T from a transposed copy of the block's latent part written while staging. The next
 // block's loads are in flight (in registers) while a block is used. Each split writes (max, sum,
-// unnormalised o) per head; the merge kernel combines the splits.
+// unnormalised o) per head; the merge kernel combines the splits, normalises and applies W_UV in
+// float32.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,10 +39,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
+// four E4M3FN codes (one 32-bit word) -> two packed bf16 pairs (exact)
+MLA_DEV u32x2_t e4m3x4_to_bf16(uint32_t w) {
+  const float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, 0), f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  const float f2 = __builtin_amdgcn_cvt_f32_fp8((int)w, 2), f3 = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  return u32x2_t{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+}
+
 // 8 waves: wave = hg + 4*lh, head group hg (heads hg*16 .. +15), half lh. A wave forms the
 // partial scores of its 16 heads over features [lh*288, lh*288+288) and, after the two halves
 // are added through LDS, mixes latent features [lh*256, lh*256+256). Two waves per SIMD hide
 // each other's LDS and memory latency; per-wave registers stay well under 256.
+template <bool FP8>
 __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   using namespace mla_dims;
   const int split = blockIdx.x, b = blockIdx.y;
@@ -44,6 +61,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int c1 = min(L, c0 + a.chunk);
   const int64_t slot0 = a.offset[seq];
   const int nblk = cdiv(c1 - c0, DKB);
+  const int eb = a.entry_bytes;
+  const int kpe_off = FP8 ? KV_LORA + 16 : KV_LORA * 2;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -53,73 +72,155 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];
   __shared__ __attribute__((aligned(16))) uint16_t sT[KV_LORA * LDT];
-  __shared__ __attribute__((aligned(16))) float xS[8][8][64];  // partial scores per wave
+  __shared__ __attribute__((aligned(16))) float xS[8][8][64];   // partial scores per wave
+  __shared__ __attribute__((aligned(16))) float sScale[DKB][4];  // FP8 group scales per position
+  // FP8: low bf16 halves of the float32 rotary key (high halves sit in sC)
+  __shared__ __attribute__((aligned(16))) uint16_t sKlo[FP8 ? DKB * 72 : 8];
 
-  // ---- staging through registers, one block ahead. Latent part as position pairs: item i (0..1)
-  // of a thread is pair kp = lane & 15 and 16-byte chunk ch = (lane >> 4) + 4*(wave + 8*i);
-  // k_pe: threads 0..255 one chunk each.
-  u32x4_t rl[2][2], rp;
+  // ---- staging through registers, one block ahead.
+  // bf16: latent part as position pairs, item i (0..1) of a thread is pair kp = lane & 15 and
+  //       16-byte chunk ch = (lane >> 4) + 4*(wave + 8*i) (8 features);
+  // FP8:  pair kp = tid & 15 and code chunk cc = tid >> 4 (16 features);
+  // k_pe: bf16 threads 0..255 one chunk each, FP8 (float32) every thread one chunk of 4 features;
+  // FP8 scales: threads 256..287 one position each.
+  u32x4_t rl[2][2], rp, rs;
   auto gload = [&](int blk) {
     const int kb = c0 + blk * DKB;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kp = lane & 15;
-      const int ch = (lane >> 4) + 4 * (wave + 8 * i);
+    if constexpr (FP8) {
+      const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int key = min(kb + 2 * kp + u, c1 - 1);  // past the split's end: re-read (masked)
-        rl[i][u] = ld16(a.cache + (slot0 + key) * a.entry_bytes + ch * 16);
+        rl[0][u] = ld16(a.cache + (slot0 + key) * eb + cc * 16);
+      }
+      if (tid >= 256 && tid < 256 + DKB) {
+        const int key = min(kb + (tid - 256), c1 - 1);
+        rs = ld16(a.cache + (slot0 + key) * eb + KV_LORA);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kp = lane & 15;
+        const int ch = (lane >> 4) + 4 * (wave + 8 * i);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int key = min(kb + 2 * kp + u, c1 - 1);
+          rl[i][u] = ld16(a.cache + (slot0 + key) * eb + ch * 16);
+        }
       }
     }
-    if (tid < 256) {
+    if constexpr (FP8) {
+      const int key = min(kb + (tid >> 4), c1 - 1);
+      rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 15) * 16);
+    } else if (tid < 256) {
       const int key = min(kb + (tid >> 3), c1 - 1);
-      rp = ld16(a.cache + (slot0 + key) * a.entry_bytes + KV_LORA * 2 + (tid & 7) * 16);
+      rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 7) * 16);
+    }
+  };
+  auto put_pair = [&](int kp, int f0, const u32x4_t& x4, const u32x4_t& y4) {
+    // 8 bf16 features f0.. of positions 2kp (x4) and 2kp+1 (y4): row-major and transposed copies
+    st16(sC + (2 * kp) * LDC + f0, x4);
+    st16(sC + (2 * kp + 1) * LDC + f0, y4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = x4[j], y = y4[j];
+      *reinterpret_cast<uint32_t*>(sT + (f0 + 2 * j) * LDT + 2 * kp) = (x & 0xffffu) | (y << 16);
+      *reinterpret_cast<uint32_t*>(sT + (f0 + 2 * j + 1) * LDT + 2 * kp) = (x >> 16) | (y & 0xffff0000u);
     }
   };
   auto sstore = [&]() {
+    if constexpr (FP8) {
+      const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kp = lane & 15;
-      const int ch = (lane >> 4) + 4 * (wave + 8 * i);
-      st16(sC + (2 * kp) * LDC + ch * 8, rl[i][0]);
-      st16(sC + (2 * kp + 1) * LDC + ch * 8, rl[i][1]);
+      for (int hlf = 0; hlf < 2; ++hlf) {  // codes 8*hlf .. 8*hlf+7 of the chunk
+        const u32x2_t x01 = e4m3x4_to_bf16(rl[0][0][2 * hlf]), x23 = e4m3x4_to_bf16(rl[0][0][2 * hlf + 1]);
+        const u32x2_t y01 = e4m3x4_to_bf16(rl[0][1][2 * hlf]), y23 = e4m3x4_to_bf16(rl[0][1][2 * hlf + 1]);
+        put_pair(kp, cc * 16 + hlf * 8, u32x4_t{x01[0], x01[1], x23[0], x23[1]},
+                 u32x4_t{y01[0], y01[1], y23[0], y23[1]});
+      }
+      if (tid >= 256 && tid < 256 + DKB) *reinterpret_cast<u32x4_t*>(&sScale[tid - 256][0]) = rs;
+      // rotary key: 4 float32 features -> bf16 high halves (sC) and low halves (sKlo)
+      const int pos = tid >> 4, f4 = (tid & 15) * 4;
+      float v[4], r[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t x = rl[i][0][j], y = rl[i][1][j];
-        // features ch*8 + 2j (low halves) and ch*8 + 2j + 1 (high halves), positions 2kp, 2kp+1
-        *reinterpret_cast<uint32_t*>(sT + (ch * 8 + 2 * j) * LDT + 2 * kp) = (x & 0xffffu) | (y << 16);
-        *reinterpret_cast<uint32_t*>(sT + (ch * 8 + 2 * j + 1) * LDT + 2 * kp) = (x >> 16) | (y & 0xffff0000u);
+        v[j] = __uint_as_float(rp[j]);
+        r[j] = v[j] - bf2f(f2bf(v[j]));
       }
+      *reinterpret_cast<u32x2_t*>(sC + pos * LDC + KV_LORA + f4) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2_t*>(sKlo + pos * 72 + f4) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kp = lane & 15;
+        const int ch = (lane >> 4) + 4 * (wave + 8 * i);
+        put_pair(kp, ch * 8, rl[i][0], rl[i][1]);
+      }
+      if (tid < 256) st16(sC + (tid >> 3) * LDC + KV_LORA + (tid & 7) * 8, rp);
     }
-    if (tid < 256) st16(sC + (tid >> 3) * LDC + KV_LORA + (tid & 7) * 8, rp);
   };
   gload(0);  // in flight during the query set-up
 
   // ---- query fragments (B operand): column = head, features lh*288 + ks*32 + g*8 .. +7;
   // features >= 512 are the rotary part, rotated here at the query's position
-  bf16x8_t qf[9];
+  // FP8: the queries are float32 and are carried as hi + lo bf16 fragments (about 16 bits)
+  bf16x8_t qf[9], ql_[FP8 ? 9 : 1];
   {
-    const uint16_t* ql = a.q_lat + ((int64_t)b * 64 + head) * KV_LORA;
-    const uint16_t* qp = a.q + ((int64_t)b * 64 + head) * QK + NOPE;
     const int pos = L - 1;
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks) {
       const int f = lh * HALF + ks * 32 + g * 8;
+      float v[8];
       if (f < KV_LORA) {
-        qf[ks] = as_bf16x8(ld16(ql + f));
+        if constexpr (FP8) {
+          const float* qlf = (const float*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f;
+          const float* qlr = qlf + a.q_lat_lo;
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qlf), v1 = *reinterpret_cast<const f32x4_t*>(qlf + 4);
+          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(qlr), r1 = *reinterpret_cast<const f32x4_t*>(qlr + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = v0[j] + r0[j];
+            v[4 + j] = v1[j] + r1[j];
+          }
+        } else {
+          qf[ks] = as_bf16x8(ld16((const uint16_t*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f));
+          continue;
+        }
       } else {
-        const u32x4_t raw = ld16(qp + (f - KV_LORA));
         const int pair0 = (f - KV_LORA) >> 1;
-        u32x4_t rot;
+        float x[8];
+        if constexpr (FP8) {
+          const float* qpf = (const float*)a.q + ((int64_t)b * 64 + head) * QK + NOPE + (f - KV_LORA);
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qpf), v1 = *reinterpret_cast<const f32x4_t*>(qpf + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j] = v0[j];
+            x[4 + j] = v1[j];
+          }
+        } else {
+          const u32x4_t raw = ld16((const uint16_t*)a.q + ((int64_t)b * 64 + head) * QK + NOPE + (f - KV_LORA));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf_lo(raw[j]);
+            x[2 * j + 1] = bf_hi(raw[j]);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x0 = bf_lo(raw[j]), x1 = bf_hi(raw[j]);
           const float c = a.rope_cs[(int64_t)pos * 32 + pair0 + j];
-          const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + pair0 + j];
-          rot[j] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+          const float sn = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + pair0 + j];
+          v[2 * j] = x[2 * j] * c - x[2 * j + 1] * sn;
+          v[2 * j + 1] = x[2 * j] * sn + x[2 * j + 1] * c;
         }
-        qf[ks] = as_bf16x8(rot);
       }
+      u32x4_t hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hi[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        lo[j] = pack_bf16x2(v[2 * j] - bf_lo(hi[j]), v[2 * j + 1] - bf_hi(hi[j]));
+      }
+      qf[ks] = as_bf16x8(hi);
+      if constexpr (FP8) ql_[ks] = as_bf16x8(lo);
     }
   }
 
@@ -136,22 +237,58 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     if (blk + 1 < nblk) gload(blk + 1);
     const int kb = c0 + blk * DKB;
 
-    // partial S^T[key][head] over this wave's 288 features, two key tiles
+    // partial S^T[key][head] over this wave's 288 features, two key tiles; in FP8 each 128-wide
+    // feature group is summed on its own and multiplied by its per-position scale
     f32x4_t sacc[2];
     sacc[0] = sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       const uint16_t* r0 = sC + l16 * LDC + lh * HALF + g * 8;
       const uint16_t* r1 = r0 + 16 * LDC;
-      bf16x8_t k0[9], k1[9];
+      if constexpr (FP8) {  // fragments read as used: the hi + lo queries already take 72 registers
+        f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
+        int cur = (lh * HALF) >> 7;
+        auto flush = [&](int grp) {
 #pragma unroll
-      for (int ks = 0; ks < 9; ++ks) {
-        k0[ks] = as_bf16x8(ld16(r0 + ks * 32));
-        k1[ks] = as_bf16x8(ld16(r1 + ks * 32));
-      }
+          for (int e = 0; e < 4; ++e) {
+            const float s0 = grp < 4 ? sScale[g * 4 + e][grp] : 1.0f;
+            const float s1 = grp < 4 ? sScale[16 + g * 4 + e][grp] : 1.0f;
+            sacc[0][e] += t0[e] * s0;
+            sacc[1][e] += t1[e] * s1;
+          }
+          t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        };
 #pragma unroll
-      for (int ks = 0; ks < 9; ++ks) {
-        sacc[0] = mfma_bf16_16x16x32(k0[ks], qf[ks], sacc[0]);
-        sacc[1] = mfma_bf16_16x16x32(k1[ks], qf[ks], sacc[1]);
+        for (int ks = 0; ks < 9; ++ks) {
+          const int f = lh * HALF + ks * 32;
+          const int grp = f < KV_LORA ? (f >> 7) : 4;
+          if (grp != cur) {
+            flush(cur);
+            cur = grp;
+          }
+          const bf16x8_t k0 = as_bf16x8(ld16(r0 + ks * 32)), k1 = as_bf16x8(ld16(r1 + ks * 32));
+          t0 = mfma_bf16_16x16x32(k0, qf[ks], t0);
+          t1 = mfma_bf16_16x16x32(k1, qf[ks], t1);
+          t0 = mfma_bf16_16x16x32(k0, ql_[ks], t0);
+          t1 = mfma_bf16_16x16x32(k1, ql_[ks], t1);
+          if (grp == 4) {  // float32 rotary key: add its low halves against the high query
+            const int fp = f - KV_LORA + g * 8;
+            t0 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + l16 * 72 + fp)), qf[ks], t0);
+            t1 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + (16 + l16) * 72 + fp)), qf[ks], t1);
+          }
+        }
+        flush(cur);
+      } else {
+        bf16x8_t k0[9], k1[9];
+#pragma unroll
+        for (int ks = 0; ks < 9; ++ks) {
+          k0[ks] = as_bf16x8(ld16(r0 + ks * 32));
+          k1[ks] = as_bf16x8(ld16(r1 + ks * 32));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 9; ++ks) {
+          sacc[0] = mfma_bf16_16x16x32(k0[ks], qf[ks], sacc[0]);
+          sacc[1] = mfma_bf16_16x16x32(k1[ks], qf[ks], sacc[1]);
+        }
       }
     }
     // add the other half's partial scores (same order in both waves of a pair)
@@ -194,12 +331,33 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
         psum += p;
       }
     lrun = lrun * alpha + psum;
-    u32x4_t w;
-    w[0] = pack_bf16x2(sv[0][0], sv[0][1]);
-    w[1] = pack_bf16x2(sv[0][2], sv[0][3]);
-    w[2] = pack_bf16x2(sv[1][0], sv[1][1]);
-    w[3] = pack_bf16x2(sv[1][2], sv[1][3]);
-    const bf16x8_t pf = as_bf16x8(w);
+    // probabilities as the B operand of the value mix (FP8: one copy per 128-feature group,
+    // each position's probability times that position's group scale)
+    // FP8 also keeps the low bf16 halves (pl) so the mix is exact to about 16 bits
+    bf16x8_t pf[2], pl[2];
+#pragma unroll
+    for (int q = 0; q < (FP8 ? 2 : 1); ++q) {
+      float s[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kt][e] = FP8 ? sv[kt][e] * sScale[kt * 16 + g * 4 + e][2 * lh + q] : sv[kt][e];
+      u32x4_t w, r;
+      w[0] = pack_bf16x2(s[0][0], s[0][1]);
+      w[1] = pack_bf16x2(s[0][2], s[0][3]);
+      w[2] = pack_bf16x2(s[1][0], s[1][1]);
+      w[3] = pack_bf16x2(s[1][2], s[1][3]);
+      pf[q] = as_bf16x8(w);
+      if constexpr (FP8) {
+        r[0] = pack_bf16x2(s[0][0] - bf_lo(w[0]), s[0][1] - bf_hi(w[0]));
+        r[1] = pack_bf16x2(s[0][2] - bf_lo(w[1]), s[0][3] - bf_hi(w[1]));
+        r[2] = pack_bf16x2(s[1][0] - bf_lo(w[2]), s[1][1] - bf_hi(w[2]));
+        r[3] = pack_bf16x2(s[1][2] - bf_lo(w[3]), s[1][3] - bf_hi(w[3]));
+        pl[q] = as_bf16x8(r);
+      }
+    }
+    if constexpr (!FP8) pf[1] = pf[0];
     // O^T[dim][head] += C^T[dim][keys] P^T[keys][head] over this wave's 256 latent features;
     // lane group g holds keys g*4..+3 and 16+g*4..+3
     {
@@ -213,9 +371,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
           hi[c] = ld8(tp + (c0_ + c) * 16 * LDT + 16);
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          oacc[c0_ + c] = mfma_bf16_16x16x32(as_bf16x8(u32x4_t{lo[c][0], lo[c][1], hi[c][0], hi[c][1]}), pf,
-                                             oacc[c0_ + c] * alpha);
+        for (int c = 0; c < 8; ++c) {
+          const bf16x8_t vt = as_bf16x8(u32x4_t{lo[c][0], lo[c][1], hi[c][0], hi[c][1]});
+          oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pf[c0_ >> 3], oacc[c0_ + c] * alpha);
+          if constexpr (FP8) oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pl[c0_ >> 3], oacc[c0_ + c]);
+        }
       }
     }
   }
@@ -233,68 +393,131 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   }
 }
 
-// One workgroup (256 threads) per (sequence, head): combine the splits, write bf16 o_lat.
-// Split statistics are read first (independent loads), then the partial outputs, eight splits
-// at a time so their loads overlap.
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
+// Merge of the splits and the value up-projection, float32 throughout. One workgroup per
+// (head, tile of up to MBT sequences):
+//   1. per sequence: o_lat = sum_s exp(m_s - m) o_s / sum_s exp(m_s - m) l_s   (LDS, float32)
+//   2. o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][c], W_UV,h = kv_b rows h*256+128 .. +255
+//      (FP8: code * block scale, exact in float32); thread = (d, half of c), halves added in LDS.
+constexpr int MBT = 16;
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void decode_merge_uv_kernel(DecodeAttnArgs a) {
   using namespace mla_dims;
-  const int head = blockIdx.x, b = blockIdx.y;
-  const int L = a.len[a.seq_ids[b]];
-  const int ns = cdiv(L, a.chunk);
-  const int64_t base = (int64_t)b * a.max_splits * 64 + head;
-  __shared__ float wsh[2048];
-  __shared__ float red[4];
-  float mx = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += 256) mx = fmaxf(mx, a.part_ml[(base + (int64_t)s * 64) * 2]);
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float lpart = 0.f;
-  for (int s = threadIdx.x; s < ns; s += 256) {
-    const int64_t p = base + (int64_t)s * 64;
-    const float w = exp2f(a.part_ml[p * 2] - mx);
-    wsh[s] = w;
-    lpart += w * a.part_ml[p * 2 + 1];
-  }
-  __syncthreads();
-  lpart = wave_sum(lpart);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = lpart;
-  __syncthreads();
-  const float l = red[0] + red[1] + red[2] + red[3];
-  const int c = threadIdx.x * 2;
-  float o0 = 0.f, o1 = 0.f;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    f32x2_t v[8];
+  const int h = blockIdx.x, bt = blockIdx.y * MBT;
+  const int nb = min(MBT, a.B - bt);
+  __shared__ __attribute__((aligned(16))) float olat[MBT][KV_LORA];
+  __shared__ float red[MBT][128];
+  const int tid = threadIdx.x;
+
+  // -- 1. merge: tps threads per sequence, dpt = 512 / tps features each
+  int tps = 256;
+  while (tps > 16 && tps * nb > 256) tps >>= 1;
+  {
+    const int bi = tid / tps, part = tid % tps;
+    if (bi < nb) {
+      const int b = bt + bi;
+      const int L = a.len[a.seq_ids[b]];
+      const int ns = cdiv(L, a.chunk);
+      const int64_t base = (int64_t)b * a.max_splits * 64 + h;
+      float mx = -INFINITY;
+      for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(base + (int64_t)s * 64) * 2]);
+      float l = 0.f;
+      const int dpt = KV_LORA / tps;
+      float o[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const f32x2_t*>(a.part_o + (base + (int64_t)(s + u) * 64) * KV_LORA + c);
+      for (int j = 0; j < 32; ++j) o[j] = 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const int64_t p = base + (int64_t)s * 64;
+        const float w = exp2f(a.part_ml[p * 2] - mx);
+        l += w * a.part_ml[p * 2 + 1];
+        const float* src = a.part_o + p * KV_LORA + part * dpt;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      o0 += wsh[s + u] * v[u][0];
-      o1 += wsh[s + u] * v[u][1];
+        for (int j = 0; j < 32; j += 2) {
+          if (j < dpt) {
+            const f32x2_t v = *reinterpret_cast<const f32x2_t*>(src + j);
+            o[j] += w * v[0];
+            o[j + 1] += w * v[1];
+          }
+        }
+      }
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < dpt) olat[bi][part * dpt + j] = o[j] * inv;
     }
   }
-  for (; s < ns; ++s) {
-    const f32x2_t v = *reinterpret_cast<const f32x2_t*>(a.part_o + (base + (int64_t)s * 64) * KV_LORA + c);
-    o0 += wsh[s] * v[0];
-    o1 += wsh[s] * v[1];
+  __syncthreads();
+
+  // -- 2. value up-projection
+  const int d = tid & 127, ch = tid >> 7;
+  float acc[MBT];
+#pragma unroll
+  for (int bi = 0; bi < MBT; ++bi) acc[bi] = 0.f;
+  const int64_t wrow = (int64_t)(h * 256 + 128 + d) * KV_LORA + ch * 256;
+  for (int c = 0; c < 256; c += 8) {
+    float w[8];
+    if constexpr (FP8) {
+      const u32x2_t codes = ld8((const uint8_t*)a.w_uv + wrow + c);
+      const float sc = a.w_uv_s[(2 * h + 1) * 4 + ((ch * 256 + c) >> 7)];
+      w[0] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 0) * sc;
+      w[1] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 1) * sc;
+      w[2] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 2) * sc;
+      w[3] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 3) * sc;
+      w[4] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 0) * sc;
+      w[5] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 1) * sc;
+      w[6] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 2) * sc;
+      w[7] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 3) * sc;
+    } else {
+      const u32x4_t raw = ld16((const uint16_t*)a.w_uv + wrow + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[2 * j] = bf_lo(raw[j]);
+        w[2 * j + 1] = bf_hi(raw[j]);
+      }
+    }
+#pragma unroll
+    for (int bi = 0; bi < MBT; ++bi) {
+      if (bi < nb) {
+        const float* ol = &olat[bi][ch * 256 + c];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[bi] += w[j] * ol[j];
+      }
+    }
   }
-  const float inv = 1.0f / l;
-  *reinterpret_cast<uint32_t*>(a.o_lat + ((int64_t)b * 64 + head) * KV_LORA + c) = pack_bf16x2(o0 * inv, o1 * inv);
+  if (ch == 1) {
+#pragma unroll
+    for (int bi = 0; bi < MBT; ++bi) red[bi][d] = acc[bi];
+  }
+  __syncthreads();
+  if (ch == 0) {
+#pragma unroll
+    for (int bi = 0; bi < MBT; ++bi) {
+      if (bi < nb) {
+        const float v = acc[bi] + red[bi][d];
+        const int64_t oi = (int64_t)(bt + bi) * O_IN + h * 128 + d;
+        if (a.o_f32) a.o_f32[oi] = v;
+        else a.o_bf16[oi] = f2bf(v);
+      }
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  if (a.fp8) return hipErrorNotSupported;
-  if (a.max_splits > 2048) return hipErrorInvalidValue;  // the merge keeps split weights in LDS
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(a.max_splits, a.B), dim3(512), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(64, a.B), dim3(256), 0, s, a);
+  dim3 g1(a.max_splits, a.B), g2(64, cdiv(a.B, MBT));
+  if (a.fp8) {
+    hipLaunchKernelGGL(decode_attn_kernel<true>, g1, dim3(512), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_uv_kernel<true>, g2, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(decode_attn_kernel<false>, g1, dim3(512), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_uv_kernel<false>, g2, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -30,7 +30,12 @@ constexpr float LOG2E = 1.4426950408889634f;
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 MLA_DEV void st8(void* p, const u32x2_t& v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
+// SPLIT (FP8 weights): q arrives in float32 and K_nope, V^T, k_pe and the probabilities carry a
+// bf16 residual next to their bf16 value; each product takes hi*hi + hi*lo + lo*hi, which is
+// accurate to about 16 significant bits (the FP8 path's o_proj quantiser amplifies any rounding
+// of its input, so bf16 alone is not enough there).
+template <bool SPLIT>
+__global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(PrefillAttnArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.z;
   const SeqMeta m = a.meta[b];
@@ -48,32 +53,61 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[PKB * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[128 * LDV];
+  __shared__ __attribute__((aligned(16))) uint16_t sKl[SPLIT ? PKB * LDK : 8];  // residual planes
+  __shared__ __attribute__((aligned(16))) uint16_t sVl[SPLIT ? 128 * LDV : 8];
 
   // ---- Q fragments: B operand of S^T, column = query, 8 features of group g per k-step
-  bf16x8_t qf[2][6];
+  bf16x8_t qf[2][6], ql[SPLIT ? 2 : 1][6];
   int qpos[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qrel = q0 + wave * 32 + qt * 16 + l16;
     qpos[qt] = m.l0 + qrel;
     const int qi = min(qrel, m.t - 1);
-    const uint16_t* qrow = a.q + ((int64_t)(m.q0 + qi) * 64 + h) * 192;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[qt][ks] = as_bf16x8(ld16(qrow + ks * 32 + g * 8));
+    const int64_t qoff = ((int64_t)(m.q0 + qi) * 64 + h) * 192;
     const int pos = m.l0 + qi;
 #pragma unroll
-    for (int ks = 4; ks < 6; ++ks) {
-      const u32x4_t raw = ld16(qrow + ks * 32 + g * 8);
-      u32x4_t rot;
-      const int pair0 = ((ks - 4) * 32 + g * 8) >> 1;
+    for (int ks = 0; ks < 6; ++ks) {
+      float x[8];
+      if constexpr (SPLIT) {
+        const float* qf32 = (const float*)a.q + qoff + ks * 32 + g * 8;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qf32), v1 = *reinterpret_cast<const f32x4_t*>(qf32 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = v0[j];
+          x[4 + j] = v1[j];
+        }
+      } else {
+        const u32x4_t raw = ld16((const uint16_t*)a.q + qoff + ks * 32 + g * 8);
+        if (ks < 4) {
+          qf[qt][ks] = as_bf16x8(raw);
+          continue;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = bf_lo(raw[j]);
+          x[2 * j + 1] = bf_hi(raw[j]);
+        }
+      }
+      if (ks >= 4) {  // rotary part, rotated at the query's position
+        const int pair0 = ((ks - 4) * 32 + g * 8) >> 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float c = a.rope_cs[(int64_t)pos * 32 + pair0 + j];
+          const float sn = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + pair0 + j];
+          const float x0 = x[2 * j], x1 = x[2 * j + 1];
+          x[2 * j] = x0 * c - x1 * sn;
+          x[2 * j + 1] = x0 * sn + x1 * c;
+        }
+      }
+      u32x4_t hi, lo;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x0 = bf_lo(raw[j]), x1 = bf_hi(raw[j]);
-        const float c = a.rope_cs[(int64_t)pos * 32 + pair0 + j];
-        const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + pair0 + j];
-        rot[j] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+        hi[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        lo[j] = pack_bf16x2(x[2 * j] - bf_lo(hi[j]), x[2 * j + 1] - bf_hi(hi[j]));
       }
-      qf[qt][ks] = as_bf16x8(rot);
+      qf[qt][ks] = as_bf16x8(hi);
+      if constexpr (SPLIT) ql[qt][ks] = as_bf16x8(lo);
     }
   }
 
@@ -82,6 +116,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const int kr = tid >> 4, kc = (tid & 15) * 8;   // K_nope: 16 threads per key row (256 B)
   const int pr = tid >> 3, pc = (tid & 7) * 8;    // k_pe / V^T: 8 threads per 128-byte row
   auto gload = [&](int blk) {
+    if constexpr (SPLIT) return;  // split staging loads and stores in one step (stage_split)
     const int kb = blk * PKB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -111,7 +146,61 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         }
     }
   };
-  auto sstore = [&]() {
+  // Split staging: hi and lo planes of K_nope and V^T, float32 k_pe split on the way to LDS.
+  // Loads are not held across the block's math (the registers hold the split queries instead).
+  auto stage_split = [&](int blk) {
+    const int kb = blk * PKB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(kb + i * 16 + kr, n_keys - 1);
+      const int64_t off = ((int64_t)(m.kbase + key) * 64 + h) * 128 + kc;
+      const u32x4_t x = ld16(a.knope + off), y = ld16(a.knope_lo + off);
+      st16(sK + (i * 16 + kr) * LDK + kc, x);
+      st16(sKl + (i * 16 + kr) * LDK + kc, y);
+    }
+    {
+      const int key = min(kb + (tid >> 2), n_keys - 1);
+      const float* kp = (const float*)(a.cache + (m.slot0 + key) * a.entry_bytes + a.kpe_off) + (tid & 3) * 16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(kp + 4 * c);
+        const uint32_t h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
+        const uint32_t r0 = pack_bf16x2(v[0] - bf_lo(h0), v[1] - bf_hi(h0));
+        const uint32_t r1 = pack_bf16x2(v[2] - bf_lo(h1), v[3] - bf_hi(h1));
+        const int col = 128 + (tid & 3) * 16 + 4 * c;
+        st8(sK + (tid >> 2) * LDK + col, u32x2_t{h0, h1});
+        st8(sKl + (tid >> 2) * LDK + col, u32x2_t{r0, r1});
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + pr;
+      const int64_t off = (int64_t)(h * 128 + row) * a.vt_ld + m.kbase + kb + pc;
+      u32x4_t x = ld16(a.vt + off), y = ld16(a.vt_lo + off);
+      if (kb + PKB > n_keys) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kb + pc + 2 * j;
+          uint32_t mask = 0xffffffffu;
+          if (key >= n_keys) mask &= 0xffff0000u;
+          if (key + 1 >= n_keys) mask &= 0x0000ffffu;
+          x[j] &= mask;
+          y[j] &= mask;
+        }
+      }
+      uint16_t* d = sV + row * LDV + pc;
+      st8(d, u32x2_t{x[0], x[1]});
+      st8(d + 4, u32x2_t{x[2], x[3]});
+      uint16_t* dl = sVl + row * LDV + pc;
+      st8(dl, u32x2_t{y[0], y[1]});
+      st8(dl + 4, u32x2_t{y[2], y[3]});
+    }
+  };
+  auto sstore = [&](int blk) {
+    if constexpr (SPLIT) {
+      stage_split(blk);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) st16(sK + (i * 16 + kr) * LDK + kc, pk[i]);
 #pragma unroll
@@ -137,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   gload(0);
   for (int blk = 0; blk < nblk; ++blk) {
     __syncthreads();
-    sstore();
+    sstore(blk);
     __syncthreads();
     if (blk + 1 < nblk) gload(blk + 1);
     const int kb = blk * PKB;
@@ -155,11 +244,23 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       for (int kt = 0; kt < 4; ++kt) {
         sacc[kt][0] = mfma_bf16_16x16x32(kf[kt], qf[0][ks], sacc[kt][0]);
         sacc[kt][1] = mfma_bf16_16x16x32(kf[kt], qf[1][ks], sacc[kt][1]);
+        if constexpr (SPLIT) {
+          sacc[kt][0] = mfma_bf16_16x16x32(kf[kt], ql[0][ks], sacc[kt][0]);
+          sacc[kt][1] = mfma_bf16_16x16x32(kf[kt], ql[1][ks], sacc[kt][1]);
+        }
+      }
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8_t kl = as_bf16x8(ld16(sKl + (kt * 16 + l16) * LDK + ks * 32 + g * 8));
+          sacc[kt][0] = mfma_bf16_16x16x32(kl, qf[0][ks], sacc[kt][0]);
+          sacc[kt][1] = mfma_bf16_16x16x32(kl, qf[1][ks], sacc[kt][1]);
+        }
       }
     }
 
     const bool need_mask = kb + PKB - 1 > wq_lo;
-    bf16x8_t pf[2][2];
+    bf16x8_t pf[2][2], pl[SPLIT ? 2 : 1][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float bmax = -INFINITY;
@@ -197,6 +298,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         w[2] = pack_bf16x2(sacc[2 * ps + 1][qt][0], sacc[2 * ps + 1][qt][1]);
         w[3] = pack_bf16x2(sacc[2 * ps + 1][qt][2], sacc[2 * ps + 1][qt][3]);
         pf[ps][qt] = as_bf16x8(w);
+        if constexpr (SPLIT) {
+          u32x4_t r;
+          r[0] = pack_bf16x2(sacc[2 * ps][qt][0] - bf_lo(w[0]), sacc[2 * ps][qt][1] - bf_hi(w[0]));
+          r[1] = pack_bf16x2(sacc[2 * ps][qt][2] - bf_lo(w[1]), sacc[2 * ps][qt][3] - bf_hi(w[1]));
+          r[2] = pack_bf16x2(sacc[2 * ps + 1][qt][0] - bf_lo(w[2]), sacc[2 * ps + 1][qt][1] - bf_hi(w[2]));
+          r[3] = pack_bf16x2(sacc[2 * ps + 1][qt][2] - bf_lo(w[3]), sacc[2 * ps + 1][qt][3] - bf_hi(w[3]));
+          pl[ps][qt] = as_bf16x8(r);
+        }
       }
     }
     // O^T[d][q] += V^T[d][keys] P^T[keys][q]; lane group g holds keys {g*4..+3, 16+g*4..+3}
@@ -209,6 +318,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         const bf16x8_t vf = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
         oacc[d][0] = mfma_bf16_16x16x32(vf, pf[ps][0], oacc[d][0]);
         oacc[d][1] = mfma_bf16_16x16x32(vf, pf[ps][1], oacc[d][1]);
+        if constexpr (SPLIT) {
+          const uint16_t* vl = sVl + (d * 16 + l16) * LDV + ps * 32 + g * 4;
+          const u32x2_t lo2 = ld8(vl), hi2 = ld8(vl + 16);
+          const bf16x8_t vfl = as_bf16x8(u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]});
+          oacc[d][0] = mfma_bf16_16x16x32(vf, pl[ps][0], oacc[d][0]);
+          oacc[d][1] = mfma_bf16_16x16x32(vf, pl[ps][1], oacc[d][1]);
+          oacc[d][0] = mfma_bf16_16x16x32(vfl, pf[ps][0], oacc[d][0]);
+          oacc[d][1] = mfma_bf16_16x16x32(vfl, pf[ps][1], oacc[d][1]);
+        }
       }
   }
 
@@ -241,7 +359,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.max_t <= 0) return hipSuccess;
   dim3 grid(64, cdiv(a.max_t, PQ), a.B);
-  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, s, a);
+  if (a.split)
+    hipLaunchKernelGGL(prefill_attn_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ constexpr int KVB_N = HEADS * (NOPE + VD);  // 16384
 constexpr int QB_N = HEADS * QK;         // 12288
 constexpr int O_IN = HEADS * VD;         // 8192
 constexpr int BF16_ENTRY_BYTES = ENTRY * 2;                 // 1152
-constexpr int FP8_ENTRY_BYTES = KV_LORA + 16 + ROPE * 2;    // 656: codes | 4 scales | k_pe
+constexpr int FP8_ENTRY_BYTES = KV_LORA + 16 + ROPE * 4;    // 784: codes | 4 scales | k_pe (fp32)
 }  // namespace mla_dims
 
 MLA_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

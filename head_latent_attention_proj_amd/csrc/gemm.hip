@@ -26,6 +26,7 @@ namespace mla_k {
 namespace {
 
 MLA_DEV void epi_store(const GemmArgs& p, int b, int m, int n, float v) {
+  if (p.c_scale) v *= p.c_scale[b * p.cs_stride + (n >> 7)];
   if (p.epi == EPI_F32) {
     ((float*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = v;
   } else if (p.epi == EPI_BF16) {

@@ -1,8 +1,479 @@
-// FP8 (OCP E4M3FN, 128x128 block-scaled weights, 1x128 dynamic activations) GEMM.
-// Placeholder entry until the FP8 kernels land: reports "not supported".
+// FP8 (OCP E4M3FN) projections: weights with one float32 scale per 128 x 128 block, activations
+// quantised per token and per aligned group of 128 features ("Key-value latent" page, linear
+// excerpt: quantization_config fmt e4m3, weight_block_size [128, 128], activation_scheme dynamic).
+//
+// C[m][n] = sum over 128-wide K groups kg of  sa[m][kg] * sb[n/128][kg] * sum_{k in kg} a[m][k] b[n][k]
+// with a, b the code values. Each K group's partial sum is formed on the matrix cores and then
+// scaled and accumulated in float32 registers. Two ways to form it:
+//   * native: one 16x16x128 FP8 MFMA (unit hardware scales) per group. Measured on gfx950, this
+//     instruction (and the 16x16x32 FP8 form) sums its products to only about 1e-4 of sum |a b|,
+//     far coarser than float32.
+//   * precise: the codes are widened to bf16 (exact: every E4M3 value is a bf16 value) and the
+//     group is summed by four 16x16x32 bf16 MFMAs, which accumulate in float32 (~1e-7).
+// Projections whose outputs are quantised again or feed the attention (q_a|kv_a, q_b, kv_b) take
+// the precise form, so that the activation quantisers downstream see float32-accurate inputs;
+// o_proj, whose output is the layer output, takes the native form.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace mla_k {
-hipError_t gemm_fp8(const GemmArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// D = A(16x128 e4m3) * B(128x16 e4m3), hardware block scales fixed at 1 (E8M0 127).
+MLA_DEV f32x4_t mfma_fp8_16x16x128(const i32x8_t& a, const i32x8_t& b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7f7f7f7f, 0,
+                                                          0x7f7f7f7f);
+}
+
+// eight E4M3 codes (two words) -> eight bf16 values, exact (unit conversion scale)
+MLA_DEV bf16x8_t widen8(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One K group (128) of a 16x16 tile in float32 precision: the lane's 32 codes of A and B
+// (k = g*32 .. g*32+31 of the group) in four bf16 MFMA steps of eight codes each.
+MLA_DEV f32x4_t group_precise(const i32x8_t& a, const bf16x8_t (&bw)[4]) {
+  f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) d = mfma_bf16_16x16x32(widen8(a[2 * s], a[2 * s + 1]), bw[s], d);
+  return d;
+}
+
+MLA_DEV i32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+MLA_DEV void epi_store8(const GemmArgs& p, int b, int m, int n, float v) {
+  if (p.epi == EPI_F32) {
+    ((float*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = v;
+  } else if (p.epi == EPI_BF16) {
+    ((uint16_t*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = f2bf(v);
+  } else {  // EPI_KVB; with knope_lo / vt_lo set, the bf16 residual goes to a second plane
+    const int h = n >> 8, r = n & 255;
+    const int64_t key = p.key_base + m;
+    const uint16_t hi = f2bf(v);
+    const uint16_t lo = f2bf(v - bf2f(hi));
+    if (r < 128) {
+      const int64_t i = key * 8192 + h * 128 + r;
+      p.knope[i] = hi;
+      if (p.knope_lo) p.knope_lo[i] = lo;
+    } else {
+      const int64_t i = (int64_t)(h * 128 + r - 128) * p.vt_ld + key;
+      p.vt[i] = hi;
+      if (p.vt_lo) p.vt_lo[i] = lo;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-sized M: one workgroup per 16-column tile, K groups split across its KW waves,
+// partial tiles summed through LDS in a fixed order.
+// ------------------------------------------------------------------------------------------
+template <int MT, int KW, int TAG, bool PREC>
+__global__ __launch_bounds__(KW * 64) void gemm_fp8_wsplit_kernel(GemmArgs p) {
+  constexpr int U = MT >= 4 ? 1 : (MT == 2 ? 2 : 4);  // K groups per pipeline stage
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int batch = blockIdx.z;
+  const uint8_t* A = (const uint8_t*)p.A + batch * p.sA;
+  const uint8_t* B = (const uint8_t*)p.B + batch * p.sB;
+  const int ngroups = p.K >> 7;
+  const int ygroups = cdiv(ngroups, (int)gridDim.y);
+  const int y0 = blockIdx.y * ygroups, y1 = min(ngroups, y0 + ygroups);
+  const int gpw = cdiv(y1 - y0, KW);
+  const int k0 = y0 + wave * gpw, k1 = min(y1, k0 + gpw);
+
+  int rows[MT];
+  const uint8_t* pa[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    rows[i] = min(i * 16 + l16, p.M - 1);
+    pa[i] = A + (int64_t)rows[i] * p.lda + g * 32;
+  }
+  const uint8_t* pb = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + g * 32;
+  const float* sbp = p.b_scale + (int64_t)(min(n0, p.N - 1) >> 7) * p.bs_ld;
+  // a-scale rows of this lane's result values: m = i*16 + g*4 + e
+  const float* sap[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sap[i][e] = p.a_scale + (int64_t)min(i * 16 + g * 4 + e, p.M - 1) * p.as_ld;
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (k0 < k1) {
+    for (int kg = k0; kg < k1; kg += U) {
+      i32x8_t af[U][MT], bf[U];
+      float sb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(kg + u, k1 - 1);
+        bf[u] = cat8(ld16(pb + kk * 128), ld16(pb + kk * 128 + 16));
+        sb[u] = sbp[kk];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) af[u][i] = cat8(ld16(pa[i] + kk * 128), ld16(pa[i] + kk * 128 + 16));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (kg + u >= k1) break;  // wave-uniform
+        bf16x8_t bw[4];
+        if constexpr (PREC) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) bw[st] = widen8(bf[u][2 * st], bf[u][2 * st + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const f32x4_t d = PREC ? group_precise(af[u][i], bw) : mfma_fp8_16x16x128(af[u][i], bf[u]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] += d[e] * (sap[i][e][kg + u] * sb[u]);
+        }
+      }
+    }
+  }
+
+  if constexpr (KW > 1) {
+    __shared__ float red[(KW - 1) * MT * 4 * 64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(((wave - 1) * MT + i) * 4 + e) * 64 + lane] = acc[i][e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] += red[((w * MT + i) * 4 + e) * 64 + lane];
+  }
+  if (gridDim.y > 1) {  // partial sum of this K split (EPI_F32 only; the consumer adds the parts)
+    float* C = (float*)p.C + blockIdx.y * p.c_split_stride + batch * p.sC;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = i * 16 + g * 4 + e, n = n0 + l16;
+        if (m < p.M && n < p.N) C[(int64_t)m * p.ldc + n] = acc[i][e];
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = i * 16 + g * 4 + e, n = n0 + l16;
+      if (m < p.M && n < p.N) epi_store8(p, batch, m, n, acc[i][e]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Prefill-sized M: BM x BN tile (128 x 256 or 128 x 128), one 128-wide K group per stage staged
+// through LDS (144-byte
+// rows: 8 consecutive rows hit 8 distinct 16-byte bank groups), double buffered.
+// ------------------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int TAG, bool PREC>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, int splits, int ksplit) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 128;        // bytes (= codes) per row per stage: one K group
+  constexpr int LDK = BK + 16;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int CPR = BK / 16;
+  constexpr int RPP = NT / CPR;
+  constexpr int AP = BM / RPP, BP = BN / RPP;
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of rows per pass");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
+  const int ntile = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((ntile & 7) == 0) bid = (bid & 7) * (ntile >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int fm = (bid / per_group) * GM;
+  const int gs = min(tiles_m - fm, GM);
+  const int tm = fm + (bid % per_group) % gs;
+  const int tn = (bid % per_group) / gs;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int batch = blockIdx.z, split = blockIdx.y;
+
+  const uint8_t* A = (const uint8_t*)p.A + batch * p.sA;
+  const uint8_t* B = (const uint8_t*)p.B + batch * p.sB;
+
+  const int lr = tid / CPR, lc = (tid % CPR) * 16;
+  const uint8_t* ga[AP];
+  const uint8_t* gb[BP];
+#pragma unroll
+  for (int i = 0; i < AP; ++i) ga[i] = A + (int64_t)min(m0 + i * RPP + lr, p.M - 1) * p.lda + lc;
+#pragma unroll
+  for (int i = 0; i < BP; ++i) gb[i] = B + (int64_t)min(n0 + i * RPP + lr, p.N - 1) * p.ldb + lc;
+
+  // scale rows of this lane's results: m = mrow0 + i*16 + e (clamped), column block of tile j
+  const int mrow0 = m0 + wm * WTM + g * 4;
+  const int ncol0 = n0 + wn * WTN;
+
+  u32x4_t ra[AP], rb[BP];
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int kb = split * ksplit;
+  const int ke = min(p.K, kb + ksplit);
+  const int nk = (ke - kb) / BK;
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) ra[i] = ld16(ga[i] + k0);
+#pragma unroll
+    for (int i = 0; i < BP; ++i) rb[i] = ld16(gb[i] + k0);
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* sa = smem + buf * (BM + BN) * LDK;
+    uint8_t* sb = sa + BM * LDK;
+#pragma unroll
+    for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lc, ra[i]);
+#pragma unroll
+    for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lc, rb[i]);
+  };
+
+  if (nk > 0) {
+    gload(kb);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const int kg = (kb >> 7) + kt;
+    if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
+    float sa[TM][4], sbv[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sa[i][e] = p.a_scale[(int64_t)min(mrow0 + i * 16 + e, p.M - 1) * p.as_ld + kg];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sbv[j] = p.b_scale[(int64_t)(min(ncol0 + j * 16, p.N - 1) >> 7) * p.bs_ld + kg];
+    const uint8_t* sA = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK + g * 32;
+    const uint8_t* sB = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK + g * 32;
+    if constexpr (PREC) {
+      // four steps of eight codes (k = g*32 + st*8 ..) widened to bf16 as they are read
+      f32x4_t d[TM][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) d[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8_t bw[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sB + j * 16 * LDK + st * 8);
+          bw[j] = widen8(r[0], r[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sA + i * 16 * LDK + st * 8);
+          const bf16x8_t aw = widen8(r[0], r[1]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) d[i][j] = mfma_bf16_16x16x32(aw, bw[j], d[i][j]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * (sa[i][e] * sbv[j]);
+    } else {
+      i32x8_t bfr[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = cat8(ld16(sB + j * 16 * LDK), ld16(sB + j * 16 * LDK + 16));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x8_t af = cat8(ld16(sA + i * 16 * LDK), ld16(sA + i * 16 * LDK + 16));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const f32x4_t d = mfma_fp8_16x16x128(af, bfr[j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[e] * (sa[i][e] * sbv[j]);
+        }
+      }
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (splits == 1) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * WTM + i * 16 + g * 4 + e;
+          const int n = n0 + wn * WTN + j * 16 + l16;
+          if (m < p.M && n < p.N) epi_store8(p, batch, m, n, acc[i][j][e]);
+        }
+    return;
+  }
+  float* part = p.part + ((int64_t)batch * splits + split) * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * WTM + i * 16 + g * 4 + e;
+        const int n = n0 + wn * WTN + j * 16 + l16;
+        if (m < p.M && n < p.N) part[(int64_t)m * p.N + n] = acc[i][j][e];
+      }
+}
+
+template <int TAG>
+__global__ __launch_bounds__(256) void splitk_reduce8_kernel(GemmArgs p, int splits) {
+  const int64_t mn = (int64_t)p.M * p.N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (idx >= mn) return;
+  const float* base = p.part + (int64_t)b * splits * mn + idx;
+  float s = 0.f;
+  for (int sp = 0; sp < splits; ++sp) s += base[sp * mn];
+  epi_store8(p, b, (int)(idx / p.N), (int)(idx % p.N), s);
+}
+
+struct Plan8 {
+  int kind;  // 0 wsplit, 1 tile128, 2 tile256
+  int mt, kw, ysplit;
+  int splits, ksplit;
+  int tiles;
+};
+
+int pow2_at_least8(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+bool tag_precise(int tag) { return tag == TAG_QKVA || tag == TAG_QB || tag == TAG_KVB; }
+
+// prec: the precise form keeps 128 x 128 tiles (two accumulator sets per lane do not fit the
+// 128 x 256 tile's registers)
+Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
+  Plan8 pl{};
+  pl.splits = 1;
+  pl.ksplit = K;
+  pl.ysplit = 1;
+  const int ngroups = K / 128;
+  if (M <= 64) {
+    pl.kind = 0;
+    pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    pl.tiles = cdiv(N, 16);
+    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 256 && ngroups >= 8 * pl.ysplit)
+      pl.ysplit *= 2;
+    int kw = pow2_at_least8(cdiv(3000, pl.tiles * batch * pl.ysplit));
+    kw = std::min(kw, pl.mt == 1 ? 16 : 8);
+    while (kw > 1 && kw > ngroups / pl.ysplit) kw >>= 1;
+    pl.kw = kw;
+    return pl;
+  }
+  const bool big = !prec && M >= 1024 && N >= 1024;
+  pl.kind = big ? 2 : 1;
+  pl.tiles = cdiv(M, 128) * cdiv(N, big ? 256 : 128);
+  int splits = 1;
+  const int wgs = pl.tiles * batch;
+  if (wgs < 256) splits = cdiv(512, wgs);
+  splits = std::max(1, std::min(splits, ngroups));
+  const int per = cdiv(ngroups, splits);
+  pl.ksplit = per * 128;
+  pl.splits = cdiv(ngroups, per);
+  return pl;
+}
+
+template <int MT, int TAG, bool PREC>
+void launch_fp8_wsplit(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
+  dim3 grid(pl.tiles, pl.ysplit, a.batch);
+  switch (pl.kw) {
+    case 1: hipLaunchKernelGGL((gemm_fp8_wsplit_kernel<MT, 1, TAG, PREC>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_fp8_wsplit_kernel<MT, 2, TAG, PREC>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_fp8_wsplit_kernel<MT, 4, TAG, PREC>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_fp8_wsplit_kernel<MT, 8, TAG, PREC>), grid, dim3(512), 0, s, a); break;
+    default:
+      if constexpr (MT == 1)
+        hipLaunchKernelGGL((gemm_fp8_wsplit_kernel<MT, 16, TAG, PREC>), grid, dim3(1024), 0, s, a);
+      break;
+  }
+}
+
+template <int TAG, bool PREC>
+void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
+  if (pl.kind == 0) {
+    if (pl.mt == 1) launch_fp8_wsplit<1, TAG, PREC>(a, pl, s);
+    else if (pl.mt == 2) launch_fp8_wsplit<2, TAG, PREC>(a, pl, s);
+    else launch_fp8_wsplit<4, TAG, PREC>(a, pl, s);
+    return;
+  }
+  dim3 grid(pl.tiles, pl.splits, a.batch);
+  if (pl.kind == 1)
+    hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 128, 2, 2, TAG, PREC>), grid, dim3(256), 0, s, a, pl.splits,
+                       pl.ksplit);
+  else if constexpr (!PREC)
+    hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 256, 2, 4, TAG, PREC>), grid, dim3(512), 0, s, a, pl.splits,
+                       pl.ksplit);
+  if (pl.splits > 1) {
+    dim3 rgrid((unsigned)(((int64_t)a.M * a.N + 255) / 256), a.batch);
+    hipLaunchKernelGGL((splitk_reduce8_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
+  }
+}
+
+}  // namespace
+
+int64_t gemm_fp8_part_floats(int M, int N, int K, int batch) {
+  int64_t mx = 0;
+  for (bool prec : {false, true}) {
+    const Plan8 pl = plan_fp8(M, N, K, batch, 1, prec);
+    if (pl.splits > 1) mx = std::max(mx, (int64_t)pl.splits * batch * M * N);
+  }
+  return mx;
+}
+
+int gemm_fp8_ysplit(const GemmArgs& a) {
+  return plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag)).ysplit;
+}
+
+hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K % 128 != 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
+  const Plan8 pl = plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag));
+  if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
+  // q_a|kv_a, q_b and kv_b: precise; o_proj (and untagged test calls): native
+  switch (a.tag) {
+    case TAG_QKVA: launch_fp8_tagged<TAG_QKVA, true>(a, pl, s); break;
+    case TAG_QB: launch_fp8_tagged<TAG_QB, true>(a, pl, s); break;
+    case TAG_KVB: launch_fp8_tagged<TAG_KVB, true>(a, pl, s); break;
+    case TAG_OPROJ: launch_fp8_tagged<TAG_OPROJ, false>(a, pl, s); break;
+    default: launch_fp8_tagged<TAG_NONE, false>(a, pl, s); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace mla_k

@@ -27,9 +27,14 @@ struct GemmArgs {
   void* C = nullptr;        int64_t ldc = 0, sC = 0;
   int M = 0, N = 0, K = 0, batch = 1;
   int epi = EPI_F32;
+  // optional output scale per (batch, 128-column block): C *= c_scale[b * cs_stride + n / 128]
+  const float* c_scale = nullptr;
+  int64_t cs_stride = 0;
   // EPI_KVB destinations
   uint16_t* knope = nullptr;
   uint16_t* vt = nullptr;
+  uint16_t* knope_lo = nullptr;  // FP8 kernels only: optional planes of the bf16 residuals
+  uint16_t* vt_lo = nullptr;     // (value - bf16(value)), same layout as knope / vt
   int64_t vt_ld = 0;
   int64_t key_base = 0;
   // FP8 (E4M3FN codes) operands: A scales per (row, 128-group) with row stride as_ld floats;
@@ -53,6 +58,8 @@ struct GemmArgs {
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_ysplit(const GemmArgs& a);
 hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s);
+int64_t gemm_fp8_part_floats(int M, int N, int K, int batch);
+int gemm_fp8_ysplit(const GemmArgs& a);
 // Bytes of split-K partials / counters the skinny path may need for an (M, N, K, batch) GEMM.
 int64_t gemm_part_floats(int M, int N, int K, int batch);
 int gemm_counters(int M, int N, int K, int batch);
@@ -113,10 +120,15 @@ hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_byte
 // Prefill attention (rebuilt keys/values, causal): o[row][h*128+d] bf16
 // ---------------------------------------------------------------------------------------------
 struct PrefillAttnArgs {
-  const uint16_t* q;       // [n_tok][64][192] bf16, rotary part not yet rotated
+  const void* q;           // [n_tok][64][192] bf16 (split: float32), rotary part not yet rotated
   const uint16_t* knope;   // [keys][64][128] bf16
   const uint16_t* vt;      // [64*128][vt_ld] bf16
   int64_t vt_ld;
+  // split precision (FP8 weights): q is float32 and every product is carried as bf16 hi + lo
+  // parts; knope_lo / vt_lo hold the residuals of knope / vt, k_pe is float32 in the entry
+  int split;
+  const uint16_t* knope_lo;
+  const uint16_t* vt_lo;
   const uint8_t* cache;    // for the rotated shared key k_pe of each position
   int entry_bytes;
   int kpe_off;             // byte offset of k_pe inside an entry
@@ -135,8 +147,9 @@ hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 // Decode attention in the latent space, split over positions, then merged
 // ---------------------------------------------------------------------------------------------
 struct DecodeAttnArgs {
-  const uint16_t* q_lat;   // [B][64][512] bf16 (q_nope absorbed through W_UK)
-  const uint16_t* q;       // [B][64][192] bf16: rotary part read from here, rotated on load
+  const void* q_lat;       // [B][64][512] q_nope absorbed through W_UK (bf16; FP8 mode: float32)
+  int64_t q_lat_lo;        // FP8 mode: q_lat is the sum of two float32 arrays, this many floats apart
+  const void* q;           // [B][64][192] q (bf16; FP8 mode: float32): rotary part rotated on load
   const uint8_t* cache;
   int entry_bytes;
   int fp8;
@@ -151,7 +164,10 @@ struct DecodeAttnArgs {
   float scale;
   float* part_o;           // [B][max_splits][64][512] fp32
   float* part_ml;          // [B][max_splits][64][2] (running max, sum)
-  uint16_t* o_lat;         // merged [B][64][512] bf16
+  const void* w_uv;        // kv_b weight (bf16, or FP8 codes); W_UV,h = rows h*256+128 .. +255
+  const float* w_uv_s;     // FP8: kv_b block scales [128][4]
+  float* o_f32;            // output o [B][8192] float32 (when set), else
+  uint16_t* o_bf16;        //        o [B][8192] bf16
 };
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s);
 
@@ -160,6 +176,10 @@ hipError_t quantize_rows_f32(const float* x, int64_t ldx, int rows, int K, uint8
                              hipStream_t s);
 hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
                               hipStream_t s);
+
+// q_nope parts of float32 q [n][64][192] -> bf16 high parts [n][64][128] followed by the bf16
+// residuals [n][64][128] (the FP8 decode absorbs both and adds the two products).
+hipError_t split_q_nope(const float* q, int n, uint16_t* out, hipStream_t s);
 
 // Fill kernel for small control blocks (used instead of memset so callers may capture graphs).
 hipError_t fill_zero_i32(int* p, int64_t n, hipStream_t s);

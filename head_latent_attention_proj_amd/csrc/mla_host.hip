@@ -42,27 +42,42 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
-// ---- W_UK^T per head: ukT[h][c][d] = kv_b[h*256 + d][c]  (d < 128, c < 512), bf16
-__global__ void transpose_uk_kernel(const uint16_t* kvb, uint16_t* ukT) {
+// ---- per-head W_UK^T: ukT[h][c][d] = W_UK,h[d][c] = kv_b[h*256 + d][c]  (d < 128, c < 512), as bf16.
+// bf16 weights are copied; FP8 codes are widened to their exact bf16 value (the block scale of
+// (h, c/128) is applied to the product's output).
+template <bool FP8>
+__global__ void transpose_uk_kernel(const void* kvb, uint16_t* ukT) {
   const int h = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // over 512*128
   if (idx >= KV_LORA * NOPE) return;
   const int c = idx / NOPE, d = idx % NOPE;
-  ukT[((int64_t)h * KV_LORA + c) * NOPE + d] = kvb[((int64_t)h * 256 + d) * KV_LORA + c];
+  const int64_t src = ((int64_t)h * 256 + d) * KV_LORA + c;
+  uint16_t v;
+  if constexpr (FP8) {
+    v = f2bf(__builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t*)kvb)[src], 0));
+  } else {
+    v = ((const uint16_t*)kvb)[src];
+  }
+  ukT[((int64_t)h * KV_LORA + c) * NOPE + d] = v;
 }
 
 }  // namespace
 
 struct mla_ctx {
   mla_config cfg;
+  bool fp8;
   float scale;
   const uint16_t* g_q;
   const uint16_t* g_kv;
   const void* w_qkva;  // packed [2112, 7168]
+  const float* s_qkva; // FP8: packed [17, 56]
   const void* w_qb;
+  const float* s_qb;   // [96, 12]
   const void* w_kvb;
-  const void* w_ukT;   // packed [64][512][128]
+  const float* s_kvb;  // [128, 4]
+  const uint16_t* w_ukT;  // packed [64][512][128] bf16
   const void* w_o;
+  const float* s_o;    // [56, 64]
   const float* rope_cs;
 };
 
@@ -84,20 +99,21 @@ mla_status check_config(const mla_config* c) {
 }
 
 struct PackedLayout {
-  size_t qkva, ukT, g_q, g_kv, rope, total;
+  size_t qkva, s_qkva, ukT, g_q, g_kv, rope, total;
 };
 
 PackedLayout packed_layout(const mla_config* c) {
   PackedLayout L{};
-  const size_t eb = c->wdtype == MLA_WDTYPE_BF16 ? 2 : 1;
+  const bool fp8 = c->wdtype == MLA_WDTYPE_FP8_E4M3_B128;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = round_up(off + bytes, 256);
     return o;
   };
-  L.qkva = take((size_t)QKVA_N * HIDDEN * eb);
-  L.ukT = take((size_t)HEADS * KV_LORA * NOPE * eb);
+  L.qkva = take((size_t)QKVA_N * HIDDEN * (fp8 ? 1 : 2));
+  L.s_qkva = take(fp8 ? (size_t)17 * 56 * sizeof(float) : 0);
+  L.ukT = take((size_t)HEADS * KV_LORA * NOPE * 2);
   L.g_q = take(Q_LORA * 2);
   L.g_kv = take(KV_LORA * 2);
   L.rope = take((size_t)c->max_positions * 32 * 2 * sizeof(float));
@@ -111,7 +127,7 @@ constexpr int QKVA_PARTS = 4;  // K splits of the fused q_a|kv_a projection at d
 constexpr int DECODE_MAX_WG = 2048;
 
 struct DecodePlan {
-  int chunk = 64, max_splits = 1;
+  int chunk = 32, max_splits = 1;
 };
 
 DecodePlan plan_decode(int B, const int* lens_after, int n) {
@@ -122,7 +138,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n) {
     max_len = std::max(max_len, lens_after[i]);
   }
   DecodePlan p;
-  p.chunk = (int)std::max<int64_t>(64, round_up((total + 511) / 512, 64));
+  p.chunk = (int)std::max<int64_t>(32, round_up((total + 511) / 512, 32));
   p.max_splits = (max_len + p.chunk - 1) / p.chunk;
   while ((int64_t)B * p.max_splits > DECODE_MAX_WG) {
     p.chunk *= 2;
@@ -132,30 +148,32 @@ DecodePlan plan_decode(int B, const int* lens_after, int n) {
 }
 
 struct WsLayout {
-  size_t counters, cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, o_lat, gpart, total;
+  size_t counters, cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
+  size_t knope_lo, vt_lo, qs;  // FP8 only: residual planes, split q_nope
+  size_t x8, x8s, qh8s, o32, o8, o8s, total;
   int64_t gpart_floats;
   int64_t vt_ld;
 };
 
-// GEMM shapes a call may run, for split-K scratch sizing: (M, N, K, batch).
-int64_t max_gemm_part(int ntok, int nkeys_seq, bool decode) {
+// Largest split-K scratch any projection of a call may need (floats).
+int64_t max_gemm_part(int ntok, int nkeys_seq, bool decode, bool fp8) {
   int64_t mx = 0;
   auto upd = [&](int M, int N, int K, int batch) {
-    if (M > 0) mx = std::max(mx, mla_k::gemm_part_floats(M, N, K, batch));
+    if (M > 0)
+      mx = std::max(mx, fp8 ? mla_k::gemm_fp8_part_floats(M, N, K, batch) : mla_k::gemm_part_floats(M, N, K, batch));
   };
   upd(ntok, QKVA_N, HIDDEN, 1);
   upd(ntok, QB_N, Q_LORA, 1);
   upd(ntok, HIDDEN, O_IN, 1);
-  if (decode) {
-    upd(ntok, KV_LORA, NOPE, HEADS);
-    upd(ntok, VD, KV_LORA, HEADS);
+  if (decode) {  // absorb (FP8: high and residual parts of q_nope stacked as 2 * ntok rows)
+    if (ntok > 0) mx = std::max(mx, mla_k::gemm_part_floats(fp8 ? 2 * ntok : ntok, KV_LORA, NOPE, HEADS));
   } else {
     upd(nkeys_seq, KVB_N, KV_LORA, 1);
   }
   return mx;
 }
 
-WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64_t gpart_floats) {
+WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64_t gpart_floats, bool fp8) {
   WsLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -165,17 +183,26 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   };
   L.counters = take(N_COUNTERS * sizeof(int));
   L.cqkv = take((size_t)ntok * QKVA_N * 4 * QKVA_PARTS);
-  L.q_hat = take((size_t)ntok * Q_LORA * 2);
-  L.q = take((size_t)ntok * QB_N * 2);
+  L.q_hat = take((size_t)ntok * Q_LORA * 2);  // bf16, or FP8 codes
+  L.q = take((size_t)ntok * QB_N * (fp8 ? 4 : 2));  // FP8: float32 q
   L.o = take((size_t)ntok * O_IN * 2);
   L.meta = take((size_t)nbatch * sizeof(mla_k::SeqMeta));
   L.vt_ld = round_up(nkeys, 64);
   L.knope = take((size_t)L.vt_ld * HEADS * NOPE * 2);
   L.vt = take((size_t)L.vt_ld * HEADS * VD * 2);
-  L.q_lat = take((size_t)nbatch * HEADS * KV_LORA * 2);
+  L.knope_lo = take(fp8 ? (size_t)L.vt_ld * HEADS * NOPE * 2 : 0);
+  L.vt_lo = take(fp8 ? (size_t)L.vt_ld * HEADS * VD * 2 : 0);
+  // q_lat: bf16 [B][64][512], or FP8: two float32 products (high and residual part of q_nope)
+  L.q_lat = take(decode_splits > 0 ? (size_t)nbatch * HEADS * KV_LORA * (fp8 ? 8 : 2) : 0);
+  L.qs = take(fp8 && decode_splits > 0 ? (size_t)2 * nbatch * HEADS * NOPE * 2 : 0);
   L.part_o = take((size_t)decode_splits * HEADS * KV_LORA * 4);
   L.part_ml = take((size_t)decode_splits * HEADS * 2 * 4);
-  L.o_lat = take((size_t)nbatch * HEADS * KV_LORA * 2);
+  L.x8 = take(fp8 ? (size_t)ntok * HIDDEN : 0);
+  L.x8s = take(fp8 ? (size_t)ntok * (HIDDEN / 128) * 4 : 0);
+  L.qh8s = take(fp8 ? (size_t)ntok * (Q_LORA / 128) * 4 : 0);
+  L.o32 = take(fp8 ? (size_t)ntok * O_IN * 4 : 0);
+  L.o8 = take(fp8 ? (size_t)ntok * O_IN : 0);
+  L.o8s = take(fp8 ? (size_t)ntok * (O_IN / 128) * 4 : 0);
   L.gpart_floats = gpart_floats;
   L.gpart = take((size_t)gpart_floats * 4);
   L.total = off;
@@ -189,6 +216,14 @@ mla_k::GemmArgs gemm_common(uint8_t* ws, const WsLayout& L) {
   g.counters = (int*)(ws + L.counters);
   g.counter_cap = N_COUNTERS;
   return g;
+}
+
+hipError_t run_proj(const mla_ctx* ctx, mla_k::GemmArgs& g, hipStream_t s) {
+  return ctx->fp8 ? mla_k::gemm_fp8(g, s) : mla_k::gemm_bf16(g, s);
+}
+
+int proj_ysplit(const mla_ctx* ctx, const mla_k::GemmArgs& g) {
+  return ctx->fp8 ? mla_k::gemm_fp8_ysplit(g) : mla_k::gemm_ysplit(g);
 }
 
 mla_status check_cache(const mla_ctx* ctx, const mla_cache* c) {
@@ -213,6 +248,20 @@ mla_status check_seq(const mla_ctx* ctx, const mla_cache* c, int s, int64_t add)
     return fail(MLA_E_CAPACITY, "sequence %d: %lld positions exceed max_positions %d", s, (long long)(len + add),
                 ctx->cfg.max_positions);
   return MLA_OK;
+}
+
+// Projection input of the o_proj / q_a|kv_a products: bf16 directly, or FP8 codes + scales.
+void set_a(const mla_ctx* ctx, mla_k::GemmArgs& g, const void* bf16, int64_t ld_bf16, const uint8_t* codes,
+           const float* scales, int64_t groups) {
+  if (ctx->fp8) {
+    g.A = codes;
+    g.lda = ld_bf16;
+    g.a_scale = scales;
+    g.as_ld = groups;
+  } else {
+    g.A = bf16;
+    g.lda = ld_bf16;
+  }
 }
 
 }  // namespace
@@ -250,18 +299,18 @@ size_t mla_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32
   // rebuilt keys: each sequence's rows are padded to a multiple of 64
   const int64_t keys = max_keys + 63LL * max_batch;
   int64_t gp = 0;
-  for (int m = 1; m <= std::min(max_tokens, 4096); ++m) gp = std::max(gp, max_gemm_part(m, 0, false));
+  for (int m = 1; m <= std::min(max_tokens, 4096); ++m) gp = std::max(gp, max_gemm_part(m, 0, false, ctx->fp8));
   const int64_t kmax = std::min<int64_t>(max_keys, 4096);
-  for (int64_t k = 1; k <= kmax; ++k) gp = std::max(gp, mla_k::gemm_part_floats((int)k, KVB_N, KV_LORA, 1));
-  return ws_layout(max_tokens, max_batch, keys, 0, gp).total;
+  for (int64_t k = 1; k <= kmax; ++k) gp = std::max(gp, max_gemm_part(0, (int)k, false, ctx->fp8));
+  return ws_layout(max_tokens, max_batch, keys, 0, gp, ctx->fp8).total;
 }
 
 size_t mla_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t max_keys) {
   if (!ctx || max_batch <= 0 || max_keys < max_batch) return 0;
   int64_t gp = 0;
-  for (int m = 1; m <= max_batch; ++m) gp = std::max(gp, max_gemm_part(m, 0, true));
-  const int64_t splits = std::min<int64_t>((int64_t)max_batch * ((max_keys + 63) / 64), DECODE_MAX_WG);
-  return ws_layout(max_batch, max_batch, 0, (int)std::max<int64_t>(splits, max_batch), gp).total;
+  for (int m = 1; m <= max_batch; ++m) gp = std::max(gp, max_gemm_part(m, 0, true, ctx->fp8));
+  const int64_t splits = std::min<int64_t>((int64_t)max_batch * ((max_keys + 31) / 32), DECODE_MAX_WG);
+  return ws_layout(max_batch, max_batch, 0, (int)std::max<int64_t>(splits, max_batch), gp, ctx->fp8).total;
 }
 
 mla_status mla_workspace_init(void* ws, size_t ws_bytes, mla_stream stream) {
@@ -279,27 +328,40 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
   mla_status st = check_config(cfg);
   if (st != MLA_OK) return st;
   if (!w || !packed) return fail(MLA_E_ARG, "weights or packed buffer is NULL");
+  const bool fp8 = cfg->wdtype == MLA_WDTYPE_FP8_E4M3_B128;
   const void* ptrs[] = {w->q_a, w->q_a_norm, w->q_b, w->kv_a, w->kv_a_norm, w->kv_b, w->o};
   for (const void* p : ptrs) {
     if (!p) return fail(MLA_E_ARG, "a weight pointer is NULL");
     if (!aligned16(p)) return fail(MLA_E_ALIGN, "a weight pointer is not 16-byte aligned");
   }
-  if (cfg->wdtype == MLA_WDTYPE_FP8_E4M3_B128)
-    return fail(MLA_E_UNSUPPORTED, "FP8 block-scaled weights are not enabled in this build");
+  if (fp8) {
+    const float* sp[] = {w->q_a_s, w->q_b_s, w->kv_a_s, w->kv_b_s, w->o_s};
+    for (const float* p : sp)
+      if (!p) return fail(MLA_E_ARG, "FP8 weights need all five scale grids");
+  }
   const PackedLayout L = packed_layout(cfg);
   if (packed_bytes < L.total) return fail(MLA_E_WORKSPACE, "packed buffer has %zu bytes, needs %zu", packed_bytes, L.total);
   if (!aligned16(packed)) return fail(MLA_E_ALIGN, "packed buffer is not 16-byte aligned");
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t* pk = (uint8_t*)packed;
-  const size_t eb = 2;
+  const size_t eb = fp8 ? 1 : 2;
   HIP_TRY(hipMemcpyAsync(pk + L.qkva, w->q_a, (size_t)Q_LORA * HIDDEN * eb, hipMemcpyDeviceToDevice, s));
   HIP_TRY(hipMemcpyAsync(pk + L.qkva + (size_t)Q_LORA * HIDDEN * eb, w->kv_a, (size_t)ENTRY * HIDDEN * eb,
                          hipMemcpyDeviceToDevice, s));
+  if (fp8) {  // scale grids of q_a [12, 56] and kv_a [5, 56] stacked: block rows of the fused weight
+    HIP_TRY(hipMemcpyAsync(pk + L.s_qkva, w->q_a_s, 12 * 56 * sizeof(float), hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(pk + L.s_qkva + 12 * 56 * sizeof(float), w->kv_a_s, 5 * 56 * sizeof(float),
+                           hipMemcpyDeviceToDevice, s));
+  }
   HIP_TRY(hipMemcpyAsync(pk + L.g_q, w->q_a_norm, Q_LORA * 2, hipMemcpyDeviceToDevice, s));
   HIP_TRY(hipMemcpyAsync(pk + L.g_kv, w->kv_a_norm, KV_LORA * 2, hipMemcpyDeviceToDevice, s));
-  hipLaunchKernelGGL(transpose_uk_kernel, dim3(KV_LORA * NOPE / 256, HEADS), dim3(256), 0, s,
-                     (const uint16_t*)w->kv_b, (uint16_t*)(pk + L.ukT));
+  if (fp8)
+    hipLaunchKernelGGL(transpose_uk_kernel<true>, dim3(KV_LORA * NOPE / 256, HEADS), dim3(256), 0, s, w->kv_b,
+                       (uint16_t*)(pk + L.ukT));
+  else
+    hipLaunchKernelGGL(transpose_uk_kernel<false>, dim3(KV_LORA * NOPE / 256, HEADS), dim3(256), 0, s, w->kv_b,
+                       (uint16_t*)(pk + L.ukT));
   HIP_TRY(hipGetLastError());
   // RoPE table: angle = position * theta^(-2i/64), computed in double, stored float32
   const int P = cfg->max_positions;
@@ -317,14 +379,19 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
 
   mla_ctx* c = new mla_ctx;
   c->cfg = *cfg;
+  c->fp8 = fp8;
   c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(1.0 / std::sqrt((double)QK));
   c->g_q = (const uint16_t*)(pk + L.g_q);
   c->g_kv = (const uint16_t*)(pk + L.g_kv);
   c->w_qkva = pk + L.qkva;
+  c->s_qkva = fp8 ? (const float*)(pk + L.s_qkva) : nullptr;
   c->w_qb = w->q_b;
+  c->s_qb = w->q_b_s;
   c->w_kvb = w->kv_b;
-  c->w_ukT = pk + L.ukT;
+  c->s_kvb = w->kv_b_s;
+  c->w_ukT = (const uint16_t*)(pk + L.ukT);
   c->w_o = w->o;
+  c->s_o = w->o_s;
   c->rope_cs = (const float*)(pk + L.rope);
   *out = c;
   g_last_error.clear();
@@ -377,61 +444,80 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     max_t = std::max(max_t, t);
   }
   const int ntok = q_start_h[B];
-  int max_keys_seq = 0;
+  int64_t gp = max_gemm_part(ntok, 0, false, ctx->fp8);
   for (int b = 0; b < B; ++b)
-    max_keys_seq = std::max(max_keys_seq, cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b]);
-  int64_t gp = max_gemm_part(ntok, 0, false);
-  for (int b = 0; b < B; ++b)
-    gp = std::max(gp, mla_k::gemm_part_floats(cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b],
-                                              KVB_N, KV_LORA, 1));
-  const WsLayout L = ws_layout(ntok, B, nkeys, 0, gp);
+    gp = std::max(gp, max_gemm_part(0, cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b], false, ctx->fp8));
+  const WsLayout L = ws_layout(ntok, B, nkeys, 0, gp, ctx->fp8);
   if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
+  const bool fp8 = ctx->fp8;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
   auto* meta = (mla_k::SeqMeta*)(w + L.meta);
   HIP_TRY(mla_k::prefill_plan(seq_ids_d, q_start_d, cache->offset_d, cache->len_d, B, meta, s));
 
-  // 1. fused q_a | kv_a projection (fp32 out)
+  // 1. fused q_a | kv_a projection (fp32 out); FP8: x quantised per token and 128-group first
+  if (fp8)
+    HIP_TRY(mla_k::quantize_rows_bf16((const uint16_t*)x, HIDDEN, ntok, HIDDEN, w + L.x8, (float*)(w + L.x8s), s));
   mla_k::GemmArgs g = gemm_common(w, L);
-  g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
-  g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32; g.tag = mla_k::TAG_QKVA;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
-  // 2. RMSNorms, RoPE of the shared key, latent entries into the cache
+  set_a(ctx, g, x, HIDDEN, w + L.x8, (const float*)(w + L.x8s), HIDDEN / 128);
+  g.B = ctx->w_qkva; g.ldb = HIDDEN; g.b_scale = ctx->s_qkva; g.bs_ld = HIDDEN / 128;
+  g.C = w + L.cqkv; g.ldc = QKVA_N; g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  g.tag = mla_k::TAG_QKVA;
+  HIP_TRY(run_proj(ctx, g, s));
+  // 2. RMSNorms, RoPE of the shared key, latent entries into the cache (FP8: quantised q_hat, c_hat)
   mla_k::NormArgs na{};
   na.cqkv = (const float*)(w + L.cqkv); na.n_part = 1; na.g_q = ctx->g_q; na.g_kv = ctx->g_kv;
   na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
-  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = ntok; na.meta = meta; na.B = B;
+  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = ntok; na.meta = meta; na.B = B;
+  na.q_hat_codes = w + L.q_hat; na.q_hat_scales = (float*)(w + L.qh8s);
   HIP_TRY(mla_k::norm_rope_append(na, s));
   // 3. q_b
   g = gemm_common(w, L);
-  g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
-  g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_QB;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
+  set_a(ctx, g, w + L.q_hat, Q_LORA, w + L.q_hat, (const float*)(w + L.qh8s), Q_LORA / 128);
+  g.B = ctx->w_qb; g.ldb = Q_LORA; g.b_scale = ctx->s_qb; g.bs_ld = Q_LORA / 128;
+  g.C = w + L.q; g.ldc = QB_N; g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.tag = mla_k::TAG_QB;
+  g.epi = fp8 ? mla_k::EPI_F32 : mla_k::EPI_BF16;
+  HIP_TRY(run_proj(ctx, g, s));
   // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values
   for (int b = 0; b < B; ++b) {
     const int sid = seq_ids_h[b];
     const int n = cache->len_h[sid] + q_start_h[b + 1] - q_start_h[b];
+    const uint8_t* rows = (const uint8_t*)cache->data + cache->offset_h[sid] * (int64_t)eb;
     g = gemm_common(w, L);
-    g.A = (const uint8_t*)cache->data + cache->offset_h[sid] * (int64_t)eb; g.lda = eb / 2;
-    g.B = ctx->w_kvb; g.ldb = KV_LORA; g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB; g.tag = mla_k::TAG_KVB;
+    if (fp8) {  // entry = [512 codes | 4 group scales | k_pe]
+      g.A = rows; g.lda = eb; g.a_scale = (const float*)(rows + KV_LORA); g.as_ld = eb / 4;
+    } else {
+      g.A = rows; g.lda = eb / 2;
+    }
+    g.B = ctx->w_kvb; g.ldb = KV_LORA; g.b_scale = ctx->s_kvb; g.bs_ld = KV_LORA / 128;
+    g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB; g.tag = mla_k::TAG_KVB;
     g.knope = (uint16_t*)(w + L.knope); g.vt = (uint16_t*)(w + L.vt); g.vt_ld = L.vt_ld; g.key_base = kbase[b];
-    HIP_TRY(mla_k::gemm_bf16(g, s));
+    if (fp8) {
+      g.knope_lo = (uint16_t*)(w + L.knope_lo);
+      g.vt_lo = (uint16_t*)(w + L.vt_lo);
+    }
+    HIP_TRY(run_proj(ctx, g, s));
   }
-  // 5. causal attention
+  // 5. causal attention (FP8: split precision, float32 output -- the o_proj quantiser's input)
   mla_k::PrefillAttnArgs pa{};
-  pa.q = (const uint16_t*)(w + L.q); pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
-  pa.vt_ld = L.vt_ld; pa.cache = (const uint8_t*)cache->data; pa.entry_bytes = eb; pa.kpe_off = KV_LORA * 2;
+  pa.q = w + L.q; pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
+  pa.split = fp8; pa.knope_lo = (const uint16_t*)(w + L.knope_lo); pa.vt_lo = (const uint16_t*)(w + L.vt_lo);
+  pa.vt_ld = L.vt_ld; pa.cache = (const uint8_t*)cache->data; pa.entry_bytes = eb;
+  pa.kpe_off = fp8 ? KV_LORA + 16 : KV_LORA * 2;
   pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
-  pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o);
+  pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o); pa.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr;
   HIP_TRY(mla_k::prefill_attention(pa, s));
   // 6. o_proj
+  if (fp8)
+    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), O_IN, ntok, O_IN, w + L.o8, (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
-  g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
-  g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
+  set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
+  g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
+  g.C = y; g.ldc = HIDDEN; g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
+  HIP_TRY(run_proj(ctx, g, s));
   // 7. lengths
   HIP_TRY(mla_k::commit_lengths(seq_ids_d, q_start_d, cache->len_d, B, s));
   for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += q_start_h[b + 1] - q_start_h[b];
@@ -455,59 +541,75 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
     lens[b] = cache->len_h[seq_ids_h[b]] + 1;
   }
   const DecodePlan dp = plan_decode(B, lens.data(), B);
-  const int64_t gp = max_gemm_part(B, 0, true);
-  const WsLayout L = ws_layout(B, B, 0, B * dp.max_splits, gp);
+  const int64_t gp = max_gemm_part(B, 0, true, ctx->fp8);
+  const WsLayout L = ws_layout(B, B, 0, B * dp.max_splits, gp, ctx->fp8);
   if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
+  const bool fp8 = ctx->fp8;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
-  // 1. fused q_a | kv_a
+  // 1. fused q_a | kv_a (K split over workgroups at small batch; the norm kernel adds the parts)
+  if (fp8)
+    HIP_TRY(mla_k::quantize_rows_bf16((const uint16_t*)x, HIDDEN, B, HIDDEN, w + L.x8, (float*)(w + L.x8s), s));
   mla_k::GemmArgs g = gemm_common(w, L);
-  g.A = x; g.lda = HIDDEN; g.B = ctx->w_qkva; g.ldb = HIDDEN; g.C = w + L.cqkv; g.ldc = QKVA_N;
-  g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32; g.tag = mla_k::TAG_QKVA;
-  g.ysplit_max = QKVA_PARTS; g.c_split_stride = (int64_t)B * QKVA_N;
-  const int qkva_parts = mla_k::gemm_ysplit(g);
-  HIP_TRY(mla_k::gemm_bf16(g, s));
+  set_a(ctx, g, x, HIDDEN, w + L.x8, (const float*)(w + L.x8s), HIDDEN / 128);
+  g.B = ctx->w_qkva; g.ldb = HIDDEN; g.b_scale = ctx->s_qkva; g.bs_ld = HIDDEN / 128;
+  g.C = w + L.cqkv; g.ldc = QKVA_N; g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
+  g.tag = mla_k::TAG_QKVA; g.ysplit_max = QKVA_PARTS; g.c_split_stride = (int64_t)B * QKVA_N;
+  const int qkva_parts = proj_ysplit(ctx, g);
+  HIP_TRY(run_proj(ctx, g, s));
   // 2. norms + shared-key RoPE + append at position len; len_d advances by one here
   mla_k::NormArgs na{};
   na.cqkv = (const float*)(w + L.cqkv); na.n_part = qkva_parts; na.part_stride = (int64_t)B * QKVA_N;
   na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
-  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = 0; na.n_tokens = B; na.meta = nullptr;
+  na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = B; na.meta = nullptr;
   na.seq_ids = seq_ids_d; na.offset = cache->offset_d; na.len = cache->len_d;
+  na.q_hat_codes = w + L.q_hat; na.q_hat_scales = (float*)(w + L.qh8s);
   HIP_TRY(mla_k::norm_rope_append(na, s));
   // 3. q_b
   g = gemm_common(w, L);
-  g.A = w + L.q_hat; g.lda = Q_LORA; g.B = ctx->w_qb; g.ldb = Q_LORA; g.C = w + L.q; g.ldc = QB_N;
-  g.M = B; g.N = QB_N; g.K = Q_LORA; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_QB;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
-  // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched GEMM)
+  set_a(ctx, g, w + L.q_hat, Q_LORA, w + L.q_hat, (const float*)(w + L.qh8s), Q_LORA / 128);
+  g.B = ctx->w_qb; g.ldb = Q_LORA; g.b_scale = ctx->s_qb; g.bs_ld = Q_LORA / 128;
+  g.C = w + L.q; g.ldc = QB_N; g.M = B; g.N = QB_N; g.K = Q_LORA; g.tag = mla_k::TAG_QB;
+  g.epi = fp8 ? mla_k::EPI_F32 : mla_k::EPI_BF16;
+  HIP_TRY(run_proj(ctx, g, s));
+  // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched). FP8: W_UK as its exact code
+  //    values with the block scale of (head, latent block) on the output; q_nope is float32 and
+  //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out, and
+  //    the attention kernel adds the two products.
   g = gemm_common(w, L);
-  g.A = w + L.q; g.lda = QB_N; g.sA = QK; g.B = ctx->w_ukT; g.ldb = NOPE; g.sB = (int64_t)KV_LORA * NOPE;
-  g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.M = B; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
-  g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_ABSORB;
+  if (fp8) {
+    HIP_TRY(mla_k::split_q_nope((const float*)(w + L.q), B, (uint16_t*)(w + L.qs), s));
+    g.A = w + L.qs; g.lda = HEADS * NOPE; g.sA = NOPE; g.M = 2 * B; g.epi = mla_k::EPI_F32;
+    g.c_scale = ctx->s_kvb;  // kv_b block (2h, c/128) scales W_UK,h
+    g.cs_stride = 2 * (KV_LORA / 128);
+  } else {
+    g.A = w + L.q; g.lda = QB_N; g.sA = QK; g.M = B; g.epi = mla_k::EPI_BF16;
+  }
+  g.B = ctx->w_ukT; g.ldb = NOPE; g.sB = (int64_t)KV_LORA * NOPE;
+  g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
+  g.tag = mla_k::TAG_ABSORB;
   HIP_TRY(mla_k::gemm_bf16(g, s));
-  // 5. split attention over the latent cache + merge
+  // 5. split attention over the latent cache, merge, W_UV (float32) -> o
   mla_k::DecodeAttnArgs da{};
-  da.q_lat = (const uint16_t*)(w + L.q_lat); da.q = (const uint16_t*)(w + L.q); da.cache = (const uint8_t*)cache->data;
-  da.entry_bytes = eb; da.fp8 = 0; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
+  da.q_lat = w + L.q_lat; da.q_lat_lo = (int64_t)B * HEADS * KV_LORA; da.q = w + L.q;
+  da.cache = (const uint8_t*)cache->data;
+  da.entry_bytes = eb; da.fp8 = fp8; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
   da.seq_ids = seq_ids_d; da.offset = cache->offset_d; da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
   da.max_splits = dp.max_splits; da.scale = ctx->scale; da.part_o = (float*)(w + L.part_o);
-  da.part_ml = (float*)(w + L.part_ml); da.o_lat = (uint16_t*)(w + L.o_lat);
+  da.part_ml = (float*)(w + L.part_ml); da.w_uv = ctx->w_kvb; da.w_uv_s = ctx->s_kvb;
+  da.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr; da.o_bf16 = (uint16_t*)(w + L.o);
   HIP_TRY(mla_k::decode_attention(da, s));
-  // 6. W_UV per head: o[b, h*128 + d] = o_lat[b,h,:] . W_UV,h[d,:]
+  // 6. o_proj
+  if (fp8)
+    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), O_IN, B, O_IN, w + L.o8, (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
-  g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
-  g.B = (const uint16_t*)ctx->w_kvb + (int64_t)NOPE * KV_LORA; g.ldb = KV_LORA; g.sB = 256 * KV_LORA;
-  g.C = w + L.o; g.ldc = O_IN; g.sC = VD; g.M = B; g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.epi = mla_k::EPI_BF16;
-  g.tag = mla_k::TAG_UV;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
-  // 7. o_proj
-  g = gemm_common(w, L);
-  g.A = w + L.o; g.lda = O_IN; g.B = ctx->w_o; g.ldb = O_IN; g.C = y; g.ldc = HIDDEN;
-  g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
-  HIP_TRY(mla_k::gemm_bf16(g, s));
+  set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
+  g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
+  g.C = y; g.ldc = HIDDEN; g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
+  HIP_TRY(run_proj(ctx, g, s));
   for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
   return MLA_OK;
 }

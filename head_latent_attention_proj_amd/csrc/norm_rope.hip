@@ -172,8 +172,13 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
     const float k1 = cval(Q_LORA + KV_LORA + 2 * tid + 1);
     const float c = a.rope_cs[(int64_t)pos * 32 + tid];
     const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + tid];
-    uint16_t* kpe = (uint16_t*)(entry + (a.fp8 ? KV_LORA + 16 : KV_LORA * 2));
-    *(uint32_t*)(kpe + 2 * tid) = pack_bf16x2(k0 * c - k1 * s, k0 * s + k1 * c);
+    if (a.fp8) {  // float32 rotary key: the scores it feeds stay exact to float32
+      float* kpe = (float*)(entry + KV_LORA + 16);
+      *(f32x2_t*)(kpe + 2 * tid) = f32x2_t{k0 * c - k1 * s, k0 * s + k1 * c};
+    } else {
+      uint16_t* kpe = (uint16_t*)(entry + KV_LORA * 2);
+      *(uint32_t*)(kpe + 2 * tid) = pack_bf16x2(k0 * c - k1 * s, k0 * s + k1 * c);
+    }
   }
   if (!a.meta) {
     __syncthreads();
@@ -210,6 +215,19 @@ __global__ void quantize_rows_kernel(const T* x, int64_t ldx, int rows, int K, u
   dst[lane] = (uint8_t)e4m3_rne_sat(v0 / sc);
   dst[lane + 64] = (uint8_t)e4m3_rne_sat(v1 / sc);
   if (lane == 0) scales[(int64_t)r * groups + gi] = sc;
+}
+
+// one thread per q_nope feature (n * 64 * 128 of them)
+__global__ void split_q_nope_kernel(const float* q, int n, uint16_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n * mla_dims::HEADS * mla_dims::NOPE;
+  if (i >= total) return;
+  const int64_t row = i >> 13;  // token (64 * 128 = 8192 features)
+  const int hd = (int)(i & 8191);
+  const float v = q[row * mla_dims::QB_N + (hd >> 7) * mla_dims::QK + (hd & 127)];
+  const uint16_t hi = f2bf(v);
+  out[i] = hi;
+  out[total + i] = f2bf(v - bf2f(hi));
 }
 
 __global__ void fill_zero_kernel(int* p, int64_t n) {
@@ -260,6 +278,13 @@ hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, u
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, ldx,
                      rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t split_q_nope(const float* q, int n, uint16_t* out, hipStream_t s) {
+  const int64_t total = (int64_t)n * mla_dims::HEADS * mla_dims::NOPE;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_q_nope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, q, n, out);
   return hipGetLastError();
 }
 

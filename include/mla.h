@@ -98,8 +98,10 @@ typedef struct {
 /* Latent KV cache: one slot per position, mla_cache_entry_bytes() bytes per slot.
  *   bf16 format: 576 bf16 = [c_hat (512, the latent RMSNorm output that kv_b consumes) |
  *                k_pe (64, rotated)]                                   -> 1,152 bytes
- *   FP8 format:  [512 E4M3FN codes of c_hat | 4 float32 group scales | k_pe 64 bf16]
- *                (the quantised latent is exactly what kv_b consumes)  ->   656 bytes
+ *   FP8 format:  [512 E4M3FN codes of c_hat | 4 float32 group scales | k_pe 64 float32]
+ *                (the quantised latent is exactly what kv_b consumes; the rotary key is kept
+ *                in float32 because the FP8 output quantiser amplifies any rounding of the
+ *                scores)                                               ->   784 bytes
  * The rebuilt per-head keys and values of the pages' cache ("KV cache" page: 20,480 values
  * per position against 576) are derived from these entries inside the kernels; the cache
  * keeps the 576-feature form ("In numbers" on the dense-block attention page: 70,272 vs
@@ -123,7 +125,7 @@ typedef struct {
  * Returns 0 for an invalid config. */
 size_t mla_packed_weight_bytes(const mla_config* cfg);
 
-/* Bytes per cache slot for cfg's weight format (1152 or 656); 0 for an invalid config. */
+/* Bytes per cache slot for cfg's weight format (1152 or 784); 0 for an invalid config. */
 size_t mla_cache_entry_bytes(const mla_config* cfg);
 
 /* Workspace bytes sufficient for any prefill call with at most max_tokens new tokens in total,

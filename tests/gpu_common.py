@@ -46,6 +46,42 @@ def layer(max_positions: int = 16384):
     return binding.Layer(binding.weights_to_device(bits), max_positions=max_positions)
 
 
+def assert_codes_valid(codes: np.ndarray, scales: np.ndarray, pre: np.ndarray, what: str,
+                       delta: float = 1e-4, max_frac: float = 1e-2):
+    """Quantised activations (E4M3FN codes + one float32 scale per 128 features) against the
+    oracle's quantiser applied to the oracle's float64 pre-quantisation values.
+
+    A code is decided by rounding t = pre / scale. The kernel computes pre in float32 from a
+    K-long accumulation, so its t carries an absolute error of order 1e-5 of the group's
+    largest |t| (448); where t sits that close to a rounding boundary the two sides may land
+    on different codes. Checked: the scales agree to `delta` (relative), at most `max_frac` of
+    the codes differ, and every code lies between the oracle's roundings of t - d and t + d with
+    d = delta * 448 (rounding is monotone, so these bound every value the kernel could have
+    rounded).
+    """
+    from oracle import fp8 as ofp8
+
+    rc, rs = ofp8.quantize_1x128(pre)
+    rel = np.abs(scales.astype(np.float64) / rs - 1.0)
+    diff = codes != rc
+    frac = float(diff.mean())
+    log(f"  {what}: scale rel-diff max {rel.max():.2e}; {int(diff.sum())} of {diff.size} codes differ ({frac:.2e})")
+    assert rel.max() <= delta, f"{what}: scales differ (rel {rel.max():.2e})"
+    assert frac <= max_frac, f"{what}: {frac:.2e} of the codes differ"
+    if diff.any():
+        n = pre.shape[0]
+        t = (pre.reshape(n, -1, 128) / rs[:, :, None]).reshape(pre.shape)[diff]
+        d = delta * 448.0
+        lo = ofp8.e4m3_value(ofp8.e4m3_encode(t - d))
+        hi = ofp8.e4m3_value(ofp8.e4m3_encode(t + d))
+        vg = ofp8.e4m3_value(codes[diff])
+        bad = (vg < lo) | (vg > hi)
+        if bad.any():
+            k = np.flatnonzero(bad)[:8]
+            log(f"  {what}: outliers t={t[k]} gpu={vg[k]} oracle={ofp8.e4m3_value(rc[diff][k])}")
+        assert not bad.any(), f"{what}: {int(bad.sum())} codes lie outside the rounding of t +- {d:.3g}"
+
+
 def y_of(t) -> np.ndarray:
     return synth.bf16_bits_to_f64(binding.tensor_to_bf16_bits(t))
 

@@ -47,7 +47,7 @@ def test_config_validation_without_gpu(L):
     assert L.mla_cache_entry_bytes(ctypes.byref(cfg)) == 1152
     assert L.mla_packed_weight_bytes(ctypes.byref(cfg)) > (2112 * 7168 + 64 * 512 * 128) * 2
     fp8 = binding.make_config(max_positions=4096, wdtype=binding.WDTYPE_FP8)
-    assert L.mla_cache_entry_bytes(ctypes.byref(fp8)) == 656
+    assert L.mla_cache_entry_bytes(ctypes.byref(fp8)) == 784
     bad = binding.make_config()
     bad.heads = 32
     assert L.mla_packed_weight_bytes(ctypes.byref(bad)) == 0
