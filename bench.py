@@ -138,6 +138,7 @@ def main():
     oproj_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     oproj_bytes = OPROJ_BYTES + 2 * 8192 + 2 * 7168
     achieved = oproj_bytes / (oproj_ms * 1e-3) / 1e9
+    traffic = counted_traffic()
 
     extra = {}
     if not args.no_extra:
@@ -195,6 +196,14 @@ def main():
             "note": "one copy of the weights (MALL may hold part of them); includes one length rewind per step",
         }
 
+    # a plain 64 MiB device copy: the reference point that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
+    # counters to bytes (its algorithmic traffic is exactly 64 MiB read + 64 MiB written)
+    cp_src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    del cp_src, cp_dst
+
     cpu = None
     if not args.no_cpu:
         log("timing CPU oracle decode step")
@@ -224,13 +233,28 @@ def main():
         "roofline": {
             "kernel": "o_proj GEMM (M=1, N=7168, K=8192, bf16 weights)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-            "frac": round(achieved / 8000.0, 4), "traffic": None,
+            "frac": round(achieved / 8000.0, 4), "traffic": traffic,
             "avg_launch_us": round(oproj_ms * 1e3, 3), "bytes_per_launch": int(oproj_bytes),
         },
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def counted_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes (profiles/oproj_decode_B1_bf16_pmc.md), or None when the kernel source has changed since."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, "profiles", "oproj_decode_B1_bf16_traffic.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if sha == rec["source_sha256"] else None
 
 
 def cpu_baseline(bits, seconds):

@@ -22,8 +22,8 @@
 // LDS feeds every head: S^T = C Q^T (A = cache rows, B = queries held in registers), then
 // O^T = C^T P^T from a transposed copy of the block's latent part written while staging. The next
 // block's loads are in flight (in registers) while a block is used. Each split writes (max, sum,
-// unnormalised o) per head; the merge kernel combines the splits, normalises and applies W_UV in
-// float32.
+// unnormalised o) per head; the merge kernel combines the splits and normalises; W_UV is applied
+// afterwards as a batched bf16 MFMA product (one 128 x 512 matrix per head).
 #include "common.h"
 #include "kernels.h"
 
@@ -393,112 +393,84 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   }
 }
 
-// Merge of the splits and the value up-projection, float32 throughout. One workgroup per
-// (head, tile of up to MBT sequences):
-//   1. per sequence: o_lat = sum_s exp(m_s - m) o_s / sum_s exp(m_s - m) l_s   (LDS, float32)
-//   2. o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][c], W_UV,h = kv_b rows h*256+128 .. +255
-//      (FP8: code * block scale, exact in float32); thread = (d, half of c), halves added in LDS.
-constexpr int MBT = 16;
-
+// Merge of the splits, float32. One workgroup per (head h, sequence b): 4 groups of 64 threads
+// take every 4th split each (8 latent features per thread, a running (max, sum, o) rescaled as
+// splits arrive, four splits' loads in flight), then the 4 groups are combined through LDS in a
+// fixed order:  o_lat = sum_s exp(m_s - m) o_s / sum_s exp(m_s - m) l_s.
+// Output for the value up-projection (a bf16 MFMA product against W_UV):
+//   bf16 weights: o_lat rounded to bf16, [B][64][512];
+//   FP8 weights:  o_lat times the W_UV block scale of its 128-feature group (so the product runs
+//                 on the exact code values), as bf16 high parts [B][64][512] followed by the bf16
+//                 residuals [B][64][512]; the two products are added by the o_proj quantiser.
 template <bool FP8>
-__global__ __launch_bounds__(256) void decode_merge_uv_kernel(DecodeAttnArgs a) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   using namespace mla_dims;
-  const int h = blockIdx.x, bt = blockIdx.y * MBT;
-  const int nb = min(MBT, a.B - bt);
-  __shared__ __attribute__((aligned(16))) float olat[MBT][KV_LORA];
-  __shared__ float red[MBT][128];
-  const int tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, sg = tid >> 6, f = (tid & 63) * 8;
+  __shared__ __attribute__((aligned(16))) float so[4][KV_LORA];
+  __shared__ float sm[4], sl[4];
+  const int ns = cdiv(a.len[a.seq_ids[b]], a.chunk);
+  const int64_t base = (int64_t)b * a.max_splits * 64 + h;
 
-  // -- 1. merge: tps threads per sequence, dpt = 512 / tps features each
-  int tps = 256;
-  while (tps > 16 && tps * nb > 256) tps >>= 1;
-  {
-    const int bi = tid / tps, part = tid % tps;
-    if (bi < nb) {
-      const int b = bt + bi;
-      const int L = a.len[a.seq_ids[b]];
-      const int ns = cdiv(L, a.chunk);
-      const int64_t base = (int64_t)b * a.max_splits * 64 + h;
-      float mx = -INFINITY;
-      for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(base + (int64_t)s * 64) * 2]);
-      float l = 0.f;
-      const int dpt = KV_LORA / tps;
-      float o[32];
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  for (int s0 = sg; s0 < ns; s0 += 16) {
+    f32x2_t ml[4];
+    f32x4_t v0[4], v1[4];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) o[j] = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const int64_t p = base + (int64_t)s * 64;
-        const float w = exp2f(a.part_ml[p * 2] - mx);
-        l += w * a.part_ml[p * 2 + 1];
-        const float* src = a.part_o + p * KV_LORA + part * dpt;
-#pragma unroll
-        for (int j = 0; j < 32; j += 2) {
-          if (j < dpt) {
-            const f32x2_t v = *reinterpret_cast<const f32x2_t*>(src + j);
-            o[j] += w * v[0];
-            o[j + 1] += w * v[1];
-          }
-        }
-      }
-      const float inv = 1.0f / l;
-#pragma unroll
-      for (int j = 0; j < 32; ++j)
-        if (j < dpt) olat[bi][part * dpt + j] = o[j] * inv;
+    for (int u = 0; u < 4; ++u) {
+      const int sp = min(s0 + 4 * u, ns - 1);  // past the end: re-read (not used)
+      const int64_t p = base + (int64_t)sp * 64;
+      ml[u] = *reinterpret_cast<const f32x2_t*>(a.part_ml + p * 2);
+      v0[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f);
+      v1[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f + 4);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + 4 * u >= ns) break;
+      const float mn = fmaxf(m, ml[u][0]);
+      const float al = exp2f(m - mn), be = exp2f(ml[u][0] - mn);
+      l = l * al + ml[u][1] * be;
+      o0 = o0 * al + v0[u] * be;
+      o1 = o1 * al + v1[u] * be;
+      m = mn;
+    }
+  }
+  *reinterpret_cast<f32x4_t*>(&so[sg][f]) = o0;
+  *reinterpret_cast<f32x4_t*>(&so[sg][f + 4]) = o1;
+  if ((tid & 63) == 0) {
+    sm[sg] = m;
+    sl[sg] = l;
   }
   __syncthreads();
-
-  // -- 2. value up-projection
-  const int d = tid & 127, ch = tid >> 7;
-  float acc[MBT];
+  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float w[4], L = 0.f;
 #pragma unroll
-  for (int bi = 0; bi < MBT; ++bi) acc[bi] = 0.f;
-  const int64_t wrow = (int64_t)(h * 256 + 128 + d) * KV_LORA + ch * 256;
-  for (int c = 0; c < 256; c += 8) {
-    float w[8];
-    if constexpr (FP8) {
-      const u32x2_t codes = ld8((const uint8_t*)a.w_uv + wrow + c);
-      const float sc = a.w_uv_s[(2 * h + 1) * 4 + ((ch * 256 + c) >> 7)];
-      w[0] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 0) * sc;
-      w[1] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 1) * sc;
-      w[2] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 2) * sc;
-      w[3] = __builtin_amdgcn_cvt_f32_fp8((int)codes[0], 3) * sc;
-      w[4] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 0) * sc;
-      w[5] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 1) * sc;
-      w[6] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 2) * sc;
-      w[7] = __builtin_amdgcn_cvt_f32_fp8((int)codes[1], 3) * sc;
-    } else {
-      const u32x4_t raw = ld16((const uint16_t*)a.w_uv + wrow + c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[2 * j] = bf_lo(raw[j]);
-        w[2 * j + 1] = bf_hi(raw[j]);
-      }
-    }
-#pragma unroll
-    for (int bi = 0; bi < MBT; ++bi) {
-      if (bi < nb) {
-        const float* ol = &olat[bi][ch * 256 + c];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[bi] += w[j] * ol[j];
-      }
-    }
+  for (int g = 0; g < 4; ++g) {
+    w[g] = sl[g] > 0.f ? exp2f(sm[g] - M) : 0.f;  // a group with no split has l = 0, m = -inf
+    L += w[g] * sl[g];
   }
-  if (ch == 1) {
+  const float inv = 1.0f / L;
+  const int c = 2 * tid;  // features c, c+1
+  float v[2];
 #pragma unroll
-    for (int bi = 0; bi < MBT; ++bi) red[bi][d] = acc[bi];
+  for (int e = 0; e < 2; ++e) {
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc += w[g] * so[g][c + e];
+    v[e] = acc * inv;
   }
-  __syncthreads();
-  if (ch == 0) {
-#pragma unroll
-    for (int bi = 0; bi < MBT; ++bi) {
-      if (bi < nb) {
-        const float v = acc[bi] + red[bi][d];
-        const int64_t oi = (int64_t)(bt + bi) * O_IN + h * 128 + d;
-        if (a.o_f32) a.o_f32[oi] = v;
-        else a.o_bf16[oi] = f2bf(v);
-      }
-    }
+  const int64_t oi = ((int64_t)b * 64 + h) * KV_LORA + c;
+  if constexpr (FP8) {
+    const float sc = a.w_uv_s[(2 * h + 1) * 4 + (c >> 7)];
+    v[0] *= sc;
+    v[1] *= sc;
+    const uint32_t hi = pack_bf16x2(v[0], v[1]);
+    *reinterpret_cast<uint32_t*>(a.o_lat + oi) = hi;
+    *reinterpret_cast<uint32_t*>(a.o_lat + (int64_t)a.B * 64 * KV_LORA + oi) =
+        pack_bf16x2(v[0] - bf_lo(hi), v[1] - bf_hi(hi));
+  } else {
+    *reinterpret_cast<uint32_t*>(a.o_lat + oi) = pack_bf16x2(v[0], v[1]);
   }
 }
 
@@ -506,17 +478,17 @@ __global__ __launch_bounds__(256) void decode_merge_uv_kernel(DecodeAttnArgs a) 
 
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  dim3 g1(a.max_splits, a.B), g2(64, cdiv(a.B, MBT));
+  dim3 g1(a.max_splits, a.B), g2(64, a.B);
   if (a.fp8) {
     hipLaunchKernelGGL(decode_attn_kernel<true>, g1, dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_uv_kernel<true>, g2, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<true>, g2, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(decode_attn_kernel<false>, g1, dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_uv_kernel<false>, g2, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<false>, g2, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -164,16 +164,16 @@ struct DecodeAttnArgs {
   float scale;
   float* part_o;           // [B][max_splits][64][512] fp32
   float* part_ml;          // [B][max_splits][64][2] (running max, sum)
-  const void* w_uv;        // kv_b weight (bf16, or FP8 codes); W_UV,h = rows h*256+128 .. +255
-  const float* w_uv_s;     // FP8: kv_b block scales [128][4]
-  float* o_f32;            // output o [B][8192] float32 (when set), else
-  uint16_t* o_bf16;        //        o [B][8192] bf16
+  const float* w_uv_s;     // FP8: kv_b block scales [128][4] (W_UV,h blocks are rows 2h+1)
+  uint16_t* o_lat;         // merged latent output, bf16 [B][64][512] (FP8: high parts, then residuals)
 };
+// Split attention + merge. Output: o_lat (see DecodeAttnArgs); W_UV is applied by the caller.
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s);
 
 // FP8 activation quantiser for a bf16/fp32 matrix [rows, K] (K multiple of 128).
-hipError_t quantize_rows_f32(const float* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
-                             hipStream_t s);
+// x2 (optional): a second matrix added to x element-wise before quantising (same layout).
+hipError_t quantize_rows_f32(const float* x, const float* x2, int64_t ldx, int rows, int K, uint8_t* codes,
+                             float* scales, hipStream_t s);
 hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
                               hipStream_t s);
 

@@ -61,6 +61,17 @@ __global__ void transpose_uk_kernel(const void* kvb, uint16_t* ukT) {
   ukT[((int64_t)h * KV_LORA + c) * NOPE + d] = v;
 }
 
+// FP8: W_UV,h codes widened to their exact bf16 values, uvw[h][d][c] = code(kv_b[h*256+128+d][c])
+// (the block scales are applied to the other operand).
+__global__ void widen_uv_kernel(const uint8_t* kvb, uint16_t* uvw) {
+  const int h = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // over 128*512
+  if (idx >= VD * KV_LORA) return;
+  const int d = idx / KV_LORA, c = idx % KV_LORA;
+  uvw[(int64_t)h * VD * KV_LORA + idx] =
+      f2bf(__builtin_amdgcn_cvt_f32_fp8((int)kvb[((int64_t)h * 256 + 128 + d) * KV_LORA + c], 0));
+}
+
 }  // namespace
 
 struct mla_ctx {
@@ -76,6 +87,8 @@ struct mla_ctx {
   const void* w_kvb;
   const float* s_kvb;  // [128, 4]
   const uint16_t* w_ukT;  // packed [64][512][128] bf16
+  const uint16_t* w_uv;   // W_UV,h rows as bf16: kv_b itself (row stride 512, head stride 256 rows)
+  int64_t uv_head_stride; //   or, FP8, the packed widened codes [64][128][512]
   const void* w_o;
   const float* s_o;    // [56, 64]
   const float* rope_cs;
@@ -99,7 +112,7 @@ mla_status check_config(const mla_config* c) {
 }
 
 struct PackedLayout {
-  size_t qkva, s_qkva, ukT, g_q, g_kv, rope, total;
+  size_t qkva, s_qkva, ukT, uvw, g_q, g_kv, rope, total;
 };
 
 PackedLayout packed_layout(const mla_config* c) {
@@ -114,6 +127,7 @@ PackedLayout packed_layout(const mla_config* c) {
   L.qkva = take((size_t)QKVA_N * HIDDEN * (fp8 ? 1 : 2));
   L.s_qkva = take(fp8 ? (size_t)17 * 56 * sizeof(float) : 0);
   L.ukT = take((size_t)HEADS * KV_LORA * NOPE * 2);
+  L.uvw = take(fp8 ? (size_t)HEADS * VD * KV_LORA * 2 : 0);
   L.g_q = take(Q_LORA * 2);
   L.g_kv = take(KV_LORA * 2);
   L.rope = take((size_t)c->max_positions * 32 * 2 * sizeof(float));
@@ -150,6 +164,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n) {
 struct WsLayout {
   size_t counters, cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
   size_t knope_lo, vt_lo, qs;  // FP8 only: residual planes, split q_nope
+  size_t o_lat;                // decode: merged latent attention output (bf16; FP8: 2 planes)
   size_t x8, x8s, qh8s, o32, o8, o8s, total;
   int64_t gpart_floats;
   int64_t vt_ld;
@@ -165,8 +180,11 @@ int64_t max_gemm_part(int ntok, int nkeys_seq, bool decode, bool fp8) {
   upd(ntok, QKVA_N, HIDDEN, 1);
   upd(ntok, QB_N, Q_LORA, 1);
   upd(ntok, HIDDEN, O_IN, 1);
-  if (decode) {  // absorb (FP8: high and residual parts of q_nope stacked as 2 * ntok rows)
-    if (ntok > 0) mx = std::max(mx, mla_k::gemm_part_floats(fp8 ? 2 * ntok : ntok, KV_LORA, NOPE, HEADS));
+  if (decode) {  // absorb and W_UV (FP8: high and residual parts stacked as 2 * ntok rows)
+    if (ntok > 0) {
+      mx = std::max(mx, mla_k::gemm_part_floats(fp8 ? 2 * ntok : ntok, KV_LORA, NOPE, HEADS));
+      mx = std::max(mx, mla_k::gemm_part_floats(fp8 ? 2 * ntok : ntok, VD, KV_LORA, HEADS));
+    }
   } else {
     upd(nkeys_seq, KVB_N, KV_LORA, 1);
   }
@@ -200,7 +218,8 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   L.x8 = take(fp8 ? (size_t)ntok * HIDDEN : 0);
   L.x8s = take(fp8 ? (size_t)ntok * (HIDDEN / 128) * 4 : 0);
   L.qh8s = take(fp8 ? (size_t)ntok * (Q_LORA / 128) * 4 : 0);
-  L.o32 = take(fp8 ? (size_t)ntok * O_IN * 4 : 0);
+  L.o32 = take(fp8 ? (size_t)ntok * O_IN * 4 * (decode_splits > 0 ? 2 : 1) : 0);  // decode: 2 planes
+  L.o_lat = take(decode_splits > 0 ? (size_t)nbatch * HEADS * KV_LORA * 2 * (fp8 ? 2 : 1) : 0);
   L.o8 = take(fp8 ? (size_t)ntok * O_IN : 0);
   L.o8s = take(fp8 ? (size_t)ntok * (O_IN / 128) * 4 : 0);
   L.gpart_floats = gpart_floats;
@@ -363,6 +382,11 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
     hipLaunchKernelGGL(transpose_uk_kernel<false>, dim3(KV_LORA * NOPE / 256, HEADS), dim3(256), 0, s, w->kv_b,
                        (uint16_t*)(pk + L.ukT));
   HIP_TRY(hipGetLastError());
+  if (fp8) {
+    hipLaunchKernelGGL(widen_uv_kernel, dim3(VD * KV_LORA / 256, HEADS), dim3(256), 0, s, (const uint8_t*)w->kv_b,
+                       (uint16_t*)(pk + L.uvw));
+    HIP_TRY(hipGetLastError());
+  }
   // RoPE table: angle = position * theta^(-2i/64), computed in double, stored float32
   const int P = cfg->max_positions;
   std::vector<float> cs((size_t)P * 64);
@@ -390,6 +414,13 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
   c->w_kvb = w->kv_b;
   c->s_kvb = w->kv_b_s;
   c->w_ukT = (const uint16_t*)(pk + L.ukT);
+  if (fp8) {
+    c->w_uv = (const uint16_t*)(pk + L.uvw);
+    c->uv_head_stride = (int64_t)VD * KV_LORA;
+  } else {
+    c->w_uv = (const uint16_t*)w->kv_b + (int64_t)NOPE * KV_LORA;
+    c->uv_head_stride = (int64_t)256 * KV_LORA;
+  }
   c->w_o = w->o;
   c->s_o = w->o_s;
   c->rope_cs = (const float*)(pk + L.rope);
@@ -512,7 +543,8 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   HIP_TRY(mla_k::prefill_attention(pa, s));
   // 6. o_proj
   if (fp8)
-    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), O_IN, ntok, O_IN, w + L.o8, (float*)(w + L.o8s), s));
+    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), nullptr, O_IN, ntok, O_IN, w + L.o8,
+                                     (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
   set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
@@ -592,19 +624,32 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
   g.tag = mla_k::TAG_ABSORB;
   HIP_TRY(mla_k::gemm_bf16(g, s));
-  // 5. split attention over the latent cache, merge, W_UV (float32) -> o
+  // 5. split attention over the latent cache and its merge -> o_lat
   mla_k::DecodeAttnArgs da{};
   da.q_lat = w + L.q_lat; da.q_lat_lo = (int64_t)B * HEADS * KV_LORA; da.q = w + L.q;
   da.cache = (const uint8_t*)cache->data;
   da.entry_bytes = eb; da.fp8 = fp8; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
   da.seq_ids = seq_ids_d; da.offset = cache->offset_d; da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
   da.max_splits = dp.max_splits; da.scale = ctx->scale; da.part_o = (float*)(w + L.part_o);
-  da.part_ml = (float*)(w + L.part_ml); da.w_uv = ctx->w_kvb; da.w_uv_s = ctx->s_kvb;
-  da.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr; da.o_bf16 = (uint16_t*)(w + L.o);
+  da.part_ml = (float*)(w + L.part_ml); da.w_uv_s = ctx->s_kvb; da.o_lat = (uint16_t*)(w + L.o_lat);
   HIP_TRY(mla_k::decode_attention(da, s));
-  // 6. o_proj
+  // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (already
+  //    scaled by the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the
+  //    exact code values, two float32 products that the quantiser adds.
+  g = gemm_common(w, L);
+  g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
+  g.B = ctx->w_uv; g.ldb = KV_LORA; g.sB = ctx->uv_head_stride;
+  g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.ldc = O_IN; g.sC = VD; g.tag = mla_k::TAG_UV;
+  if (fp8) {
+    g.M = 2 * B; g.C = w + L.o32; g.epi = mla_k::EPI_F32;
+  } else {
+    g.M = B; g.C = w + L.o; g.epi = mla_k::EPI_BF16;
+  }
+  HIP_TRY(mla_k::gemm_bf16(g, s));
+  // 7. o_proj
   if (fp8)
-    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), O_IN, B, O_IN, w + L.o8, (float*)(w + L.o8s), s));
+    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), (const float*)(w + L.o32) + (int64_t)B * O_IN, O_IN,
+                                     B, O_IN, w + L.o8, (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
   set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;

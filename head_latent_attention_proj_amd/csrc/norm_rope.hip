@@ -194,7 +194,8 @@ __global__ void copy_append_kernel(uint8_t* dst, const uint8_t* src, int64_t nve
 
 // One wave per 128-feature group of one row.
 template <typename T>
-__global__ void quantize_rows_kernel(const T* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales) {
+__global__ void quantize_rows_kernel(const T* x, const T* x2, int64_t ldx, int rows, int K, uint8_t* codes,
+                                     float* scales) {
   const int lane = threadIdx.x & 63;
   const int64_t gid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int groups = K / 128;
@@ -208,6 +209,11 @@ __global__ void quantize_rows_kernel(const T* x, int64_t ldx, int rows, int K, u
   } else {
     v0 = src[lane];
     v1 = src[lane + 64];
+    if (x2) {
+      const T* s2 = x2 + r * ldx + gi * 128;
+      v0 += s2[lane];
+      v1 += s2[lane + 64];
+    }
   }
   const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
   const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
@@ -263,12 +269,12 @@ hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_byte
   return hipGetLastError();
 }
 
-hipError_t quantize_rows_f32(const float* x, int64_t ldx, int rows, int K, uint8_t* codes, float* scales,
-                             hipStream_t s) {
+hipError_t quantize_rows_f32(const float* x, const float* x2, int64_t ldx, int rows, int K, uint8_t* codes,
+                             float* scales, hipStream_t s) {
   const int64_t waves = (int64_t)rows * (K / 128);
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, ldx, rows,
-                     K, codes, scales);
+  hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, x2, ldx,
+                     rows, K, codes, scales);
   return hipGetLastError();
 }
 
@@ -276,8 +282,8 @@ hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, u
                               hipStream_t s) {
   const int64_t waves = (int64_t)rows * (K / 128);
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, ldx,
-                     rows, K, codes, scales);
+  hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x,
+                     (const uint16_t*)nullptr, ldx, rows, K, codes, scales);
   return hipGetLastError();
 }
 
