@@ -291,28 +291,27 @@ struct Plan {
   int tiles;  // workgroups per (split, batch)
 };
 
-int pow2_at_least(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-
 Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1) {
   Plan pl{};
   pl.splits = 1;
   pl.ksplit = K;
   pl.ysplit = 1;
-  if (M <= 64) {
+  // Streaming kernel for decode-sized M: always up to 16 rows; up to 64 rows when K is short
+  // (kv_b, W_UK / W_UV), where a staged tile would spend most of its time filling LDS.
+  if (M <= 16 || (M <= 64 && K <= 512)) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     pl.tiles = cdiv(N, 16);
-    // fewer tiles than CUs: split K over workgroups too (partials summed by the consumer)
-    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 256 && K / 32 >= 32 * pl.ysplit)
+    const int steps = K / 32;
+    // Measured on MI355X: a stream runs best with at least ~24 K steps per wave and ~1-2
+    // thousand waves in the grid. K is first split over workgroups where the consumer adds
+    // the parts (ysplit), then over the waves of a workgroup.
+    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 512 && steps / (pl.ysplit * 2) >= 32)
       pl.ysplit *= 2;
-    // about three thousand waves in flight over the GPU; no more waves than 32-wide K steps
-    int kw = pow2_at_least(cdiv(3000, pl.tiles * batch * pl.ysplit));
-    kw = std::min(kw, pl.mt == 1 ? 16 : 8);
-    while (kw > 1 && kw > K / 32 / pl.ysplit) kw >>= 1;
+    int kw = 1;
+    while (kw * 2 <= (pl.mt == 1 ? 16 : 8) && steps / (pl.ysplit * kw * 2) >= 24 &&
+           pl.tiles * batch * pl.ysplit * kw * 2 <= 2048)
+      kw *= 2;
     pl.kw = kw;
     return pl;
   }

@@ -368,12 +368,6 @@ struct Plan8 {
   int tiles;
 };
 
-int pow2_at_least8(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-
 bool tag_precise(int tag) { return tag == TAG_QKVA || tag == TAG_QB || tag == TAG_KVB; }
 
 // prec: the precise form keeps 128 x 128 tiles (two accumulator sets per lane do not fit the
@@ -384,15 +378,17 @@ Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
   pl.ksplit = K;
   pl.ysplit = 1;
   const int ngroups = K / 128;
-  if (M <= 64) {
+  // streaming kernel up to 16 rows (64 when K is short), as for bf16; a K step is one 128 group
+  if (M <= 16 || (M <= 64 && K <= 512)) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     pl.tiles = cdiv(N, 16);
-    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 256 && ngroups >= 8 * pl.ysplit)
+    while (pl.ysplit * 2 <= ysplit_max && pl.tiles * batch * pl.ysplit < 512 && ngroups / (pl.ysplit * 2) >= 8)
       pl.ysplit *= 2;
-    int kw = pow2_at_least8(cdiv(3000, pl.tiles * batch * pl.ysplit));
-    kw = std::min(kw, pl.mt == 1 ? 16 : 8);
-    while (kw > 1 && kw > ngroups / pl.ysplit) kw >>= 1;
+    int kw = 1;
+    while (kw * 2 <= (pl.mt == 1 ? 16 : 8) && ngroups / (pl.ysplit * kw * 2) >= 6 &&
+           pl.tiles * batch * pl.ysplit * kw * 2 <= 2048)
+      kw *= 2;
     pl.kw = kw;
     return pl;
   }

@@ -94,18 +94,34 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   }
 
   const float* row = a.cqkv + (int64_t)tok * QKVA_N;
-  // partial sums of a K-split projection are added in a fixed order
-  auto cval = [&](int c) {
-    float v = row[c];
-    for (int p = 1; p < a.n_part; ++p) v += row[p * a.part_stride + c];
-    return v;
-  };
+  // Every load of the token's row (all K-split parts, up to MAX_PARTS) is issued before any is
+  // used: at decode this kernel is one workgroup per token and runs at load latency. The parts
+  // are then added in part order.
+  constexpr int MAX_PARTS = 4;
+  float pv[MAX_PARTS][9];
+#pragma unroll
+  for (int p = 0; p < MAX_PARTS; ++p) {
+    const float* r = row + (p < a.n_part ? p : 0) * a.part_stride;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pv[p][i] = r[tid + i * 256];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pv[p][6 + i] = r[Q_LORA + tid + i * 256];
+    pv[p][8] = tid < ROPE ? r[Q_LORA + KV_LORA + tid] : 0.f;
+  }
+  float v9[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    v9[i] = pv[0][i];
+#pragma unroll
+    for (int p = 1; p < MAX_PARTS; ++p)
+      if (p < a.n_part) v9[i] += pv[p][i];
+  }
   // ---- query latent RMSNorm (1536 = 6 per thread)
   float xq[6];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 6; ++i) {
-    xq[i] = cval(tid + i * 256);
+    xq[i] = v9[i];
     ss += xq[i] * xq[i];
   }
   const float rq = 1.0f / sqrtf(block_sum256(ss, red) / (float)Q_LORA + a.eps);
@@ -114,7 +130,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    xc[i] = cval(Q_LORA + tid + i * 256);
+    xc[i] = v9[6 + i];
     ss += xc[i] * xc[i];
   }
   const float rc = 1.0f / sqrtf(block_sum256(ss, red) / (float)KV_LORA + a.eps);
@@ -166,10 +182,14 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
       }
     }
   }
-  // ---- shared rotary key: 32 pairs, rotated by this token's position
+  // ---- shared rotary key: 32 pairs, rotated by this token's position (thread t < 64 holds
+  // rotary feature t; pairs are exchanged through LDS)
+  __shared__ float kraw[ROPE];
+  if (tid < ROPE) kraw[tid] = v9[8];
+  __syncthreads();
   if (tid < ROPE / 2) {
-    const float k0 = cval(Q_LORA + KV_LORA + 2 * tid);
-    const float k1 = cval(Q_LORA + KV_LORA + 2 * tid + 1);
+    const float k0 = kraw[2 * tid];
+    const float k1 = kraw[2 * tid + 1];
     const float c = a.rope_cs[(int64_t)pos * 32 + tid];
     const float s = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + tid];
     if (a.fp8) {  // float32 rotary key: the scores it feeds stay exact to float32
