@@ -393,6 +393,212 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   }
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// D(32x32) += A(32x16) B(16x32), bf16 in, float32 accumulate. Lane l supplies row (A) / column
+// (B) l%32 and the eight k of group l/32; the result holds column l%32, rows
+// 8*(e/4) + 4*(l/32) + e%4 for e = 0..15 (checked on gfx950).
+MLA_DEV f32x16_t mfma_bf16_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3. With lane r of a group
+// pointing at row (r/4), columns 4*(r%4) .. +3 of a row-major tile, lane i receives column i of
+// rows 0..3: a K-major fragment read out of a K x N row-major tile. The value is bit-cast whole
+// (per-element access of the 16-bit vector is avoided).
+MLA_DEV u32x2_t ds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Latent decode attention, bf16 cache entries, 32x32 MFMA tiles. Workgroup = (sequence, split),
+// 8 waves = 2 head groups of 32 x 4 feature quarters; each 16-byte cache fragment read from LDS
+// feeds 32 heads. 32-position blocks are staged row-major through registers, two blocks ahead
+// (two register sets alternate), so about 72 KB per CU are in flight while a block is used:
+//   S^T = C Q^T      A = cache rows (ds_read_b128), B = queries in registers (9 k-steps of 16
+//                    per wave); the four quarters' partial scores are added through LDS in a
+//                    fixed order, identical in all four waves of a head group;
+//   O^T += C^T P^T   A = cache columns via transpose reads (no transposed copy is written),
+//                    B = probabilities straight from the score accumulators (same lane layout
+//                    up to a fixed permutation of positions, used on both operands).
+// The running maximum is raised only when a block's maximum exceeds it by more than 8 (log2
+// units), so probabilities stay <= 256 and the output accumulators are rescaled rarely; the
+// decision is taken for the whole wave.
+constexpr int LDC2 = 584;  // 1168-byte rows: 16 consecutive rows start in distinct 4-bank groups
+
+__global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs a) {
+  using namespace mla_dims;
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int seq = a.seq_ids[b];
+  const int L = a.len[seq];
+  const int c0 = split * a.chunk;
+  if (c0 >= L) return;
+  const int c1 = min(L, c0 + a.chunk);
+  const int64_t slot0 = a.offset[seq];
+  const int nblk = cdiv(c1 - c0, DKB);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 1, fq = wave >> 1;
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int head = hg * 32 + l32;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sC[(DKB + 1) * LDC2];  // + a scratch row
+  __shared__ __attribute__((aligned(16))) float xS[8][16][64];
+
+  // staging: 32 rows x 72 chunks of 16 bytes; thread takes chunks c = tid + 512 i (i < 5, c < 2304).
+  // Every load is issued unconditionally (an index past the block re-reads its last chunk and is
+  // not stored): with no branch among them, the compiler's wait counts stay exact and the two
+  // register sets really are in flight together.
+  auto gload = [&](int blk, u32x4_t (&rs)[5]) {
+    const int kb = c0 + blk * DKB;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int c = min(tid + 512 * i, DKB * 72 - 1);
+      const int key = min(kb + c / 72, c1 - 1);  // rows past the split's end: re-read, masked later
+      rs[i] = ld16(a.cache + (slot0 + key) * BF16_ENTRY_BYTES + (c % 72) * 16);
+    }
+  };
+  auto sstore = [&](const u32x4_t (&rs)[5]) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {  // chunks past the block go to a scratch row (no branch)
+      const int c = tid + 512 * i;
+      st16(c < DKB * 72 ? sC + (c / 72) * LDC2 + (c % 72) * 8 : sC + DKB * LDC2 + (tid & 63) * 8, rs[i]);
+    }
+  };
+  u32x4_t rA[5], rB[5];
+  gload(0, rA);
+  gload(min(1, nblk - 1), rB);
+
+  // query fragments: column = head, features 144*fq + 16*ks + 8*kg .. +7 (>= 512: rotary part,
+  // rotated at the query's position)
+  bf16x8_t qf[9];
+  {
+    const int pos = L - 1;
+    const uint16_t* ql = (const uint16_t*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)b * 64 + head) * QK + NOPE;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      const int f = 144 * fq + 16 * ks + 8 * kg;
+      if (f < KV_LORA) {
+        qf[ks] = as_bf16x8(ld16(ql + f));
+      } else {
+        const u32x4_t raw = ld16(qp + (f - KV_LORA));
+        const int pair0 = (f - KV_LORA) >> 1;
+        u32x4_t rot;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = bf_lo(raw[j]), x1 = bf_hi(raw[j]);
+          const float c = a.rope_cs[(int64_t)pos * 32 + pair0 + j];
+          const float sn = a.rope_cs[(int64_t)a.max_pos * 32 + (int64_t)pos * 32 + pair0 + j];
+          rot[j] = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+        }
+        qf[ks] = as_bf16x8(rot);
+      }
+    }
+  }
+  // All prologue loads complete here, so that inside the block loop the compiler tracks only the
+  // staging loads (otherwise it waits for every load before the first use of a query fragment
+  // in each iteration, which drains the staging pipeline).
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const float sl2 = a.scale * LOG2E;
+  float m_used = -INFINITY, l_run = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o[t] = f32x16_t{};
+
+  auto step = [&](int blk, u32x4_t (&rs)[5]) {
+    __syncthreads();  // the previous block's LDS reads are done
+    sstore(rs);
+    __syncthreads();
+    // unconditional (past the end: the last block again, from cache) so that no branch sits
+    // among the loads and the compiler's wait counts stay exact
+    gload(min(blk + 2, nblk - 1), rs);
+    const int kb = c0 + blk * DKB;  // >= c1 for the masked extra block
+
+    // partial S^T[pos][head] over this wave's 144 features (two chains, added at the end)
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+    {
+      const uint16_t* ap = sC + l32 * LDC2 + 144 * fq + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < 9; ks += 2) {
+        s0 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap + 16 * ks)), qf[ks], s0);
+        if (ks + 1 < 9) s1 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap + 16 * ks + 16)), qf[ks + 1], s1);
+      }
+    }
+    const f32x16_t sacc = s0 + s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xS[wave][e][lane] = sacc[e];
+    __syncthreads();
+    float sv[16];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = ((xS[hg][e][lane] + xS[hg + 2][e][lane]) + xS[hg + 4][e][lane]) + xS[hg + 6][e][lane];
+      v *= sl2;
+      if (kb + 8 * (e >> 2) + 4 * kg + (e & 3) >= c1) v = -INFINITY;
+      sv[e] = v;
+      bmax = fmaxf(bmax, v);
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    if (__any(bmax > m_used + 8.0f)) {  // wave-uniform
+      const float mn = fmaxf(m_used, bmax);
+      const float al = exp2f(m_used - mn);
+      l_run *= al;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] *= al;
+      m_used = mn;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sv[e] = exp2f(sv[e] - m_used);
+      psum += sv[e];
+    }
+    l_run += psum;
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pf[ks] = as_bf16x8(u32x4_t{pack_bf16x2(sv[8 * ks], sv[8 * ks + 1]), pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]),
+                                 pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]), pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7])});
+
+    // O^T[feature][head] over this wave's 128 latent features: 4 tiles x 2 position steps
+    const int r = lane & 15, cc = 16 * ((lane >> 4) & 1);
+    const uint16_t* tp = sC + (4 * kg + (r >> 2)) * LDC2 + 128 * fq + cc + 4 * (r & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* p0 = tp + 16 * ks * LDC2 + 32 * t;
+        const u32x2_t w0 = ds_read_tr16(p0), w1 = ds_read_tr16(p0 + 8 * LDC2);
+        o[t] = mfma_bf16_32x32x16(as_bf16x8(u32x4_t{w0[0], w0[1], w1[0], w1[1]}), pf[ks], o[t]);
+      }
+  };
+  // Both steps run unconditionally (with an odd block count the last step is a fully masked
+  // block, which changes nothing): a branch around a step would again blur the wait counts.
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, rA);
+    step(blk + 1, rB);
+  }
+
+  // ---- split outputs: unnormalised o (relative to m_used), m_used and the sum per head
+  l_run += __shfl_xor(l_run, 32);
+  const int64_t pidx = ((int64_t)b * a.max_splits + split) * 64 + head;
+  float* po = a.part_o + pidx * KV_LORA + 128 * fq + 4 * kg;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4_t*>(po + 32 * t + 8 * q) = f32x4_t{o[t][4 * q], o[t][4 * q + 1], o[t][4 * q + 2], o[t][4 * q + 3]};
+  if (fq == 0 && kg == 0) {
+    a.part_ml[pidx * 2] = m_used;
+    a.part_ml[pidx * 2 + 1] = l_run;
+  }
+}
+
 // Merge of the splits, float32. One workgroup per (head h, sequence b): 4 groups of 64 threads
 // take every 4th split each (8 latent features per thread, a running (max, sum, o) rescaled as
 // splits arrive, four splits' loads in flight), then the 4 groups are combined through LDS in a
@@ -485,7 +691,7 @@ hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel<true>, g2, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(decode_attn_kernel<false>, g1, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(decode_attn_bf16_kernel, g1, dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel<false>, g2, dim3(256), 0, s, a);
