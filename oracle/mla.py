@@ -169,7 +169,7 @@ def attend(q_nope: np.ndarray, q_pe: np.ndarray, k: np.ndarray, v: np.ndarray, q
 
 
 def forward(x: np.ndarray, w: dict, cfg: Config = KIMI_K2, cache: tuple | None = None,
-            rows: np.ndarray | None = None, w8a8: bool = False) -> dict:
+            rows: np.ndarray | None = None, w8a8: bool = False, absorbed: bool = False) -> dict:
     """One MLA call for ONE sequence: prefill (T tokens) or decode (T = 1) on a latent cache.
 
     x        [T, hidden] float64, this call's tokens.
@@ -178,6 +178,10 @@ def forward(x: np.ndarray, w: dict, cfg: Config = KIMI_K2, cache: tuple | None =
     cache    (c_hat [L0, kv_lora], k_pe [L0, rope]) entries of positions 0..L0-1, or None.
     rows     indices into this call's tokens whose outputs are wanted (default: all).
     w8a8     pass every projection input through the dynamic FP8 activation quantiser.
+    absorbed attend in the 512-feature latent space (attend_absorbed) instead of rebuilding
+             per-head keys and values for every cached position: the same values (pinned
+             against the rebuilt form), at a cost that stays small for tens of thousands of
+             cached positions.
 
     Token t sits at position L0 + t. All T entries are appended to the cache before the
     scores are formed, so the keys cover positions 0..L0+T-1 and the causal mask limits each
@@ -198,10 +202,12 @@ def forward(x: np.ndarray, w: dict, cfg: Config = KIMI_K2, cache: tuple | None =
         c_all = np.concatenate([cache[0], lat["c_hat"]], axis=0)
         kpe_all = np.concatenate([cache[1], lat["k_pe"]], axis=0)
     n_keys = l0 + int(rows.max()) + 1 if rows.size else 0
-    k, v = rebuild_kv(c_all[:n_keys], kpe_all[:n_keys], w["kv_b"], cfg)
-
     qp = query_path(x[rows], w, pos[rows], cfg, w8a8)
-    o = attend(qp["q_nope"], qp["q_pe"], k, v, pos[rows], cfg.sigma)
+    if absorbed:
+        o = attend_absorbed(qp["q_nope"], qp["q_pe"], c_all[:n_keys], kpe_all[:n_keys], w["kv_b"], pos[rows], cfg)
+    else:
+        k, v = rebuild_kv(c_all[:n_keys], kpe_all[:n_keys], w["kv_b"], cfg)
+        o = attend(qp["q_nope"], qp["q_pe"], k, v, pos[rows], cfg.sigma)
     o_flat = o.reshape(len(rows), cfg.heads * cfg.v)  # index h*128 + d
     y = linear(_act(o_flat, w8a8), w["o"])
     return {"y": y, "o": o_flat, "c_hat": lat["c_hat"], "k_pe": lat["k_pe"], "ckv": lat["ckv"], **qp}

@@ -217,6 +217,23 @@ def test_absorbed_form_equals_rebuilt_form():
     assert np.allclose(o_abs.reshape(7, -1), out["o"], rtol=0, atol=1e-12)
 
 
+def test_forward_absorbed_option_equals_rebuilt_forward():
+    """forward(absorbed=True) (latent-space attention) against the rebuilt form, with a cached
+    prefix and a subset of query rows."""
+    cfg = mla.Config(hidden=96, q_lora=48, kv_lora=32, heads=4, nope=16, rope=8, v=12)
+    w = tiny_weights(cfg, seed=61)
+    rng = np.random.default_rng(62)
+    x0 = rng.standard_normal((5, cfg.hidden))
+    x1 = rng.standard_normal((6, cfg.hidden))
+    first = mla.forward(x0, w, cfg)
+    cache = (first["c_hat"], first["k_pe"])
+    rows = np.array([0, 3, 5])
+    a = mla.forward(x1, w, cfg, cache=cache, rows=rows)
+    b = mla.forward(x1, w, cfg, cache=cache, rows=rows, absorbed=True)
+    assert np.allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+    assert np.allclose(a["o"], b["o"], rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------------ P9, P11
 def test_prefill_equals_prefill_then_decode():
     cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
