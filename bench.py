@@ -72,6 +72,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="layer copies stepped in turn")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -195,6 +196,62 @@ def main():
             "sum_len": int(lens.sum()),
             "note": "one copy of the weights (MALL may hold part of them); includes one length rewind per step",
         }
+
+    if not args.no_extra and not args.no_fp8:
+        # ---------------- FP8 weights (E4M3, 128x128 block scales): decode B=128 x 16384 cached
+        # positions, prefill B=4 x T=4096
+        log("FP8: generating weights and a 128 x 16384 cache")
+        wq = synth.make_weights_fp8(seed=0)
+        lf = binding.Layer(binding.weights_to_device(wq), max_positions=16448, wdtype=binding.WDTYPE_FP8)
+        B8, P8 = 128, 16384
+        ents8 = torch.from_numpy(synth.make_cache_entries_fp8(P8, seed=2100)).cuda()
+        c8 = binding.Cache(lf, [P8 + 1] * B8)
+        for s_ in range(B8):
+            lf.cache_append(c8, s_, ents8)
+        del ents8
+        x8 = binding.bf16_tensor(synth.make_hidden(B8, seed=1005))
+        y8 = torch.empty_like(x8)
+        sid8h = np.arange(B8, dtype=np.int32)
+        sid8d = torch.arange(B8, dtype=torch.int32, device="cuda")
+        lens8 = np.full(B8, P8, dtype=np.int32)
+        torch.cuda.synchronize()
+
+        def dec8(i):
+            lf.decode(c8, sid8h, x8, y=y8, seq_ids_d=sid8d)
+            c8.len_h[:] = lens8
+            c8.len_d.sub_(1)
+
+        log("timing FP8 decode B=128 x 16384")
+        t = timed_loop(torch, dec8, 10, 3)
+        w8_bytes = sum(int(v.nbytes) for k, v in wq.items())
+        byts = w8_bytes + 784 * B8 * (P8 + 1) + 2 * 2 * 7168 * B8
+        extra["fp8_decode_B128_L16384"] = {
+            "us_per_step": round(t * 1e6, 2), "bytes": int(byts),
+            "hbm_gbs": round(byts / t / 1e9, 1), "hbm_frac": round(byts / t / HBM_PEAK, 4),
+            "note": "784-byte FP8 cache slots (synthetic codes); includes one length rewind per step",
+        }
+        del c8
+        log("timing FP8 prefill B=4 x T=4096")
+        T8 = 4096
+        xp8 = binding.bf16_tensor(synth.make_hidden(4 * T8, seed=1006))
+        yp8 = torch.empty_like(xp8)
+        cp8 = binding.Cache(lf, [T8] * 4)
+        qs8 = np.arange(5, dtype=np.int32) * T8
+        sids = np.arange(4, dtype=np.int32)
+
+        def pre8(i):
+            cp8.len_h[:] = 0
+            cp8.len_d.zero_()
+            lf.prefill(cp8, sids, qs8, xp8, y=yp8)
+
+        t = timed_loop(torch, pre8, 3, 1)
+        fl = 4 * prefill_flops(T8)
+        extra["fp8_prefill_B4_T4096"] = {
+            "ms": round(t * 1e3, 3), "tokens_per_s": round(4 * T8 / t, 1), "tflops": round(fl / t / 1e12, 2),
+            "note": "flops count projections and causal attention once; o_proj runs on FP8 MFMA, the "
+                    "other projections on bf16 MFMA over exactly widened codes, attention at split precision",
+        }
+        del cp8, lf
 
     # a plain 64 MiB device copy: the reference point that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
     # counters to bytes (its algorithmic traffic is exactly 64 MiB read + 64 MiB written)

@@ -152,7 +152,9 @@ DecodePlan plan_decode(int B, const int* lens_after, int n) {
     max_len = std::max(max_len, lens_after[i]);
   }
   DecodePlan p;
-  p.chunk = (int)std::max<int64_t>(32, round_up((total + 511) / 512, 32));
+  // at least 64 positions per split: fewer float32 partials to write and merge when the batch
+  // holds little cache (measured on MI355X at one sequence of 1000 positions)
+  p.chunk = (int)std::max<int64_t>(64, round_up((total + 511) / 512, 32));
   p.max_splits = (max_len + p.chunk - 1) / p.chunk;
   while ((int64_t)B * p.max_splits > DECODE_MAX_WG) {
     p.chunk *= 2;

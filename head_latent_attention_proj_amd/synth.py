@@ -185,6 +185,21 @@ def make_cache_entries(n: int, d: Dims = KIMI_K2, seed: int = 2000, latent_std: 
     return f32_to_bf16_bits(np.concatenate([lat, kpe], axis=1).astype(np.float32))
 
 
+def make_cache_entries_fp8(n: int, seed: int = 2100) -> np.ndarray:
+    """Synthetic 784-byte FP8 cache slots [n, 784] (uint8) for timing long caches: 512 random
+    E4M3FN codes (any finite code, either sign), four float32 group scales 2^U(-9, -6) and a
+    float32 rotary key N(0, 1.7)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7F, size=(n, 512), dtype=np.uint8) | (rng.integers(0, 2, size=(n, 512), dtype=np.uint8) << 7)
+    scales = np.exp2(rng.uniform(-9.0, -6.0, size=(n, 4))).astype(np.float32)
+    kpe = rng.normal(0.0, 1.7, size=(n, 64)).astype(np.float32)
+    out = np.empty((n, 784), dtype=np.uint8)
+    out[:, :512] = codes
+    out[:, 512:528] = scales.view(np.uint8).reshape(n, 16)
+    out[:, 528:] = kpe.view(np.uint8).reshape(n, 256)
+    return out
+
+
 def make_activations(rows: int, cols: int, seed: int, std: float = 1.0) -> np.ndarray:
     """A [rows, cols] N(0, std) activation matrix in bf16 bits (e.g. an o_proj input)."""
     rng = np.random.default_rng(seed)
