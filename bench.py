@@ -131,6 +131,10 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     for i in range(10):
         gemm(xo, layers[i % args.copies].weights["o"], yo, 1, 7168, 8192, stage="oproj")
+    # hold the stream for a few milliseconds so that every (event, launch, event) triple below is
+    # queued before the first one runs: the events then bracket back-to-back kernels, not the
+    # host's launch latency
+    torch.cuda._sleep(20_000_000)
     for i in range(n_ev):
         evs[i][0].record(stream)
         gemm(xo, layers[i % args.copies].weights["o"], yo, 1, 7168, 8192, stage="oproj")
