@@ -1,10 +1,11 @@
-// bf16 MFMA GEMMs for the five MLA projections and the per-head absorption products.
+// bf16 GEMMs (MFMA tiles; VALU for one or two rows) for the five MLA projections and the per-head
+// absorption products.
 //
 // C[b] = A[b] * B[b]^T with A [M, K] and B [N, K] both K-contiguous: nn.Linear keeps its weight
 // [out, in] ("Key content up-projection" page, Parameters), so every projection y = x W^T is
 // this "NT" form and both MFMA operands load 16 contiguous bytes per lane.
 //
-// Two kernels:
+// Three kernels:
 //   * gemm_tile   -- prefill-sized M: BM x BN workgroup tile staged through LDS (double
 //                    buffered, padded rows so 16-byte fragment reads are bank-conflict free),
 //                    16x16x32 bf16 MFMA, XCD-aware grouped tile order. Optional split-K.
@@ -14,6 +15,8 @@
 //                    four 32-wide K steps in flight), and the waves' partial tiles are summed
 //                    through LDS in a fixed order. No cross-workgroup synchronisation, no float
 //                    atomics: the result is deterministic.
+//   * gemm_rows   -- one or two rows of A: each load of a wave reads 1 KB (or 256 B) runs of
+//                    single weight rows, dot products on the VALU with x staged in LDS.
 //   Split-K of the tile kernel (few tiles, small M) writes fp32 partials and a separate
 //   reduction kernel sums them in a fixed order.
 #include <algorithm>
@@ -282,20 +285,173 @@ __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// M <= 2: whole weight-row segments per load, dot products on the VALU
+// ------------------------------------------------------------------------------------------
+// With one or two activation rows the product is a pure weight stream, and the MFMA fragment
+// layout (16 rows x 64 bytes per load) is not the best way to read it. Here one load of a wave
+// covers RPI weight rows with 64/RPI lanes each, so a row segment is 1 KB (RPI = 1, K a multiple
+// of 512) or 256 B (RPI = 4); x (this workgroup's K range) sits in LDS. Each wave owns `rw`
+// groups of RPI rows, streams their segments in two sets of U loads, and sums a row over its lanes
+// once its K range is done. The K range may be split over gridDim.y workgroups (EPI_F32 only:
+// split y writes its partial sums to C + y * c_split_stride). Sums run in a fixed order.
+MLA_DEV float dot8_bf16(const u32x4_t& w, const u32x4_t& x, float acc) {
+  // whole-vector shuffles: element-wise bit casts of u32x4 lanes were miscompiled (every
+  // element read as the first)
+  const bf16x8_t a = as_bf16x8(w), b = as_bf16x8(x);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+
+constexpr int ROWS_LDS_MAX = 32768;  // bytes of x a rows workgroup stages
+
+// Raw (stride 0) buffer descriptor over `bytes` bytes: a load at an offset past the end returns
+// zero without touching memory, which lets a wave issue a fixed number of loads whatever its
+// share of the rows. Third descriptor word: 32-bit data format, as the gfx9 family requires.
+MLA_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+MLA_DEV u32x4_t buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+template <int RPI, int MT, int U, int TAG>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw) {
+  constexpr int LPR = 64 / RPI;     // lanes per row
+  constexpr int SEG = LPR * 8;      // K elements of a row segment
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / LPR, j = lane % LPR;
+  const int batch = blockIdx.z;
+  const int ks = p.K / (int)gridDim.y, k0 = blockIdx.y * ks;
+  // operand windows of this batch (the plan keeps both under 2 GiB)
+  const uint32_t a_bytes = (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+  const uint32_t b_bytes = (uint32_t)(((int64_t)(p.N - 1) * p.ldb + p.K) * 2);
+  const __amdgpu_buffer_rsrc_t ra_src = buffer_rsrc((const uint16_t*)p.A + batch * p.sA, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb_src = buffer_rsrc((const uint16_t*)p.B + batch * p.sB, b_bytes);
+  const int nseg = ks / SEG;
+  const int row0 = (blockIdx.x * 4 + wave) * rw * RPI;
+  const int total = rw * nseg;  // loads of this wave
+  // next load (lg = row group, ls = segment). The pipeline below issues whole register sets;
+  // loads past the wave's last one point past the buffer end (zeros, no memory access) and
+  // their products are never stored. Selects, not branches, between the loads.
+  int lg = 0, ls = 0, issued = 0;
+  auto next = [&]() -> u32x4_t {
+    const bool live = issued < total;
+    const int row = min(row0 + lg * RPI + r, p.N - 1);
+    const uint32_t off = live ? (uint32_t)(row * p.ldb + k0 + ls * SEG + j * 8) * 2u : b_bytes;
+    ++issued;
+    const bool wrap = ls + 1 == nseg;
+    lg = live && wrap ? lg + 1 : lg;
+    ls = live ? (wrap ? 0 : ls + 1) : ls;
+    return buffer_ld16(rb_src, off);
+  };
+  // two register sets of U loads: one is multiplied while the other is in flight
+  u32x4_t ra[U], rb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) ra[u] = next();
+  // x into LDS behind the first weight loads: every thread issues all of its (at most
+  // ROWS_LDS_MAX / 16 / 256) 16-byte loads before the first store
+  {
+    constexpr int XC = ROWS_LDS_MAX / 16 / 256;
+    const int cpr = ks / 8, nc = MT * cpr;
+    u32x4_t xv[XC];
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      const int m = c / cpr, cc = c - m * cpr;
+      xv[i] = buffer_ld16(ra_src, c < nc ? (uint32_t)(m * p.lda + k0 + cc * 8) * 2u : a_bytes);
+    }
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      if (c < nc) st16(xs + c * 8, xv[i]);
+    }
+  }
+  __syncthreads();
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+  int cg = 0, cs = 0;  // row group and segment being multiplied
+  auto consume = [&](const u32x4_t (&rr)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = dot8_bf16(rr[u], ld16(xs + m * ks + cs * SEG + j * 8), acc[m]);
+      if (++cs == nseg) {  // row group done: sum each row over its lanes
+        const int n = row0 + cg * RPI + r;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float v = acc[m];
+#pragma unroll
+          for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+          acc[m] = 0.f;
+          if (j == 0 && cg < rw && n < p.N && m < p.M) {
+            if (gridDim.y > 1)
+              ((float*)p.C)[blockIdx.y * p.c_split_stride + batch * p.sC + (int64_t)m * p.ldc + n] = v;
+            else
+              epi_store(p, batch, m, n, v);
+          }
+        }
+        cs = 0;
+        ++cg;
+      }
+    }
+  };
+  for (int it = 0; it < total; it += 2 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) rb[u] = next();
+    consume(ra);
+#pragma unroll
+    for (int u = 0; u < U; ++u) ra[u] = next();
+    consume(rb);
+  }
+}
+
 constexpr int TARGET_WGS = 512;  // two workgroups per CU on 256 CUs
 
 struct Plan {
-  int kind;  // 0 wsplit, 1 tile128, 2 tile256
+  int kind;  // 0 wsplit, 1 tile128, 2 tile256, 3 rows
   int mt, kw, ysplit;
+  int rpi, rw, u;  // rows kernel: rows per load, row groups per wave, loads per register set
   int splits, ksplit;
   int tiles;  // workgroups per (split, batch)
 };
 
-Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1) {
+Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok = true) {
   Plan pl{};
   pl.splits = 1;
   pl.ksplit = K;
   pl.ysplit = 1;
+  // One or two rows of a single product: weight-row streaming on the VALU. Measured on MI355X:
+  // ~1-2 thousand workgroups, at least four loads per wave (six when K is split over
+  // workgroups), two register sets of 4 loads when a wave has 16 or more, else of 2 (more in
+  // flight per wave was slower). The per-head batched products stay on the MFMA kernel.
+  if (M <= 2 && batch == 1 && rows_ok) {
+    pl.kind = 3;
+    pl.mt = M;
+    pl.rpi = K % 512 == 0 ? 1 : 4;
+    const int nseg = K / (pl.rpi == 1 ? 512 : 128);
+    auto wgs = [&]() { return (int64_t)cdiv(N, 4 * pl.rw * pl.rpi) * batch * pl.ysplit; };
+    pl.rw = 1;
+    while ((pl.rw * nseg < 4 || wgs() > 2048) && 4 * pl.rw * pl.rpi < N) pl.rw *= 2;
+    while (pl.ysplit * 2 <= ysplit_max && wgs() < 1024 && nseg % (pl.ysplit * 2) == 0 &&
+           pl.rw * nseg / (pl.ysplit * 2) >= 6)
+      pl.ysplit *= 2;
+    while ((int64_t)M * (K / pl.ysplit) * 2 > ROWS_LDS_MAX && pl.ysplit * 2 <= ysplit_max && nseg % (pl.ysplit * 2) == 0)
+      pl.ysplit *= 2;
+    pl.tiles = cdiv(N, 4 * pl.rw * pl.rpi);
+    pl.u = pl.rw * nseg / pl.ysplit >= 16 ? 4 : 2;
+    if ((int64_t)M * (K / pl.ysplit) * 2 <= ROWS_LDS_MAX) return pl;
+    pl = Plan{};
+    pl.splits = 1;
+    pl.ksplit = K;
+    pl.ysplit = 1;
+  }
   // Streaming kernel for decode-sized M: always up to 16 rows; up to 64 rows when K is short
   // (kv_b, W_UK / W_UV), where a staged tile would spend most of its time filling LDS.
   if (M <= 16 || (M <= 64 && K <= 512)) {
@@ -344,8 +500,26 @@ void launch_wsplit(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   }
 }
 
+template <int RPI, int U, int TAG>
+void launch_rows(const GemmArgs& a, const Plan& pl, dim3 grid, size_t lds, hipStream_t s) {
+  if (pl.mt == 1) hipLaunchKernelGGL((gemm_rows_kernel<RPI, 1, U, TAG>), grid, dim3(256), lds, s, a, pl.rw);
+  else hipLaunchKernelGGL((gemm_rows_kernel<RPI, 2, U, TAG>), grid, dim3(256), lds, s, a, pl.rw);
+}
+
 template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+  if (pl.kind == 3) {
+    dim3 grid(pl.tiles, pl.ysplit, a.batch);
+    const size_t lds = (size_t)pl.mt * (a.K / pl.ysplit) * 2;
+    if (pl.rpi == 1) {
+      if (pl.u == 4) launch_rows<1, 4, TAG>(a, pl, grid, lds, s);
+      else launch_rows<1, 2, TAG>(a, pl, grid, lds, s);
+    } else {
+      if (pl.u == 4) launch_rows<4, 4, TAG>(a, pl, grid, lds, s);
+      else launch_rows<4, 2, TAG>(a, pl, grid, lds, s);
+    }
+    return;
+  }
   if (pl.kind == 0) {
     if (pl.mt == 1) launch_wsplit<1, TAG>(a, pl, s);
     else if (pl.mt == 2) launch_wsplit<2, TAG>(a, pl, s);
@@ -372,14 +546,20 @@ int64_t gemm_part_floats(int M, int N, int K, int batch) {
 
 int gemm_counters(int, int, int, int) { return 0; }
 
+// The rows kernel addresses each operand through a buffer descriptor: windows under 2 GiB.
+bool rows_ok(const GemmArgs& a) {
+  constexpr int64_t LIM = (int64_t)1 << 31;
+  return ((int64_t)(a.M - 1) * a.lda + a.K) * 2 < LIM && ((int64_t)(a.N - 1) * a.ldb + a.K) * 2 < LIM;
+}
+
 int gemm_ysplit(const GemmArgs& a) {
-  return plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1).ysplit;
+  return plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, rows_ok(a)).ysplit;
 }
 
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 128 != 0) return hipErrorInvalidValue;
-  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1);
+  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, rows_ok(a));
   if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
   switch (a.tag) {
     case TAG_QKVA: launch_tagged<TAG_QKVA>(a, pl, s); break;

@@ -20,7 +20,8 @@ def bf16_rand(shape, seed, std=1.0):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 2112, 7168), (1, 7168, 8192), (3, 12288, 1536), (16, 7168, 8192), (17, 2112, 7168),
+    (1, 2112, 7168), (1, 7168, 8192), (2, 7168, 8192), (1, 12288, 1536), (2, 2112, 7168),
+    (1, 1100, 1536), (2, 1100, 640), (1, 20, 128), (3, 12288, 1536), (16, 7168, 8192), (17, 2112, 7168),
     (33, 16384, 512), (64, 7168, 8192), (65, 2112, 7168), (100, 12288, 1536), (128, 7168, 8192),
     (300, 16384, 512), (1000, 2112, 7168), (1024, 1100, 1536), (2048, 7168, 8192),
 ])
@@ -43,12 +44,13 @@ def test_gemm_matches_float64(M, N, K):
     assert err.max() <= 2e-5 * scale * 8
 
 
-def test_gemm_bf16_output_and_batched_strides():
+@pytest.mark.parametrize("Bt", [1, 2, 5])
+def test_gemm_bf16_output_and_batched_strides(Bt):
     """Per-head batched product with row/batch strides (the decode absorption layout)."""
     import torch
 
-    log("batched gemm")
-    Bt, H = 5, 64
+    log(f"batched gemm Bt={Bt}")
+    H = 64
     q = bf16_rand((Bt, H * 192), 11)
     w = bf16_rand((H, 512, 128), 12, std=0.05)
     Q, W = binding.bf16_tensor(q), binding.bf16_tensor(w)
@@ -61,6 +63,28 @@ def test_gemm_bf16_output_and_batched_strides():
     ref = np.einsum("bhd,hcd->bhc", q64, synth.bf16_bits_to_f64(w))
     err = np.abs(got - ref)
     assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-6
+
+
+@pytest.mark.parametrize("Bt", [1, 2])
+def test_gemm_value_mix_layout(Bt):
+    """Per-head W_UV product: o[b][h*128 + d] = sum_c o_lat[b][h][c] W_UV,h[d][c] (K = 512)."""
+    import torch
+
+    log(f"value-mix gemm Bt={Bt}")
+    H = 64
+    ol = bf16_rand((Bt, H * 512), 21)
+    w = bf16_rand((H, 256, 512), 22, std=0.05)  # per head [128 key rows | 128 value rows]
+    OL, W = binding.bf16_tensor(ol), binding.bf16_tensor(w)
+    out = torch.empty((Bt, H * 128), dtype=torch.float32, device="cuda")
+    binding.Gemm()(OL, W[:, 128:, :], out, Bt, 128, 512, batch=H, lda=H * 512, sA=512, ldb=512, sB=256 * 512,
+                   ldc=H * 128, sC=128, stage="uv")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = np.einsum("bhc,hdc->bhd", synth.bf16_bits_to_f64(ol).reshape(Bt, H, 512),
+                    synth.bf16_bits_to_f64(w)[:, 128:, :]).reshape(Bt, H * 128)
+    err = np.abs(got - ref)
+    log(f"  max err {err.max():.3e}")
+    assert err.max() <= 2e-5 * np.abs(ref).max()
 
 
 def test_gemm_rejects_bad_shapes():
