@@ -445,8 +445,15 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   const int l32 = lane & 31, kg = lane >> 5;
   const int head = hg * 32 + l32;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sC[(DKB + 1) * LDC2];  // + a scratch row
-  __shared__ __attribute__((aligned(16))) float xS[8][16][64];
+  // LDS: cache block (+ a scratch row) and the partial-score exchange; after the block loop the
+  // same bytes stage the output rows
+  constexpr int SC_BYTES = (DKB + 1) * LDC2 * 2;
+  constexpr int XS_BYTES = 8 * 16 * 64 * 4;
+  constexpr int ST_LD = 256 + 4;  // staged half row: 256 floats + 16 bytes
+  static_assert(SC_BYTES % 16 == 0 && 64 * ST_LD * 4 <= SC_BYTES + XS_BYTES, "LDS carve-up");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SC_BYTES + XS_BYTES];
+  uint16_t* sC = reinterpret_cast<uint16_t*>(smem);
+  float (*xS)[16][64] = reinterpret_cast<float (*)[16][64]>(smem + SC_BYTES);
 
   // staging: 32 rows x 72 chunks of 16 bytes; thread takes chunks c = tid + 512 i (i < 5, c < 2304).
   // Every load is issued unconditionally (an index past the block re-reads its last chunk and is
@@ -586,16 +593,34 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
 
   // ---- split outputs: unnormalised o (relative to m_used), m_used and the sum per head
   l_run += __shfl_xor(l_run, 32);
-  const int64_t pidx = ((int64_t)b * a.max_splits + split) * 64 + head;
-  float* po = a.part_o + pidx * KV_LORA + 128 * fq + 4 * kg;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4_t*>(po + 32 * t + 8 * q) = f32x4_t{o[t][4 * q], o[t][4 * q + 1], o[t][4 * q + 2], o[t][4 * q + 3]};
+  const int64_t prow = ((int64_t)b * a.max_splits + split) * 64;  // head 0 of this split
   if (fq == 0 && kg == 0) {
-    a.part_ml[pidx * 2] = m_used;
-    a.part_ml[pidx * 2 + 1] = l_run;
+    a.part_ml[(prow + head) * 2] = m_used;
+    a.part_ml[(prow + head) * 2 + 1] = l_run;
+  }
+  // The accumulators hold 32-byte runs of 32 different head rows; written straight out, every
+  // store would touch 32 rows. Instead each half of the 512 features goes through LDS (the four
+  // waves that own it write [head][256] rows), and every wave then stores whole 1 KB half rows.
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // LDS free: block loop done / previous half stored
+    if ((fq >> 1) == half) {
+      float* dst = st + head * ST_LD + 128 * (fq & 1) + 4 * kg;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + 32 * t + 8 * q) =
+              f32x4_t{o[t][4 * q], o[t][4 * q + 1], o[t][4 * q + 2], o[t][4 * q + 3]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // wave w: heads 8w .. 8w+7, lane = 16-byte piece of the half row
+      const int hh = wave * 8 + i;
+      *reinterpret_cast<f32x4_t*>(a.part_o + (prow + hh) * KV_LORA + 256 * half + 4 * lane) =
+          *reinterpret_cast<const f32x4_t*>(st + hh * ST_LD + 4 * lane);
+    }
   }
 }
 
