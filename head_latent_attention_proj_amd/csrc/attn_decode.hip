@@ -705,6 +705,112 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   }
 }
 
+// Merge of the splits followed by the value up-projection, bf16 weights, small batches (one
+// launch instead of two; the W_UV rows are in flight while the partial outputs are merged).
+// Workgroup = (head h, half of its 128 value rows, sequence b); both halves merge the head:
+//   o_lat = sum_s exp(m_s - m) o_s / sum_s exp(m_s - m) l_s      (float32, in LDS)
+//   o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[c]                 (float32 sums, bf16 out)
+// Wave w owns 8 rows of W_UV,h, one whole 1 KB row per load (lane = 8 features); the merge is
+// split over the 8 waves by split index (8 features per thread) and combined through LDS in a
+// fixed order. A wave's 8 row sums are reduced over its lanes by recursive halving (each step
+// hands half of the rows to the partner lane), 10 lane exchanges instead of 48.
+__global__ __launch_bounds__(512) void decode_merge_uv_kernel(DecodeAttnArgs a) {
+  using namespace mla_dims;
+  const int h = blockIdx.x >> 1, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int f = lane * 8;
+  const int row0 = 64 * (blockIdx.x & 1) + 8 * wave;  // first value row of this wave
+  __shared__ __attribute__((aligned(16))) float so[8][KV_LORA];
+  __shared__ float sm[8], sl[8];
+
+  u32x4_t wv[8];
+  const uint16_t* wr = a.w_uv + h * a.uv_head_stride + (int64_t)row0 * KV_LORA + f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wv[i] = ld16(wr + i * KV_LORA);
+
+  const int ns = cdiv(a.len[a.seq_ids[b]], a.chunk);
+  const int64_t base = (int64_t)b * a.max_splits * 64 + h;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  for (int s0 = wave; s0 < ns; s0 += 16) {
+    f32x2_t ml[2];
+    f32x4_t v0[2], v1[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sp = min(s0 + 8 * u, ns - 1);  // past the end: re-read (not used)
+      const int64_t p = base + (int64_t)sp * 64;
+      ml[u] = *reinterpret_cast<const f32x2_t*>(a.part_ml + p * 2);
+      v0[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f);
+      v1[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (s0 + 8 * u >= ns) break;
+      const float mn = fmaxf(m, ml[u][0]);
+      const float al = exp2f(m - mn), be = exp2f(ml[u][0] - mn);
+      l = l * al + ml[u][1] * be;
+      o0 = o0 * al + v0[u] * be;
+      o1 = o1 * al + v1[u] * be;
+      m = mn;
+    }
+  }
+  *reinterpret_cast<f32x4_t*>(&so[wave][f]) = o0;
+  *reinterpret_cast<f32x4_t*>(&so[wave][f + 4]) = o1;
+  if (lane == 0) {
+    sm[wave] = m;
+    sl[wave] = l;
+  }
+  __syncthreads();
+  float M = sm[0];
+#pragma unroll
+  for (int g = 1; g < 8; ++g) M = fmaxf(M, sm[g]);
+  float wg[8], L = 0.f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    wg[g] = sl[g] > 0.f ? exp2f(sm[g] - M) : 0.f;  // a group with no split has l = 0, m = -inf
+    L += wg[g] * sl[g];
+  }
+  const float inv = 1.0f / L;
+  f32x4_t q0 = {0.f, 0.f, 0.f, 0.f}, q1 = q0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    q0 += wg[g] * *reinterpret_cast<const f32x4_t*>(&so[g][f]);
+    q1 += wg[g] * *reinterpret_cast<const f32x4_t*>(&so[g][f + 4]);
+  }
+  const float ol[8] = {q0[0] * inv, q0[1] * inv, q0[2] * inv, q0[3] * inv,
+                       q1[0] * inv, q1[1] * inv, q1[2] * inv, q1[3] * inv};
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc += bf_lo(wv[i][j]) * ol[2 * j];
+      acc += bf_hi(wv[i][j]) * ol[2 * j + 1];
+    }
+    r[i] = acc;
+  }
+  // recursive halving: after the steps over lane bits 5, 4, 3 lane keeps row (lane >> 3) & 7
+  // summed over 8 lanes; bits 2, 1, 0 finish the sum
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int n = 4 >> k;  // rows kept after this step
+    const bool up = (lane >> (5 - k)) & 1;
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const float give = up ? r[j] : r[j + n];
+      const float keep = up ? r[j + n] : r[j];
+      r[j] = keep + __shfl_xor(give, 32 >> k);
+    }
+  }
+  float v = r[0];
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  if ((lane & 7) == 0) a.o[(int64_t)b * (HEADS * VD) + h * VD + row0 + (lane >> 3)] = f2bf(v);
+}
+
 }  // namespace
 
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
@@ -719,7 +825,12 @@ hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(decode_attn_bf16_kernel, g1, dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel<false>, g2, dim3(256), 0, s, a);
+    if (a.w_uv) {
+      if (a.B > MERGE_UV_MAX_B) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(decode_merge_uv_kernel, dim3(128, a.B), dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(decode_merge_kernel<false>, g2, dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

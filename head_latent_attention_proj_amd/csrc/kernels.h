@@ -166,8 +166,15 @@ struct DecodeAttnArgs {
   float* part_ml;          // [B][max_splits][64][2] (running max, sum)
   const float* w_uv_s;     // FP8: kv_b block scales [128][4] (W_UV,h blocks are rows 2h+1)
   uint16_t* o_lat;         // merged latent output, bf16 [B][64][512] (FP8: high parts, then residuals)
+  // bf16 weights, B <= MERGE_UV_MAX_B: when w_uv is set the merge also applies W_UV and writes
+  // o = [B][64 * 128] bf16 (o_lat is then not written)
+  const uint16_t* w_uv;    // W_UV,h = rows [128][512] at w_uv + h * uv_head_stride
+  int64_t uv_head_stride;
+  uint16_t* o;
 };
-// Split attention + merge. Output: o_lat (see DecodeAttnArgs); W_UV is applied by the caller.
+constexpr int MERGE_UV_MAX_B = 4;
+// Split attention + merge. Output: o_lat (see DecodeAttnArgs), W_UV applied by the caller; or,
+// with w_uv set, o.
 hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s);
 
 // FP8 activation quantiser for a bf16/fp32 matrix [rows, K] (K multiple of 128).

@@ -639,20 +639,26 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   da.seq_ids = seq_ids_d; da.offset = cache->offset_d; da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
   da.max_splits = dp.max_splits; da.scale = ctx->scale; da.part_o = (float*)(w + L.part_o);
   da.part_ml = (float*)(w + L.part_ml); da.w_uv_s = ctx->s_kvb; da.o_lat = (uint16_t*)(w + L.o_lat);
+  const bool fuse_uv = !fp8 && B <= mla_k::MERGE_UV_MAX_B;  // merge and W_UV in one kernel
+  if (fuse_uv) {
+    da.w_uv = (const uint16_t*)ctx->w_uv; da.uv_head_stride = ctx->uv_head_stride; da.o = (uint16_t*)(w + L.o);
+  }
   HIP_TRY(mla_k::decode_attention(da, s));
   // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (already
   //    scaled by the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the
   //    exact code values, two float32 products that the quantiser adds.
-  g = gemm_common(w, L);
-  g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
-  g.B = ctx->w_uv; g.ldb = KV_LORA; g.sB = ctx->uv_head_stride;
-  g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.ldc = O_IN; g.sC = VD; g.tag = mla_k::TAG_UV;
-  if (fp8) {
-    g.M = 2 * B; g.C = w + L.o32; g.epi = mla_k::EPI_F32;
-  } else {
-    g.M = B; g.C = w + L.o; g.epi = mla_k::EPI_BF16;
+  if (!fuse_uv) {
+    g = gemm_common(w, L);
+    g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
+    g.B = ctx->w_uv; g.ldb = KV_LORA; g.sB = ctx->uv_head_stride;
+    g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.ldc = O_IN; g.sC = VD; g.tag = mla_k::TAG_UV;
+    if (fp8) {
+      g.M = 2 * B; g.C = w + L.o32; g.epi = mla_k::EPI_F32;
+    } else {
+      g.M = B; g.C = w + L.o; g.epi = mla_k::EPI_BF16;
+    }
+    HIP_TRY(mla_k::gemm_bf16(g, s));
   }
-  HIP_TRY(mla_k::gemm_bf16(g, s));
   // 7. o_proj
   if (fp8)
     HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), (const float*)(w + L.o32) + (int64_t)B * O_IN, O_IN,
