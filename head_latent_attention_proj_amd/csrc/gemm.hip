@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "norm_dev.h"
 
 namespace mla_k {
 
@@ -318,8 +319,12 @@ MLA_DEV u32x4_t buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
-template <int RPI, int MT, int U, int TAG>
-__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw) {
+// QNORM (the q_b projection at decode, bf16): x is not read from A but built here as the query
+// latent RMSNorm of the fused q_a | kv_a sums (na.cqkv), the same in every workgroup; workgroup
+// (0, 0) also writes the tokens' cache entries (latent RMSNorm, rotated shared key) and
+// advances their lengths. This replaces the norm kernel between q_a | kv_a and q_b.
+template <int RPI, int MT, int U, int TAG, bool QNORM>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, NormArgs na) {
   constexpr int LPR = 64 / RPI;     // lanes per row
   constexpr int SEG = LPR * 8;      // K elements of a row segment
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
@@ -356,7 +361,11 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw) {
   for (int u = 0; u < U; ++u) ra[u] = next();
   // x into LDS behind the first weight loads: every thread issues all of its (at most
   // ROWS_LDS_MAX / 16 / 256) 16-byte loads before the first store
-  {
+  __shared__ float red[4];
+  if constexpr (QNORM) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) q_norm_bf16(na, min(m, p.M - 1), xs + m * ks, red);
+  } else {
     constexpr int XC = ROWS_LDS_MAX / 16 / 256;
     const int cpr = ks / 8, nc = MT * cpr;
     u32x4_t xv[XC];
@@ -409,6 +418,12 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) ra[u] = next();
     consume(rb);
+  }
+  if constexpr (QNORM) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      __shared__ float kraw[mla_dims::ROPE];
+      for (int t = 0; t < na.n_tokens; ++t) kv_norm_rope_append_bf16(na, t, red, kraw);
+    }
   }
 }
 
@@ -502,8 +517,9 @@ void launch_wsplit(const GemmArgs& a, const Plan& pl, hipStream_t s) {
 
 template <int RPI, int U, int TAG>
 void launch_rows(const GemmArgs& a, const Plan& pl, dim3 grid, size_t lds, hipStream_t s) {
-  if (pl.mt == 1) hipLaunchKernelGGL((gemm_rows_kernel<RPI, 1, U, TAG>), grid, dim3(256), lds, s, a, pl.rw);
-  else hipLaunchKernelGGL((gemm_rows_kernel<RPI, 2, U, TAG>), grid, dim3(256), lds, s, a, pl.rw);
+  const NormArgs none{};
+  if (pl.mt == 1) hipLaunchKernelGGL((gemm_rows_kernel<RPI, 1, U, TAG, false>), grid, dim3(256), lds, s, a, pl.rw, none);
+  else hipLaunchKernelGGL((gemm_rows_kernel<RPI, 2, U, TAG, false>), grid, dim3(256), lds, s, a, pl.rw, none);
 }
 
 template <int TAG>
@@ -554,6 +570,26 @@ bool rows_ok(const GemmArgs& a) {
 
 int gemm_ysplit(const GemmArgs& a) {
   return plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, rows_ok(a)).ysplit;
+}
+
+bool gemm_bf16_fuses_qnorm(const GemmArgs& a) {
+  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, 1, rows_ok(a));
+  return pl.kind == 3 && pl.ysplit == 1 && pl.rpi == 1 && a.K == mla_dims::Q_LORA && a.batch == 1;
+}
+
+hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s) {
+  if (!gemm_bf16_fuses_qnorm(a) || na.n_tokens != a.M || na.meta || na.fp8) return hipErrorInvalidValue;
+  const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, 1, rows_ok(a));
+  dim3 grid(pl.tiles, 1, 1);
+  const size_t lds = (size_t)pl.mt * a.K * 2;
+  if (pl.u == 4) {
+    if (pl.mt == 1) hipLaunchKernelGGL((gemm_rows_kernel<1, 1, 4, TAG_QB, true>), grid, dim3(256), lds, s, a, pl.rw, na);
+    else hipLaunchKernelGGL((gemm_rows_kernel<1, 2, 4, TAG_QB, true>), grid, dim3(256), lds, s, a, pl.rw, na);
+  } else {
+    if (pl.mt == 1) hipLaunchKernelGGL((gemm_rows_kernel<1, 1, 2, TAG_QB, true>), grid, dim3(256), lds, s, a, pl.rw, na);
+    else hipLaunchKernelGGL((gemm_rows_kernel<1, 2, 2, TAG_QB, true>), grid, dim3(256), lds, s, a, pl.rw, na);
+  }
+  return hipGetLastError();
 }
 
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {

@@ -112,6 +112,12 @@ struct NormArgs {
 };
 hipError_t norm_rope_append(const NormArgs& a, hipStream_t s);
 
+// Decode q_b with the norms folded in (bf16 weights, the row-streaming plan): a.A is ignored,
+// x = q_hat is built from na.cqkv in every workgroup, and the cache entries are written as
+// norm_rope_append would. gemm_bf16_fuses_qnorm() tells whether the shape takes this path.
+bool gemm_bf16_fuses_qnorm(const GemmArgs& a);
+hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s);
+
 // Byte copy of n ready-made entries to dst (the slot of position len[seq]); len[seq] += n.
 hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_bytes, int n, int seq, int32_t* len_d,
                                 hipStream_t s);

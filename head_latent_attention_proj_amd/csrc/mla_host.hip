@@ -606,14 +606,19 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = B; na.meta = nullptr;
   na.seq_ids = seq_ids_d; na.offset = cache->offset_d; na.len = cache->len_d;
   na.q_hat_codes = w + L.q_hat; na.q_hat_scales = (float*)(w + L.qh8s);
-  HIP_TRY(mla_k::norm_rope_append(na, s));
-  // 3. q_b
+  // 3. q_b. bf16 weights at one or two tokens: the norms of step 2 run inside the q_b kernel
+  //    (one launch less on a latency-bound path); otherwise a norm kernel first.
   g = gemm_common(w, L);
   set_a(ctx, g, w + L.q_hat, Q_LORA, w + L.q_hat, (const float*)(w + L.qh8s), Q_LORA / 128);
   g.B = ctx->w_qb; g.ldb = Q_LORA; g.b_scale = ctx->s_qb; g.bs_ld = Q_LORA / 128;
   g.C = w + L.q; g.ldc = QB_N; g.M = B; g.N = QB_N; g.K = Q_LORA; g.tag = mla_k::TAG_QB;
   g.epi = fp8 ? mla_k::EPI_F32 : mla_k::EPI_BF16;
-  HIP_TRY(run_proj(ctx, g, s));
+  if (!fp8 && mla_k::gemm_bf16_fuses_qnorm(g)) {
+    HIP_TRY(mla_k::gemm_bf16_qnorm(g, na, s));
+  } else {
+    HIP_TRY(mla_k::norm_rope_append(na, s));
+    HIP_TRY(run_proj(ctx, g, s));
+  }
   // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched). FP8: W_UK as its exact code
   //    values with the block scale of (head, latent block) on the output; q_nope is float32 and
   //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out, and

@@ -12,6 +12,7 @@
 // input of kv_b, so it is what the keys and values are rebuilt from).
 #include "common.h"
 #include "kernels.h"
+#include "norm_dev.h"
 
 namespace mla_k {
 
@@ -30,17 +31,6 @@ MLA_DEV uint32_t e4m3_rne_sat(float q) {
   const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
   const uint32_t e = (r >> 3) - 127u + 7u;
   return sign | (e << 3) | (r & 7u);
-}
-
-// Block-wide sum over 256 threads (4 waves).
-MLA_DEV float block_sum256(float v, float* red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const float s = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return s;
 }
 
 __global__ void plan_kernel(const int32_t* seq_ids, const int32_t* q_start, const int64_t* offset,
