@@ -448,12 +448,14 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   // LDS: cache block (+ a scratch row) and the partial-score exchange; after the block loop the
   // same bytes stage the output rows
   constexpr int SC_BYTES = (DKB + 1) * LDC2 * 2;
-  constexpr int XS_BYTES = 8 * 16 * 64 * 4;
+  constexpr int XSL = 20;  // floats per lane in the score exchange: 16 + 4 (80-byte rows: the
+                           // eight lanes of one 128-byte LDS cycle hit distinct banks)
+  constexpr int XS_BYTES = 8 * 64 * XSL * 4;
   constexpr int ST_LD = 256 + 4;  // staged half row: 256 floats + 16 bytes
   static_assert(SC_BYTES % 16 == 0 && 64 * ST_LD * 4 <= SC_BYTES + XS_BYTES, "LDS carve-up");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SC_BYTES + XS_BYTES];
   uint16_t* sC = reinterpret_cast<uint16_t*>(smem);
-  float (*xS)[16][64] = reinterpret_cast<float (*)[16][64]>(smem + SC_BYTES);
+  float* xS = reinterpret_cast<float*>(smem + SC_BYTES);  // [wave][lane][XSL]
 
   // staging: 32 rows x 72 chunks of 16 bytes; thread takes chunks c = tid + 512 i (i < 5, c < 2304).
   // Every load is issued unconditionally (an index past the block re-reads its last chunk and is
@@ -537,14 +539,26 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
       }
     }
     const f32x16_t sacc = s0 + s1;
+    {
+      float* xw = xS + (wave * 64 + lane) * XSL;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) xS[wave][e][lane] = sacc[e];
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(xw + 4 * q) = f32x4_t{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    }
     __syncthreads();
+    // the four partial score sets of this head group, added in quarter order
+    f32x4_t xs4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xs4[q] = *reinterpret_cast<const f32x4_t*>(xS + (hg * 64 + lane) * XSL + 4 * q);
+#pragma unroll
+    for (int f = 1; f < 4; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs4[q] += *reinterpret_cast<const f32x4_t*>(xS + ((hg + 2 * f) * 64 + lane) * XSL + 4 * q);
     float sv[16];
     float bmax = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float v = ((xS[hg][e][lane] + xS[hg + 2][e][lane]) + xS[hg + 4][e][lane]) + xS[hg + 6][e][lane];
+      float v = xs4[e >> 2][e & 3];
       v *= sl2;
       if (kb + 8 * (e >> 2) + 4 * kg + (e & 3) >= c1) v = -INFINITY;
       sv[e] = v;
