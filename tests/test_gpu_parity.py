@@ -120,6 +120,35 @@ def test_decode_varlen_batch(torch_cuda):
     assert list(cache.len_d.cpu().numpy()) == [n + 1 for n in lens]
 
 
+@pytest.mark.parametrize("lens", [[700, 0], [64, 1, 1500], [33, 2000, 65, 129]])
+def test_decode_small_batch(torch_cuda, lens):
+    """Decode of two to four sequences: the launch sequences where the norms run inside the q_b
+    kernel (one or two tokens) and W_UV inside the merge (up to four); the new cache entries too."""
+    B = len(lens)
+    log(f"decode small batch lens={lens}")
+    L = layer()
+    _, w64 = weights()
+    cache = binding.Cache(L, [n + 1 for n in lens])
+    ents = {}
+    for s, n in enumerate(lens):
+        if n:
+            ents[s] = synth.make_cache_entries(n, seed=3100 + s)
+            L.cache_append(cache, s, binding.bf16_tensor(ents[s]))
+    order = np.arange(B, dtype=np.int32)[::-1].copy()  # batch rows in reverse sequence order
+    xn = synth.make_hidden(B, seed=1013 + B)
+    y = y_of(L.decode(cache, order, binding.bf16_tensor(xn)))
+    torch_cuda.cuda.synchronize()
+    for b, s in enumerate(order):
+        e = synth.bf16_bits_to_f64(ents[s]) if lens[s] else np.zeros((0, 576))
+        ref = omla.forward(synth.bf16_bits_to_f64(xn[b:b + 1]), w64, cache=(e[:, :512], e[:, 512:]))
+        assert_close(y[b:b + 1], ref["y"], f"seq {s} (L={lens[s]})")
+        c_gpu, k_gpu = entries_f64(cache.slots(s).cpu().numpy()[lens[s]:lens[s] + 1])
+        assert_close(c_gpu, ref["c_hat"], f"seq {s} new c_hat")
+        assert_close(k_gpu, ref["k_pe"], f"seq {s} new k_pe")
+    assert list(cache.len_h) == [n + 1 for n in lens]
+    assert list(cache.len_d.cpu().numpy()) == [n + 1 for n in lens]
+
+
 def test_prefill_then_decode_steps(torch_cuda):
     """prefill(T) followed by decode steps equals the oracle's prefill over all tokens."""
     log("prefill 33 + 3 decode steps")
