@@ -24,6 +24,8 @@
 // block's loads are in flight (in registers) while a block is used. Each split writes (max, sum,
 // unnormalised o) per head; the merge kernel combines the splits and normalises; W_UV is applied
 // afterwards as a batched bf16 MFMA product (one 128 x 512 matrix per head).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];
   __shared__ __attribute__((aligned(16))) uint16_t sT[KV_LORA * LDT];
   __shared__ __attribute__((aligned(16))) float xS[8][8][64];   // partial scores per wave
-  __shared__ __attribute__((aligned(16))) float sScale[DKB][4];  // FP8 group scales per position
+  __shared__ __attribute__((aligned(16))) float sScale[4][DKB];  // FP8 group scales [group][position]
   // FP8: low bf16 halves of the float32 rotary key (high halves sit in sC)
   __shared__ __attribute__((aligned(16))) uint16_t sKlo[FP8 ? DKB * 72 : 8];
 
@@ -138,7 +140,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
         put_pair(kp, cc * 16 + hlf * 8, u32x4_t{x01[0], x01[1], x23[0], x23[1]},
                  u32x4_t{y01[0], y01[1], y23[0], y23[1]});
       }
-      if (tid >= 256 && tid < 256 + DKB) *reinterpret_cast<u32x4_t*>(&sScale[tid - 256][0]) = rs;
+      if (tid >= 256 && tid < 256 + DKB) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[q]);
+      }
       // rotary key: 4 float32 features -> bf16 high halves (sC) and low halves (sKlo)
       const int pos = tid >> 4, f4 = (tid & 15) * 4;
       float v[4], r[4];
@@ -244,39 +249,59 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     {
       const uint16_t* r0 = sC + l16 * LDC + lh * HALF + g * 8;
       const uint16_t* r1 = r0 + 16 * LDC;
-      if constexpr (FP8) {  // fragments read as used: the hi + lo queries already take 72 registers
-        f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
-        int cur = (lh * HALF) >> 7;
-        auto flush = [&](int grp) {
+      if constexpr (FP8) {
+        // The half (lh) is wave-uniform; each half gets its own fully unrolled loop so that the
+        // 128-feature group boundaries are compile-time: a group's partial scores are summed on
+        // their own and scaled by the positions' group scales (read once per block as 16-byte
+        // vectors), and the next step's fragments are read before this step's products.
+        auto qk_half = [&](auto lhc) {
+          constexpr int LH = decltype(lhc)::value;
+          constexpr int G0 = (LH * HALF) >> 7;
+          f32x4_t sc0[3], sc1[3];  // this half's groups (at most three below the rotary part)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float s0 = grp < 4 ? sScale[g * 4 + e][grp] : 1.0f;
-            const float s1 = grp < 4 ? sScale[16 + g * 4 + e][grp] : 1.0f;
-            sacc[0][e] += t0[e] * s0;
-            sacc[1][e] += t1[e] * s1;
+          for (int gi = 0; gi < 3; ++gi) {
+            const int grp = min(G0 + gi, 3);
+            sc0[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][g * 4]);
+            sc1[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][16 + g * 4]);
           }
-          t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
+          bf16x8_t k0 = as_bf16x8(ld16(r0)), k1 = as_bf16x8(ld16(r1));
+#pragma unroll
+          for (int ks = 0; ks < 9; ++ks) {
+            const int f = LH * HALF + ks * 32;
+            const int grp = f < KV_LORA ? (f >> 7) : 4;
+            bf16x8_t n0 = k0, n1 = k1;
+            if (ks + 1 < 9) {
+              n0 = as_bf16x8(ld16(r0 + ks * 32 + 32));
+              n1 = as_bf16x8(ld16(r1 + ks * 32 + 32));
+            }
+            t0 = mfma_bf16_16x16x32(k0, qf[ks], t0);
+            t1 = mfma_bf16_16x16x32(k1, qf[ks], t1);
+            t0 = mfma_bf16_16x16x32(k0, ql_[ks], t0);
+            t1 = mfma_bf16_16x16x32(k1, ql_[ks], t1);
+            if (grp == 4) {  // float32 rotary key: add its low halves against the high query
+              const int fp = f - KV_LORA + g * 8;
+              t0 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + l16 * 72 + fp)), qf[ks], t0);
+              t1 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + (16 + l16) * 72 + fp)), qf[ks], t1);
+            }
+            const int fn = f + 32;
+            const int gnext = ks + 1 < 9 ? (fn < KV_LORA ? (fn >> 7) : 4) : -1;
+            if (gnext != grp) {  // group done: scale (rotary part: scale 1) and add
+              if (grp < 4) {
+                sacc[0] += t0 * sc0[grp - G0];
+                sacc[1] += t1 * sc1[grp - G0];
+              } else {
+                sacc[0] += t0;
+                sacc[1] += t1;
+              }
+              t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            k0 = n0;
+            k1 = n1;
+          }
         };
-#pragma unroll
-        for (int ks = 0; ks < 9; ++ks) {
-          const int f = lh * HALF + ks * 32;
-          const int grp = f < KV_LORA ? (f >> 7) : 4;
-          if (grp != cur) {
-            flush(cur);
-            cur = grp;
-          }
-          const bf16x8_t k0 = as_bf16x8(ld16(r0 + ks * 32)), k1 = as_bf16x8(ld16(r1 + ks * 32));
-          t0 = mfma_bf16_16x16x32(k0, qf[ks], t0);
-          t1 = mfma_bf16_16x16x32(k1, qf[ks], t1);
-          t0 = mfma_bf16_16x16x32(k0, ql_[ks], t0);
-          t1 = mfma_bf16_16x16x32(k1, ql_[ks], t1);
-          if (grp == 4) {  // float32 rotary key: add its low halves against the high query
-            const int fp = f - KV_LORA + g * 8;
-            t0 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + l16 * 72 + fp)), qf[ks], t0);
-            t1 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + (16 + l16) * 72 + fp)), qf[ks], t1);
-          }
-        }
-        flush(cur);
+        if (lh == 0) qk_half(std::integral_constant<int, 0>{});
+        else qk_half(std::integral_constant<int, 1>{});
       } else {
         bf16x8_t k0[9], k1[9];
 #pragma unroll
@@ -342,7 +367,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[kt][e] = FP8 ? sv[kt][e] * sScale[kt * 16 + g * 4 + e][2 * lh + q] : sv[kt][e];
+          s[kt][e] = FP8 ? sv[kt][e] * sScale[2 * lh + q][kt * 16 + g * 4 + e] : sv[kt][e];
       u32x4_t w, r;
       w[0] = pack_bf16x2(s[0][0], s[0][1]);
       w[1] = pack_bf16x2(s[0][2], s[0][3]);
