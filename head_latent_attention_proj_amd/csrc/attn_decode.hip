@@ -20,7 +20,7 @@
 // Work layout: one workgroup = (sequence, split of `chunk` positions), 8 waves = 4 head groups of
 // 16 x 2 feature halves. Heads are the MFMA column dimension, so one 32-position block staged in
 // LDS feeds every head: S^T = C Q^T (A = cache rows, B = queries held in registers), then
-// O^T = C^T P^T from a transposed copy of the block's latent part written while staging. The next
+// O^T = C^T P^T with the block's columns read by LDS transpose reads. The next
 // block's loads are in flight (in registers) while a block is used. Each split writes (max, sum,
 // unnormalised o) per head; the merge kernel combines the splits and normalises; W_UV is applied
 // afterwards as a batched bf16 MFMA product (one 128 x 512 matrix per head).
@@ -35,11 +35,22 @@ namespace {
 
 constexpr int DKB = 32;    // positions per block
 constexpr int LDC = 584;   // sC row: 576 features + pad (1168 B: 16 rows -> distinct bank groups)
-constexpr int LDT = 36;    // sT row: 32 positions + pad (72 B: 16 rows -> distinct 8-byte slots)
 constexpr int HALF = 288;  // score features per wave: [0, 288) or [288, 576)
 constexpr float LOG2E = 1.4426950408889634f;
 
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3. With lane r of a group
+// pointing at row (r/4), columns 4*(r%4) .. +3 of a row-major tile, lane i receives column i of
+// rows 0..3: a K-major fragment read out of a K x N row-major tile. The value is bit-cast whole
+// (per-element access of the 16-bit vector is avoided).
+MLA_DEV u32x2_t ds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
 
 // four E4M3FN codes (one 32-bit word) -> two packed bf16 pairs (exact)
 MLA_DEV u32x2_t e4m3x4_to_bf16(uint32_t w) {
@@ -73,7 +84,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int head = hg * 16 + l16;
 
   __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];
-  __shared__ __attribute__((aligned(16))) uint16_t sT[KV_LORA * LDT];
   __shared__ __attribute__((aligned(16))) float xS[8][8][64];   // partial scores per wave
   __shared__ __attribute__((aligned(16))) float sScale[4][DKB];  // FP8 group scales [group][position]
   // FP8: low bf16 halves of the float32 rotary key (high halves sit in sC)
@@ -120,15 +130,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     }
   };
   auto put_pair = [&](int kp, int f0, const u32x4_t& x4, const u32x4_t& y4) {
-    // 8 bf16 features f0.. of positions 2kp (x4) and 2kp+1 (y4): row-major and transposed copies
+    // 8 bf16 features f0.. of positions 2kp (x4) and 2kp+1 (y4), row-major (the value mix reads
+    // columns with transpose reads)
     st16(sC + (2 * kp) * LDC + f0, x4);
     st16(sC + (2 * kp + 1) * LDC + f0, y4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = x4[j], y = y4[j];
-      *reinterpret_cast<uint32_t*>(sT + (f0 + 2 * j) * LDT + 2 * kp) = (x & 0xffffu) | (y << 16);
-      *reinterpret_cast<uint32_t*>(sT + (f0 + 2 * j + 1) * LDT + 2 * kp) = (x >> 16) | (y & 0xffff0000u);
-    }
   };
   auto sstore = [&]() {
     if constexpr (FP8) {
@@ -386,14 +391,17 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     // O^T[dim][head] += C^T[dim][keys] P^T[keys][head] over this wave's 256 latent features;
     // lane group g holds keys g*4..+3 and 16+g*4..+3
     {
-      const uint16_t* tp = sT + (lh * 256 + l16) * LDT + g * 4;
+      // lane (l16, g): feature lh*256 + 16c + l16 at keys 4g..4g+3 (lo) and 16+4g.. (hi), read
+      // as columns of the row-major block: lane r of the 16-lane group g points at key 4g + r/4,
+      // features 4(r%4) .. +3 of the 16-feature tile
+      const uint16_t* tp = sC + (4 * g + (l16 >> 2)) * LDC + lh * 256 + 4 * (l16 & 3);
 #pragma unroll
       for (int c0_ = 0; c0_ < 16; c0_ += 8) {
         u32x2_t lo[8], hi[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          lo[c] = ld8(tp + (c0_ + c) * 16 * LDT);
-          hi[c] = ld8(tp + (c0_ + c) * 16 * LDT + 16);
+          lo[c] = ds_read_tr16(tp + (c0_ + c) * 16);
+          hi[c] = ds_read_tr16(tp + 16 * LDC + (c0_ + c) * 16);
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -419,7 +427,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // D(32x32) += A(32x16) B(16x32), bf16 in, float32 accumulate. Lane l supplies row (A) / column
 // (B) l%32 and the eight k of group l/32; the result holds column l%32, rows
@@ -428,15 +435,6 @@ MLA_DEV f32x16_t mfma_bf16_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives element
-// (i % 4) of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3. With lane r of a group
-// pointing at row (r/4), columns 4*(r%4) .. +3 of a row-major tile, lane i receives column i of
-// rows 0..3: a K-major fragment read out of a K x N row-major tile. The value is bit-cast whole
-// (per-element access of the 16-bit vector is avoided).
-MLA_DEV u32x2_t ds_read_tr16(const uint16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
-  return __builtin_bit_cast(u32x2_t, v);
-}
 
 // Latent decode attention, bf16 cache entries, 32x32 MFMA tiles. Workgroup = (sequence, split),
 // 8 waves = 2 head groups of 32 x 4 feature quarters; each 16-byte cache fragment read from LDS
