@@ -427,10 +427,64 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, Norm
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Per-head products at 16 < M <= 64 with short K (decode W_UK absorb and W_UV, batch 17..64)
+// ------------------------------------------------------------------------------------------
+// Workgroup = (head, 128 output columns); x_h (M x K, K = 32 KS) is staged in LDS once and
+// every wave streams 16 weight rows over the whole K with all of its loads issued up front;
+// 16x16x32 MFMA, A fragments from LDS (rows >= M are copies of row M - 1 and never stored).
+template <int KS, int TAG>
+__global__ __launch_bounds__(512) void gemm_head_kernel(GemmArgs p) {
+  constexpr int LDX = KS * 32 + 8;  // padded LDS row: consecutive rows in distinct 16-byte bank groups
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * LDX];
+  const int batch = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.y * 128 + wave * 16;
+  const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
+  const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
+  u32x4_t wb[KS];
+  const uint16_t* wr = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) wb[ks] = ld16(wr + 32 * ks);
+  {
+    constexpr int CH = KS * 4;              // 16-byte chunks per row
+    constexpr int PER = 64 * CH / 512;      // chunks per thread
+    u32x4_t xv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 512 * i, row = c / CH, ch = c % CH;
+      xv[i] = ld16(A + (int64_t)min(row, p.M - 1) * p.lda + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 512 * i, row = c / CH, ch = c % CH;
+      st16(xs + row * LDX + ch * 8, xv[i]);
+    }
+  }
+  __syncthreads();
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = mfma_bf16_16x16x32(as_bf16x8(ld16(xs + (16 * i + l16) * LDX + 32 * ks + 8 * g)), as_bf16x8(wb[ks]), acc[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * i + 4 * g + e, n = n0 + l16;
+      if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][e]);
+    }
+}
+
 constexpr int TARGET_WGS = 512;  // two workgroups per CU on 256 CUs
 
 struct Plan {
-  int kind;  // 0 wsplit, 1 tile128, 2 tile256, 3 rows
+  int kind;  // 0 wsplit, 1 tile128, 2 tile256, 3 rows, 4 head
   int mt, kw, ysplit;
   int rpi, rw, u;  // rows kernel: rows per load, row groups per wave, loads per register set
   int splits, ksplit;
@@ -466,6 +520,14 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
     pl.splits = 1;
     pl.ksplit = K;
     pl.ysplit = 1;
+  }
+  // Per-head products, 16 < M <= 64, K of 128 or 512: x staged once per (head, 128 columns).
+  // Measured on MI355X at M = 64: W_UK absorb and W_UV run in a fraction of the streaming
+  // kernel's time, whose 16-column tiles re-read x for every tile.
+  if (M > 16 && M <= 64 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
+    pl.kind = 4;
+    pl.tiles = N / 128;
+    return pl;
   }
   // Streaming kernel for decode-sized M: always up to 16 rows; up to 64 rows when K is short
   // (kv_b, W_UK / W_UV), where a staged tile would spend most of its time filling LDS.
@@ -524,6 +586,12 @@ void launch_rows(const GemmArgs& a, const Plan& pl, dim3 grid, size_t lds, hipSt
 
 template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+  if (pl.kind == 4) {
+    dim3 grid(a.batch, pl.tiles);
+    if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, TAG>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gemm_head_kernel<16, TAG>), grid, dim3(512), 0, s, a);
+    return;
+  }
   if (pl.kind == 3) {
     dim3 grid(pl.tiles, pl.ysplit, a.batch);
     const size_t lds = (size_t)pl.mt * (a.K / pl.ysplit) * 2;

@@ -44,7 +44,7 @@ def test_gemm_matches_float64(M, N, K):
     assert err.max() <= 2e-5 * scale * 8
 
 
-@pytest.mark.parametrize("Bt", [1, 2, 5])
+@pytest.mark.parametrize("Bt", [1, 2, 5, 33, 64])
 def test_gemm_bf16_output_and_batched_strides(Bt):
     """Per-head batched product with row/batch strides (the decode absorption layout)."""
     import torch
@@ -65,7 +65,7 @@ def test_gemm_bf16_output_and_batched_strides(Bt):
     assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-6
 
 
-@pytest.mark.parametrize("Bt", [1, 2])
+@pytest.mark.parametrize("Bt", [1, 2, 20, 64])
 def test_gemm_value_mix_layout(Bt):
     """Per-head W_UV product: o[b][h*128 + d] = sum_c o_lat[b][h][c] W_UV,h[d][c] (K = 512)."""
     import torch
