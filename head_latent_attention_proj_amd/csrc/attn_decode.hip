@@ -84,7 +84,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int head = hg * 16 + l16;
 
   __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];
-  __shared__ __attribute__((aligned(16))) float xS[8][8][64];   // partial scores per wave
+  __shared__ __attribute__((aligned(16))) float xS[8][64][12];  // partial scores [wave][lane][8 + pad]
   __shared__ __attribute__((aligned(16))) float sScale[4][DKB];  // FP8 group scales [group][position]
   // FP8: low bf16 halves of the float32 rotary key (high halves sit in sC)
   __shared__ __attribute__((aligned(16))) uint16_t sKlo[FP8 ? DKB * 72 : 8];
@@ -322,20 +322,18 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
       }
     }
     // add the other half's partial scores (same order in both waves of a pair)
+    // 16-byte LDS accesses on 48-byte lane rows (eight lanes of one LDS cycle in distinct banks)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xS[wave][kt * 4 + e][lane] = sacc[kt][e];
+    for (int kt = 0; kt < 2; ++kt) *reinterpret_cast<f32x4_t*>(&xS[wave][lane][4 * kt]) = sacc[kt];
     __syncthreads();
     const int other = wave ^ 4;
     float sv[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      const f32x4_t theirs = *reinterpret_cast<const f32x4_t*>(&xS[other][lane][4 * kt]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float mine = sacc[kt][e], theirs = xS[other][kt * 4 + e][lane];
-        sv[kt][e] = lh == 0 ? mine + theirs : theirs + mine;
-      }
+      for (int e = 0; e < 4; ++e) sv[kt][e] = lh == 0 ? sacc[kt][e] + theirs[e] : theirs[e] + sacc[kt][e];
+    }
     float bmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -348,19 +346,27 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
       }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float mnew = fmaxf(mrun, bmax);
-    const float alpha = exp2f(mrun - mnew);
-    mrun = mnew;
+    // the running maximum is raised only when a block's maximum exceeds it by more than 8 (log2
+    // units): probabilities stay <= 256 and the accumulators are rescaled rarely (wave-uniform
+    // decision; every split's first block has a valid position, so mrun is finite after it)
+    if (__any(bmax > mrun + 8.0f)) {
+      const float mnew = fmaxf(mrun, bmax);
+      const float alpha = exp2f(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) oacc[c] *= alpha;
+      mrun = mnew;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(sv[kt][e] - mnew);
+        const float p = exp2f(sv[kt][e] - mrun);
         sv[kt][e] = p;
         psum += p;
       }
-    lrun = lrun * alpha + psum;
+    lrun += psum;
     // probabilities as the B operand of the value mix (FP8: one copy per 128-feature group,
     // each position's probability times that position's group scale)
     // FP8 also keeps the low bf16 halves (pl) so the mix is exact to about 16 bits
@@ -369,10 +375,12 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int q = 0; q < (FP8 ? 2 : 1); ++q) {
       float s[2][4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8) sc = *reinterpret_cast<const f32x4_t*>(&sScale[2 * lh + q][kt * 16 + g * 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[kt][e] = FP8 ? sv[kt][e] * sScale[2 * lh + q][kt * 16 + g * 4 + e] : sv[kt][e];
+        for (int e = 0; e < 4; ++e) s[kt][e] = sv[kt][e] * sc[e];
+      }
       u32x4_t w, r;
       w[0] = pack_bf16x2(s[0][0], s[0][1]);
       w[1] = pack_bf16x2(s[0][2], s[0][3]);
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const bf16x8_t vt = as_bf16x8(u32x4_t{lo[c][0], lo[c][1], hi[c][0], hi[c][1]});
-          oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pf[c0_ >> 3], oacc[c0_ + c] * alpha);
+          oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pf[c0_ >> 3], oacc[c0_ + c]);
           if constexpr (FP8) oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pl[c0_ >> 3], oacc[c0_ + c]);
         }
       }
