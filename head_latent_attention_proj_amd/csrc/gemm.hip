@@ -5,16 +5,18 @@
 // [out, in] ("Key content up-projection" page, Parameters), so every projection y = x W^T is
 // this "NT" form and both MFMA operands load 16 contiguous bytes per lane.
 //
-// Three kernels:
+// Kernels:
 //   * gemm_tile   -- prefill-sized M: BM x BN workgroup tile staged through LDS (double
 //                    buffered, padded rows so 16-byte fragment reads are bank-conflict free),
 //                    16x16x32 bf16 MFMA, XCD-aware grouped tile order. Optional split-K.
-//   * gemm_wsplit -- decode-sized M (<= 64): operands go straight from global memory into MFMA
-//                    fragments; the K range of a 16-column tile is split across the waves of one
-//                    workgroup (each wave streams its own contiguous slice of the weight rows,
-//                    four 32-wide K steps in flight), and the waves' partial tiles are summed
-//                    through LDS in a fixed order. No cross-workgroup synchronisation, no float
-//                    atomics: the result is deterministic.
+//   * gemm_skinny -- 16 < M <= 64 with K >= 1024: a ring of LDS stages filled by direct-to-LDS
+//                    loads in MFMA operand order, several stages in flight per workgroup.
+//   * gemm_wsplit -- other decode-sized M (<= 64): operands go straight from global memory into
+//                    MFMA fragments; the K range of a 16*NT-column tile is split across the waves
+//                    of one workgroup (each wave streams its own contiguous slice of the weight
+//                    rows), and the waves' partial tiles are summed through LDS in a fixed order.
+//                    No cross-workgroup synchronisation, no float atomics: deterministic.
+//   * gemm_head   -- per-head batched products at 16 < M <= 64 with K of 128 or 512.
 //   * gemm_rows   -- one or two rows of A: each load of a wave reads 1 KB (or 256 B) runs of
 //                    single weight rows, dot products on the VALU with x staged in LDS.
 //   Split-K of the tile kernel (few tiles, small M) writes fp32 partials and a separate
@@ -185,15 +187,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int spli
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode-sized M: one workgroup per 16-column tile, K split across its KW waves
+// Decode-sized M: one workgroup per 16*NT-column tile, K split across its KW waves
 // ------------------------------------------------------------------------------------------
-template <int MT, int KW, int TAG>
+// Each wave streams its own contiguous slice of K for all MT*16 rows of A and NT*16 weight rows
+// straight from global memory into MFMA fragments, U 32-wide K steps per pipeline stage, two
+// stages in flight. A wave reads MT A fragments and NT weight fragments per step, so for M > 16
+// a tile of NT > 1 columns keeps the (cached) activation reads near the weight stream instead
+// of MT times it. The waves' partial tiles are then summed through LDS by halving (wave w adds
+// wave w + KW/2, then w + KW/4, ...): a fixed order, so the result is deterministic.
+template <int MT, int NT, int U, int KW, int TAG>
 __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
-  constexpr int U = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);  // 32-wide K steps per pipeline stage
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NT;
   const int batch = blockIdx.z;
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
@@ -205,85 +212,108 @@ __global__ __launch_bounds__(KW * 64) void gemm_wsplit_kernel(GemmArgs p) {
   const int s0 = y0 + wave * spw;
   const int s1 = min(y1, s0 + spw);
 
-  // lane (l16, g): row l16 of the tile, features g*8 .. g*8+7 of each 32-wide step
+  // lane (l16, g): row l16 of each 16-row tile, features g*8 .. g*8+7 of each 32-wide step
   const uint16_t* pa[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) pa[i] = A + (int64_t)min(i * 16 + l16, p.M - 1) * p.lda + g * 8;
-  const uint16_t* pb = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + g * 8;
-
-  f32x4_t acc[MT];
+  const uint16_t* pb[NT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) pb[j] = B + (int64_t)min(n0 + j * 16 + l16, p.N - 1) * p.ldb + g * 8;
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (s0 < s1) {
     // Loads are unconditional (steps past the wave's range re-read its last step) so the
     // next stage's loads stay in flight while the current stage multiplies; a step past the
-    // range multiplies a zero weight fragment instead of being branched around.
-    u32x4_t ca[U][MT], cb[U];
-    auto load = [&](int s, u32x4_t (&ra)[U][MT], u32x4_t (&rb)[U]) {
+    // range multiplies zero weight fragments instead of being branched around.
+    u32x4_t ca[U][MT], cb[U][NT];
+    auto load = [&](int s, u32x4_t (&ra)[U][MT], u32x4_t (&rb)[U][NT]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int st = min(s + u, s1 - 1) * 32;
-        rb[u] = ld16(pb + st);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) rb[u][j] = ld16(pb[j] + st);
 #pragma unroll
         for (int i = 0; i < MT; ++i) ra[u][i] = ld16(pa[i] + st);
       }
     };
     load(s0, ca, cb);
     for (int s = s0; s < s1; s += U) {
-      u32x4_t na[U][MT], nb[U];
+      u32x4_t na[U][MT], nb[U][NT];
       load(min(s + U, s1 - 1), na, nb);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
-        const u32x4_t bw = (s + u < s1) ? cb[u] : zero;
+        const bool live = s + u < s1;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16_16x16x32(as_bf16x8(ca[u][i]), as_bf16x8(bw), acc[i]);
+        for (int j = 0; j < NT; ++j) {
+          const u32x4_t bw = live ? cb[u][j] : zero;
+#pragma unroll
+          for (int i = 0; i < MT; ++i) acc[i][j] = mfma_bf16_16x16x32(as_bf16x8(ca[u][i]), as_bf16x8(bw), acc[i][j]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        cb[u] = nb[u];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) cb[u][j] = nb[u][j];
 #pragma unroll
         for (int i = 0; i < MT; ++i) ca[u][i] = na[u][i];
       }
     }
   }
 
-  // fixed-order sum of the waves' partial tiles through LDS
+  // fixed-order sum of the waves' partial tiles through LDS, halving the live waves each round
   if constexpr (KW > 1) {
-    __shared__ float red[(KW - 1) * MT * 4 * 64];
-    if (wave > 0) {
+    __shared__ float red[(KW / 2) * MT * NT * 4 * 64];
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+    for (int half = KW / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(((wave - 1) * MT + i) * 4 + e) * 64 + lane] = acc[i][e];
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((((wave - half) * MT + i) * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] += red[(((wave * MT + i) * NT + j) * 4 + e) * 64 + lane];
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (wave != 0) return;
-    for (int w = 0; w < KW - 1; ++w)
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] += red[((w * MT + i) * 4 + e) * 64 + lane];
   }
   if (gridDim.y > 1) {  // partial sum of this K split (EPI_F32 only; the consumer adds the parts)
     float* C = (float*)p.C + blockIdx.y * p.c_split_stride + batch * p.sC;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = i * 16 + g * 4 + e, n = n0 + l16;
-        if (m < p.M && n < p.N) C[(int64_t)m * p.ldc + n] = acc[i][e];
-      }
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = i * 16 + g * 4 + e, n = n0 + j * 16 + l16;
+          if (m < p.M && n < p.N) C[(int64_t)m * p.ldc + n] = acc[i][j][e];
+        }
     return;
   }
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = i * 16 + g * 4 + e, n = n0 + l16;
-      if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][e]);
-    }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = i * 16 + g * 4 + e, n = n0 + j * 16 + l16;
+        if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][j][e]);
+      }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -481,11 +511,149 @@ __global__ __launch_bounds__(512) void gemm_head_kernel(GemmArgs p) {
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// 16 < M <= 64 with long K: a ring of LDS stages filled by direct-to-LDS loads
+// ------------------------------------------------------------------------------------------
+// Workgroup = NW waves = 16*NW output columns over one K split. A stage covers 64 features: the
+// A tile (16*MT rows as 2*MT fragment blocks of 16 rows x 32 features, fetched by the waves in
+// turn) and each wave's own two weight blocks (its 16 rows). One wave instruction fetches one
+// 1 KB block straight into LDS (lane l's 16 bytes land at byte 16*l), with lane (l16, g) reading
+// row l16, features 8g .. 8g+7: the block in LDS is already the MFMA operand image, and every
+// lane reads its operand back at 16*l (contiguous, conflict-free). The loads hold no registers,
+// so S-1 stages are in flight while one is multiplied, and one barrier per stage suffices.
+MLA_DEV void gl2lds16(const void* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt and lgkmcnt at their maxima).
+template <int N>
+MLA_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS byte address of a __shared__ pointer.
+MLA_DEV uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// One stage's operands of a wave: A blocks 0 .. 2*MT-1 at a + 1024*b, the wave's two weight blocks
+// at w and w + 1024 (byte addresses, this lane's 16 bytes). Written as one asm block that waits
+// for its own reads: the compiler does not know that these LDS reads never touch the ring slots
+// the direct-to-LDS loads are still filling, and would otherwise wait for every load in flight.
+// The outputs are early-clobber: a read's destination must not be an address register of a later
+// read in the block.
+template <int MT>
+MLA_DEV void lds_stage_operands(uint32_t a, uint32_t w, u32x4_t (&ra)[2 * MT], u32x4_t (&rb)[2]) {
+  if constexpr (MT == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %10 offset:1024\n\t"
+        "ds_read_b128 %2, %10 offset:2048\n\tds_read_b128 %3, %10 offset:3072\n\t"
+        "ds_read_b128 %4, %10 offset:4096\n\tds_read_b128 %5, %10 offset:5120\n\t"
+        "ds_read_b128 %6, %10 offset:6144\n\tds_read_b128 %7, %10 offset:7168\n\t"
+        "ds_read_b128 %8, %11\n\tds_read_b128 %9, %11 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(ra[4]), "=&v"(ra[5]), "=&v"(ra[6]), "=&v"(ra[7]),
+          "=&v"(rb[0]), "=&v"(rb[1])
+        : "v"(a), "v"(w)
+        : "memory");
+  } else {
+    static_assert(MT == 2, "MT 2 or 4");
+    asm volatile(
+        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:1024\n\t"
+        "ds_read_b128 %2, %6 offset:2048\n\tds_read_b128 %3, %6 offset:3072\n\t"
+        "ds_read_b128 %4, %7\n\tds_read_b128 %5, %7 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1])
+        : "v"(a), "v"(w)
+        : "memory");
+  }
+}
+
+// mode 0: epilogue; 1: split y's partial sum to C + y * c_split_stride (the consumer adds the
+// parts); 2: partials to p.part for splitk_reduce_kernel.
+template <int MT, int NW, int S, int TAG>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs p, int ksplit, int mode) {
+  constexpr int ABLK = 2 * MT;   // A fragment blocks per stage
+  constexpr int APW = ABLK / NW;  // of which each wave fetches APW
+  static_assert(ABLK % NW == 0 && S >= 2, "A blocks divide over the waves");
+  constexpr int LPS = APW + 2;                  // loads per stage per wave
+  constexpr int STAGE = (ABLK + 2 * NW) * 512;  // bf16 elements per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[S * STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NW + wave * 16;
+  const int batch = blockIdx.z;
+  const int kb = blockIdx.y * ksplit;
+  const int nst = (min(p.K, kb + ksplit) - kb) >> 6;  // >= 1 (plan)
+  const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
+  const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
+
+  const uint16_t* ga[APW];
+#pragma unroll
+  for (int j = 0; j < APW; ++j) {
+    const int blk = wave * APW + j;  // row group blk / 2, feature half blk % 2
+    ga[j] = A + (int64_t)min((blk >> 1) * 16 + l16, p.M - 1) * p.lda + kb + (blk & 1) * 32 + g * 8;
+  }
+  const uint16_t* gb = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + kb + g * 8;
+
+  // Fetch stage st into ring slot buf. Callers clamp st to the last stage: in the tail the
+  // re-fetch goes to the slot of a stage already consumed, so every iteration issues the same
+  // number of loads and the wait count below stays exact.
+  auto issue = [&](int st, int buf) {
+    uint16_t* base = ring + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < APW; ++j) gl2lds16(ga[j] + st * 64, base + (wave * APW + j) * 512);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) gl2lds16(gb + st * 64 + h * 32, base + (ABLK + wave * 2 + h) * 512);
+  };
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(min(t, nst - 1), t);
+  for (int t = 0; t < nst; ++t) {
+    wait_vmcnt<(S - 2) * LPS>();  // this wave's part of stage t has landed
+    // ... and every other wave's; all are done with stage t - 1. A plain barrier: __syncthreads'
+    // release fence would wait for every load in flight, collapsing the ring to one stage.
+    asm volatile("s_barrier" ::: "memory");
+    issue(min(t + S - 1, nst - 1), (t + S - 1) % S);
+    const uint16_t* base = ring + (t % S) * STAGE + lane * 8;
+    u32x4_t ra[2 * MT], rb[2];
+    lds_stage_operands<MT>(lds_addr(base), lds_addr(base + (ABLK + wave * 2) * 512), ra, rb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i] = mfma_bf16_16x16x32(as_bf16x8(ra[2 * i + h]), as_bf16x8(rb[h]), acc[i]);
+  }
+  wait_vmcnt<0>();  // the tail's re-fetches land before the workgroup's LDS is released
+
+  const int n = n0 + l16;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = i * 16 + g * 4 + e;
+      if (m >= p.M || n >= p.N) continue;
+      if (mode == 0)
+        epi_store(p, batch, m, n, acc[i][e]);
+      else if (mode == 1)
+        ((float*)p.C)[blockIdx.y * p.c_split_stride + batch * p.sC + (int64_t)m * p.ldc + n] = acc[i][e];
+      else
+        p.part[((int64_t)batch * gridDim.y + blockIdx.y) * p.M * p.N + (int64_t)m * p.N + n] = acc[i][e];
+    }
+}
+
 constexpr int TARGET_WGS = 512;  // two workgroups per CU on 256 CUs
 
 struct Plan {
-  int kind;  // 0 wsplit, 1 tile128, 2 tile256, 3 rows, 4 head
-  int mt, kw, ysplit;
+  int kind;  // 0 wsplit, 1 tile128, 2 tile256, 3 rows, 4 head, 5 skinny (LDS ring)
+  int mt, nt, kw, ysplit;
+  int nw;    // skinny kernel: waves (16 columns each) per workgroup
+  int mode;  // skinny kernel: 0 epilogue, 1 K-split parts to C (consumer adds), 2 parts + reduce
   int rpi, rw, u;  // rows kernel: rows per load, row groups per wave, loads per register set
   int splits, ksplit;
   int tiles;  // workgroups per (split, batch)
@@ -529,12 +697,34 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
     pl.tiles = N / 128;
     return pl;
   }
-  // Streaming kernel for decode-sized M: always up to 16 rows; up to 64 rows when K is short
-  // (kv_b, W_UK / W_UV), where a staged tile would spend most of its time filling LDS.
-  if (M <= 16 || (M <= 64 && K <= 512)) {
+  // 16 < M <= 64 with long K (single products: the projections at decode batch 17..64 and at
+  // short prefills): the LDS-ring kernel. Measured on MI355X at M = 64: o_proj (7168 x 8192)
+  // runs best with 128-column tiles and K split to about two workgroups per CU (40 us; the
+  // 128 x 128 tile kernel 44 us), q_b (K = 1536) and kv_b-sized products with 64-column tiles
+  // and no split (21.5 us against 25), q_a | kv_a with 64-column tiles and 4 splits.
+  if (M > 16 && M <= 64 && batch == 1 && K >= 1024) {
+    pl.kind = 5;
+    pl.mt = M <= 32 ? 2 : 4;
+    pl.nw = (pl.mt == 4 && (int64_t)N * K >= ((int64_t)32 << 20)) ? 8 : 4;
+    pl.tiles = cdiv(N, 16 * pl.nw);
+    const int nst = K / 64;
+    int sp = pl.nw == 8 ? (TARGET_WGS + pl.tiles / 2) / pl.tiles : (K <= 2048 ? 1 : 4);
+    sp = std::max(1, std::min(sp, nst / 8));
+    pl.ksplit = cdiv(nst, sp) * 64;
+    sp = cdiv(K, pl.ksplit);
+    if (sp == 1) pl.mode = 0;
+    else if (sp <= ysplit_max) { pl.mode = 1; pl.ysplit = sp; }
+    else { pl.mode = 2; pl.splits = sp; }
+    return pl;
+  }
+  // Streaming kernel for decode-sized M: 16-column tiles up to 16 rows, 32-column tiles (two
+  // weight fragments per step, so activation reads stay within twice the weight stream) up to
+  // 64 rows.
+  if (M <= 64) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    pl.tiles = cdiv(N, 16);
+    pl.nt = M <= 16 ? 1 : 2;
+    pl.tiles = cdiv(N, 16 * pl.nt);
     const int steps = K / 32;
     // Measured on MI355X: a stream runs best with at least ~24 K steps per wave and ~1-2
     // thousand waves in the grid. K is first split over workgroups where the consumer adds
@@ -563,17 +753,35 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
   return pl;
 }
 
-template <int MT, int TAG>
+template <int MT, int NT, int U, int TAG>
 void launch_wsplit(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   dim3 grid(pl.tiles, pl.ysplit, a.batch);
   switch (pl.kw) {
-    case 1: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 1, TAG>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 2, TAG>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 4, TAG>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 8, TAG>), grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, NT, U, 1, TAG>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, NT, U, 2, TAG>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, NT, U, 4, TAG>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_wsplit_kernel<MT, NT, U, 8, TAG>), grid, dim3(512), 0, s, a); break;
     default:
-      if constexpr (MT == 1) hipLaunchKernelGGL((gemm_wsplit_kernel<MT, 16, TAG>), grid, dim3(1024), 0, s, a);
+      if constexpr (MT == 1) hipLaunchKernelGGL((gemm_wsplit_kernel<MT, NT, U, 16, TAG>), grid, dim3(1024), 0, s, a);
       break;
+  }
+}
+
+template <int MT, int TAG>
+void launch_skinny(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+  dim3 grid(pl.tiles, std::max(pl.splits, pl.ysplit), a.batch);
+  if constexpr (MT == 4) {
+    if (pl.nw == 8) {
+      hipLaunchKernelGGL((gemm_skinny_kernel<MT, 8, 3, TAG>), grid, dim3(512), 0, s, a, pl.ksplit, pl.mode);
+    } else {
+      hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, 4, TAG>), grid, dim3(256), 0, s, a, pl.ksplit, pl.mode);
+    }
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, 4, TAG>), grid, dim3(256), 0, s, a, pl.ksplit, pl.mode);
+  }
+  if (pl.mode == 2) {
+    dim3 rgrid((unsigned)(((int64_t)a.M * a.N + 255) / 256), a.batch);
+    hipLaunchKernelGGL((splitk_reduce_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
   }
 }
 
@@ -604,10 +812,15 @@ void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
     }
     return;
   }
+  if (pl.kind == 5) {
+    if (pl.mt == 2) launch_skinny<2, TAG>(a, pl, s);
+    else launch_skinny<4, TAG>(a, pl, s);
+    return;
+  }
   if (pl.kind == 0) {
-    if (pl.mt == 1) launch_wsplit<1, TAG>(a, pl, s);
-    else if (pl.mt == 2) launch_wsplit<2, TAG>(a, pl, s);
-    else launch_wsplit<4, TAG>(a, pl, s);
+    if (pl.mt == 1) launch_wsplit<1, 1, 8, TAG>(a, pl, s);
+    else if (pl.mt == 2) launch_wsplit<2, 2, 4, TAG>(a, pl, s);
+    else launch_wsplit<4, 2, 2, TAG>(a, pl, s);
     return;
   }
   dim3 grid(pl.tiles, pl.splits, a.batch);

@@ -24,6 +24,8 @@ def bf16_rand(shape, seed, std=1.0):
     (1, 1100, 1536), (2, 1100, 640), (1, 20, 128), (3, 12288, 1536), (16, 7168, 8192), (17, 2112, 7168),
     (33, 16384, 512), (64, 7168, 8192), (65, 2112, 7168), (100, 12288, 1536), (128, 7168, 8192),
     (300, 16384, 512), (1000, 2112, 7168), (1024, 1100, 1536), (2048, 7168, 8192),
+    # LDS-ring kernel (16 < M <= 64, K >= 1024): 64- and 128-column tiles, K splits, ragged N
+    (48, 12288, 1536), (32, 2112, 7168), (64, 16384, 1024), (20, 1100, 1024), (40, 7100, 8192),
 ])
 def test_gemm_matches_float64(M, N, K):
     import torch
