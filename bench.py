@@ -99,7 +99,7 @@ def main():
     # ---------------- headline: decode B=1 at position 1000 over 1000 cached positions
     P0 = 1000
     total_steps = args.steps + args.warmup
-    caps = P0 + total_steps // args.copies + 2
+    caps = P0 + 2 * (total_steps // args.copies + 2)  # the headline steps, then the block's
     caches, xs = [], []
     x_fill = binding.bf16_tensor(synth.make_hidden(P0, seed=1001))
     for c, L in enumerate(layers):
@@ -121,6 +121,18 @@ def main():
     us_per_step = t_dec * 1e6
     lens_after = np.array([P0 + 1])
     dec_bytes = decode_step_bytes(lens_after, 1)
+
+    # ---------------- the same step as the attention half of a decoder block (input RMSNorm
+    # before the layer, residual added in o_proj's epilogue), on the same caches
+    log("timing block decode B=1")
+    gain = binding.bf16_tensor(synth.make_block_norm(seed=7))
+    h_new = torch.empty_like(x_new)
+
+    def block_step(i):
+        c = i % args.copies
+        layers[c].block_decode(caches[c], sid_h, gain, x_new, h=h_new, seq_ids_d=sid_d)
+
+    t_blk = timed_loop(torch, block_step, args.steps, args.warmup)
 
     # ---------------- roofline: o_proj kernel of that step, HIP events on its stream
     log("timing o_proj kernel")
@@ -145,7 +157,10 @@ def main():
     achieved = oproj_bytes / (oproj_ms * 1e-3) / 1e9
     traffic = counted_traffic()
 
-    extra = {}
+    extra = {"block_decode_B1": {
+        "us_per_step": round(t_blk * 1e6, 3),
+        "note": "decoder-block attention half h = x + MLA(RMSNorm(x)): input-norm kernel, the decode step, "
+                "residual fused into o_proj; positions 1000+ on the headline caches"}}
     if not args.no_extra:
         # ---------------- prefill T=64 and T=8192
         for T, steps in ((64, 30), (8192, 5)):

@@ -22,6 +22,7 @@ EXPORTED = (
     "mla_packed_weight_bytes", "mla_cache_entry_bytes", "mla_prefill_workspace_bytes",
     "mla_decode_workspace_bytes", "mla_workspace_init", "mla_init_weights", "mla_prefill", "mla_decode",
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
+    "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
     "mla_test_gemm_workspace_bytes", "mla_test_gemm",
 )
 STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6}
@@ -80,6 +81,14 @@ def lib() -> ctypes.CDLL:
     L.mla_prefill.restype = ctypes.c_int
     L.mla_decode.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp, sz, vp]
     L.mla_decode.restype = ctypes.c_int
+    L.mla_block_prefill_workspace_bytes.argtypes = [vp, i32, i32, i64]
+    L.mla_block_prefill_workspace_bytes.restype = sz
+    L.mla_block_decode_workspace_bytes.argtypes = [vp, i32, i64]
+    L.mla_block_decode_workspace_bytes.restype = sz
+    L.mla_block_prefill.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.mla_block_prefill.restype = ctypes.c_int
+    L.mla_block_decode.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.mla_block_decode.restype = ctypes.c_int
     L.mla_cache_append.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), i32, vp, i32, vp]
     L.mla_cache_append.restype = ctypes.c_int
     L.mla_destroy.argtypes = [vp]
@@ -241,6 +250,43 @@ class Layer:
                                _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
         self._keep = (seq_ids_d,)
         return y
+
+    def block_prefill(self, cache: Cache, seq_ids, q_start, norm_weight, x, h=None, stream=None):
+        """Attention half of a decoder block, h = x + MLA(RMSNorm(x)); x [sum T, 7168] bf16 cuda,
+        norm_weight [7168] bf16 cuda. h may be x (in place). Returns h."""
+        import torch
+
+        seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        q_start = np.ascontiguousarray(q_start, dtype=np.int32)
+        B = len(seq_ids)
+        keys = int(sum(cache.held(s) + int(q_start[b + 1] - q_start[b]) for b, s in enumerate(seq_ids)))
+        ws = self.workspace(lib().mla_block_prefill_workspace_bytes(self.ctx, int(q_start[-1]), B, keys), stream)
+        if h is None:
+            h = torch.empty_like(x)
+        sid_d = torch.from_numpy(seq_ids).to(x.device)
+        qs_d = torch.from_numpy(q_start).to(x.device)
+        check(lib().mla_block_prefill(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(sid_d),
+                                      q_start.ctypes.data, _ptr(qs_d), B, _ptr(norm_weight), _ptr(x), _ptr(h),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+        self._keep = (sid_d, qs_d)
+        return h
+
+    def block_decode(self, cache: Cache, seq_ids, norm_weight, x, h=None, seq_ids_d=None, stream=None):
+        """Decode step of the block's attention half: x [B, 7168] bf16 cuda. Returns h."""
+        import torch
+
+        seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        B = len(seq_ids)
+        keys = int(sum(cache.held(s) + 1 for s in seq_ids))
+        ws = self.workspace(lib().mla_block_decode_workspace_bytes(self.ctx, B, keys), stream)
+        if h is None:
+            h = torch.empty_like(x)
+        if seq_ids_d is None:
+            seq_ids_d = torch.from_numpy(seq_ids).to(x.device)
+        check(lib().mla_block_decode(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(seq_ids_d), B,
+                                     _ptr(norm_weight), _ptr(x), _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
+        self._keep = (seq_ids_d,)
+        return h
 
     def cache_append(self, cache: Cache, seq: int, entries, stream=None):
         """entries: cuda tensor holding n * entry_bytes bytes in the slot format."""

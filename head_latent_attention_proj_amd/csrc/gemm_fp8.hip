@@ -56,6 +56,7 @@ MLA_DEV void epi_store8(const GemmArgs& p, int b, int m, int n, float v) {
   if (p.epi == EPI_F32) {
     ((float*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = v;
   } else if (p.epi == EPI_BF16) {
+    if (p.resid) v += bf2f(p.resid[(int64_t)m * p.ldr + n]);
     ((uint16_t*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = f2bf(v);
   } else {  // EPI_KVB; with knope_lo / vt_lo set, the bf16 residual goes to a second plane
     const int h = n >> 8, r = n & 255;

@@ -45,6 +45,10 @@ struct GemmArgs {
   // split y writing its partial sum to C + y * c_split_stride (the consumer adds the parts).
   int ysplit_max = 1;
   int64_t c_split_stride = 0;
+  // EPI_BF16 only: residual added before the bf16 rounding, C[m][n] = bf16(acc + resid[m * ldr + n])
+  // (batch 1; the decoder block's residual connection fused into o_proj)
+  const uint16_t* resid = nullptr;
+  int64_t ldr = 0;
   // split-K scratch (workspace): fp32 partials and per-tile arrival counters (kept zeroed)
   float* part = nullptr;
   int* counters = nullptr;
@@ -193,6 +197,10 @@ hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, u
 // q_nope parts of float32 q [n][64][192] -> bf16 high parts [n][64][128] followed by the bf16
 // residuals [n][64][128] (the FP8 decode absorbs both and adds the two products).
 hipError_t split_q_nope(const float* q, int n, uint16_t* out, hipStream_t s);
+
+// Decoder-block input RMSNorm over the hidden features (K = 7168) of n bf16 rows:
+// y = bf16(g * bf16(x * r)), r = 1 / sqrt(mean(x^2) + eps) in float32.
+hipError_t input_rmsnorm(const uint16_t* x, const uint16_t* g, float eps, int n, uint16_t* y, hipStream_t s);
 
 // Fill kernel for small control blocks (used instead of memset so callers may capture graphs).
 hipError_t fill_zero_i32(int* p, int64_t n, hipStream_t s);

@@ -456,9 +456,26 @@ mla_status mla_cache_append(mla_ctx* ctx, mla_cache* cache, int32_t seq_id, cons
   return MLA_OK;
 }
 
-mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
-                       const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
-                       void* ws, size_t ws_bytes, mla_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Bytes at the front of a block call's workspace that hold the normalised input [ntok][7168] bf16.
+size_t block_xn_bytes(int64_t ntok) { return round_up((size_t)std::max<int64_t>(ntok, 0) * HIDDEN * 2, 256); }
+
+// The block's h may be its x (in place: o_proj reads each residual element right before writing
+// the same element) or a disjoint buffer; a partial overlap is rejected.
+bool partial_overlap(const void* a, const void* b, size_t bytes) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa != pb && pa < pb + bytes && pb < pa + bytes;
+}
+
+// One prefill call. norm_w == nullptr: the layer, y = MLA(x). Otherwise the attention half of a
+// decoder block: the workspace starts with xn = input RMSNorm of x (gain norm_w), the layer runs
+// on xn and o_proj adds the residual x: y = x + MLA(xn).
+mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                        const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
+                        void* ws, size_t ws_bytes, mla_stream stream, const void* norm_w) {
   if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
   mla_status st = check_cache(ctx, cache);
   if (st != MLA_OK) return st;
@@ -486,10 +503,21 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   for (int b = 0; b < B; ++b)
     gp = std::max(gp, max_gemm_part(0, cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b], false, ctx->fp8));
   const WsLayout L = ws_layout(ntok, B, nkeys, 0, gp, ctx->fp8);
-  if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
+  const size_t xn_bytes = norm_w ? block_xn_bytes(ntok) : 0;
+  if (ws_bytes < xn_bytes + L.total)
+    return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, xn_bytes + L.total);
+  if (norm_w && partial_overlap(x, y, (size_t)ntok * HIDDEN * 2))
+    return fail(MLA_E_ARG, "h must be x itself or not overlap it");
 
   hipStream_t s = (hipStream_t)stream;
-  uint8_t* w = (uint8_t*)ws;
+  const void* resid = nullptr;
+  if (norm_w) {
+    HIP_TRY(mla_k::input_rmsnorm((const uint16_t*)x, (const uint16_t*)norm_w, ctx->cfg.rms_eps, ntok,
+                                 (uint16_t*)ws, s));
+    resid = x;
+    x = ws;
+  }
+  uint8_t* w = (uint8_t*)ws + xn_bytes;
   const bool fp8 = ctx->fp8;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
   auto* meta = (mla_k::SeqMeta*)(w + L.meta);
@@ -556,6 +584,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
   g.C = y; g.ldc = HIDDEN; g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
+  g.resid = (const uint16_t*)resid; g.ldr = HIDDEN;
   HIP_TRY(run_proj(ctx, g, s));
   // 7. lengths
   HIP_TRY(mla_k::commit_lengths(seq_ids_d, q_start_d, cache->len_d, B, s));
@@ -563,8 +592,9 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   return MLA_OK;
 }
 
-mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
-                      const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream) {
+// One decode step; norm_w as in prefill_impl.
+mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
+                       const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream, const void* norm_w) {
   if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
   mla_status st = check_cache(ctx, cache);
   if (st != MLA_OK) return st;
@@ -582,10 +612,20 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   const DecodePlan dp = plan_decode(B, lens.data(), B, ctx->fp8);
   const int64_t gp = max_gemm_part(B, 0, true, ctx->fp8);
   const WsLayout L = ws_layout(B, B, 0, B * dp.max_splits, gp, ctx->fp8);
-  if (ws_bytes < L.total) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, L.total);
+  const size_t xn_bytes = norm_w ? block_xn_bytes(B) : 0;
+  if (ws_bytes < xn_bytes + L.total)
+    return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, xn_bytes + L.total);
+  if (norm_w && partial_overlap(x, y, (size_t)B * HIDDEN * 2))
+    return fail(MLA_E_ARG, "h must be x itself or not overlap it");
 
   hipStream_t s = (hipStream_t)stream;
-  uint8_t* w = (uint8_t*)ws;
+  const void* resid = nullptr;
+  if (norm_w) {
+    HIP_TRY(mla_k::input_rmsnorm((const uint16_t*)x, (const uint16_t*)norm_w, ctx->cfg.rms_eps, B, (uint16_t*)ws, s));
+    resid = x;
+    x = ws;
+  }
+  uint8_t* w = (uint8_t*)ws + xn_bytes;
   const bool fp8 = ctx->fp8;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
   // 1. fused q_a | kv_a (K split over workgroups at small batch; the norm kernel adds the parts)
@@ -672,9 +712,52 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
   g.C = y; g.ldc = HIDDEN; g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
+  g.resid = (const uint16_t*)resid; g.ldr = HIDDEN;
   HIP_TRY(run_proj(ctx, g, s));
   for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                       const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
+                       void* ws, size_t ws_bytes, mla_stream stream) {
+  return prefill_impl(ctx, cache, seq_ids_h, seq_ids_d, q_start_h, q_start_d, B, x, y, ws, ws_bytes, stream, nullptr);
+}
+
+mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
+                      const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream) {
+  return decode_impl(ctx, cache, seq_ids_h, seq_ids_d, B, x, y, ws, ws_bytes, stream, nullptr);
+}
+
+size_t mla_block_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32_t max_batch, int64_t max_keys) {
+  const size_t n = mla_prefill_workspace_bytes(ctx, max_tokens, max_batch, max_keys);
+  return n ? n + block_xn_bytes(max_tokens) : 0;
+}
+
+size_t mla_block_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t max_keys) {
+  const size_t n = mla_decode_workspace_bytes(ctx, max_batch, max_keys);
+  return n ? n + block_xn_bytes(max_batch) : 0;
+}
+
+mla_status mla_block_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                             const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* norm_weight,
+                             const void* x, void* h, void* ws, size_t ws_bytes, mla_stream stream) {
+  if (!norm_weight) return fail(MLA_E_ARG, "norm_weight is NULL");
+  if (!aligned16(norm_weight)) return fail(MLA_E_ALIGN, "norm_weight is not 16-byte aligned");
+  return prefill_impl(ctx, cache, seq_ids_h, seq_ids_d, q_start_h, q_start_d, B, x, h, ws, ws_bytes, stream,
+                      norm_weight);
+}
+
+mla_status mla_block_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                            int32_t B, const void* norm_weight, const void* x, void* h, void* ws, size_t ws_bytes,
+                            mla_stream stream) {
+  if (!norm_weight) return fail(MLA_E_ARG, "norm_weight is NULL");
+  if (!aligned16(norm_weight)) return fail(MLA_E_ALIGN, "norm_weight is not 16-byte aligned");
+  return decode_impl(ctx, cache, seq_ids_h, seq_ids_d, B, x, h, ws, ws_bytes, stream, norm_weight);
 }
 
 size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch) {

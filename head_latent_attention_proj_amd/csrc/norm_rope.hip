@@ -246,6 +246,49 @@ __global__ void split_q_nope_kernel(const float* q, int n, uint16_t* out) {
   out[total + i] = f2bf(v - bf2f(hi));
 }
 
+// Decoder-block input RMSNorm ("Attention input" page: the block excerpt normalises the block
+// input before the attention; the rmsnorm excerpt computes in float32 and casts the normalised
+// value back to the input dtype before the gain, and bf16 gain times bf16 activation is again
+// bf16). One 128-thread workgroup per token, 7 16-byte chunks of the 7168 features per thread:
+// y = bf16(g * bf16(x * r)), r = 1 / sqrt(mean(x^2) + eps).
+__global__ __launch_bounds__(128) void input_rmsnorm_kernel(const uint16_t* x, const uint16_t* g, float eps,
+                                                            uint16_t* y) {
+  constexpr int K = mla_dims::HIDDEN;
+  constexpr int CH = K / (128 * 8);
+  static_assert(CH * 128 * 8 == K, "hidden size is a multiple of 1024");
+  __shared__ float part[2];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * K;
+  u32x4_t v[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    v[c] = ld16(xr + (c * 128 + tid) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf_lo(v[c][j]), b = bf_hi(v[c][j]);
+      ss += a * a + b * b;
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((part[0] + part[1]) / (float)K + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int f = (c * 128 + tid) * 8;
+    const u32x4_t gv = ld16(g + f);
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float t0 = bf2f(f2bf(bf_lo(v[c][j]) * r)), t1 = bf2f(f2bf(bf_hi(v[c][j]) * r));
+      o[j] = pack_bf16x2(bf_lo(gv[j]) * t0, bf_hi(gv[j]) * t1);
+    }
+    st16(y + row * K + f, o);
+  }
+}
+
 __global__ void fill_zero_kernel(int* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -301,6 +344,12 @@ hipError_t split_q_nope(const float* q, int n, uint16_t* out, hipStream_t s) {
   const int64_t total = (int64_t)n * mla_dims::HEADS * mla_dims::NOPE;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(split_q_nope_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, q, n, out);
+  return hipGetLastError();
+}
+
+hipError_t input_rmsnorm(const uint16_t* x, const uint16_t* g, float eps, int n, uint16_t* y, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(input_rmsnorm_kernel, dim3(n), dim3(128), 0, s, x, g, eps, y);
   return hipGetLastError();
 }
 

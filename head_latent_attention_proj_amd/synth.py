@@ -155,6 +155,12 @@ def make_hidden(n_tokens: int, d: Dims = KIMI_K2, seed: int = 1000, std: float =
     return _normal_bf16(rng, (n_tokens, d.hidden), 0.0, std)
 
 
+def make_block_norm(d: Dims = KIMI_K2, seed: int = 7, gain_std: float = 0.1) -> np.ndarray:
+    """Decoder-block input RMSNorm gain [hidden] ~ 1 + N(0, gain_std) in bf16 bits."""
+    rng = np.random.default_rng(seed)
+    return _normal_bf16(rng, (d.hidden,), 1.0, gain_std)
+
+
 def make_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Per-sequence cached lengths, uniform integers in [lo, hi] inclusive."""
     rng = np.random.default_rng(seed)

@@ -172,6 +172,30 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
 mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
                       int32_t B, const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream);
 
+/* ---- Attention half of a decoder block ("Attention input" page, block excerpt): the block
+ * keeps its input as the residual, feeds the attention its input RMSNorm and adds the attention
+ * output back:  h = x + MLA(xn),  xn = RMSNorm(x) over the 7168 hidden features with gain
+ * norm_weight and eps = cfg.rms_eps. xn follows the rmsnorm excerpt's dtypes: the normalised
+ * value (float32) is rounded to bf16 before the gain and the product with the bf16 gain is
+ * bf16, xn = bf16(g * bf16(x / sqrt(mean(x^2) + eps))). The residual is added to o_proj's
+ * float32 sum before its single bf16 rounding.
+ *   norm_weight  device [7168] bf16 (the block's input_layernorm weight), 16-byte aligned
+ *   x, h         device [rows, 7168] bf16; h may be x itself (in place) or a buffer that does
+ *                not overlap it (a partial overlap gives MLA_E_ARG)
+ *   ws           workspace of ws_bytes >= mla_block_prefill_workspace_bytes(...) (or
+ *                _decode_), initialised once with mla_workspace_init; its first
+ *                rows * 7168 * 2 bytes (rounded up to 256) hold xn, the rest is the layer's.
+ * Everything else (cache, positions, validation before any enqueue, errors) is exactly as for
+ * mla_prefill / mla_decode. */
+size_t mla_block_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32_t max_batch, int64_t max_keys);
+size_t mla_block_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t max_keys);
+mla_status mla_block_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                             const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* norm_weight,
+                             const void* x, void* h, void* ws, size_t ws_bytes, mla_stream stream);
+mla_status mla_block_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                            int32_t B, const void* norm_weight, const void* x, void* h, void* ws, size_t ws_bytes,
+                            mla_stream stream);
+
 /* Append n ready-made entries (device, n * mla_cache_entry_bytes bytes, the slot format above)
  * to sequence seq_id at positions len .. len+n-1: a byte copy into the slots, then len += n.
  * Used to load a cache produced elsewhere (for example from a saved state). */

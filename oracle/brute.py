@@ -6,7 +6,8 @@ head widths 2-4, a handful of tokens). Every loop follows one equation of the pa
 
   "Key-value latent" page, mla-init / mla-kv / rmsnorm excerpts;
   "Key content up-projection" page, code excerpt (assembly, scores, mask, softmax, P.V);
-  dense-block attention page, mla-output excerpt (flatten heads, o_proj).
+  dense-block attention page, mla-output excerpt (flatten heads, o_proj);
+  "Attention input" page, block and rmsnorm excerpts (input RMSNorm in bf16, residual add).
 """
 from __future__ import annotations
 
@@ -81,3 +82,26 @@ def forward(x, w, dims, eps, theta, sigma, cache_entries=None):
             o_flat.extend(o_h)
         ys.append(_matvec(w["o"], o_flat))
     return ys, entries[l0:]
+
+
+def _bf16(v):
+    """Nearest bfloat16 (8 significant bits, ties to even) of a Python float."""
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)          # v = m * 2**e, 0.5 <= |m| < 1
+    q = m * 256.0
+    r = math.floor(q)
+    d = q - r
+    if d > 0.5 or (d == 0.5 and r % 2 == 1):
+        r += 1
+    return math.ldexp(r, e - 8)
+
+
+def block(x, w, g_in, dims, eps, theta, sigma, cache_entries=None):
+    """h = x + layer(xn) per token, xn = bf16(g_in * bf16(x / rms(x))). Returns (h rows, entries)."""
+    xn = []
+    for xt in x:
+        r = 1.0 / math.sqrt(sum(v * v for v in xt) / len(xt) + eps)
+        xn.append([_bf16(g_in[i] * _bf16(xt[i] * r)) for i in range(len(xt))])
+    ys, ents = forward(xn, w, dims, eps, theta, sigma, cache_entries)
+    return [[x[t][i] + ys[t][i] for i in range(len(x[t]))] for t in range(len(x))], ents

@@ -230,6 +230,44 @@ def kv_entries(x: np.ndarray, w: dict, pos0: int = 0, cfg: Config = KIMI_K2, w8a
 
 
 # ----------------------------------------------------------------------------------------------
+# attention half of a decoder block: input RMSNorm, the layer, residual addition
+# ----------------------------------------------------------------------------------------------
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even (8 significant bits), in float64.
+
+    frexp gives v = m * 2^e with 0.5 <= |m| < 1; the significand m * 2^8 is rounded to an
+    integer (numpy rounds halves to even) and scaled back. Values stay in the normal range here.
+    """
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def input_rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """The block's input RMSNorm with the dtype flow of the rmsnorm excerpt ("Attention input"
+    page): the normalised activation is cast back to the input dtype (bf16) before the gain, and
+    the product of the bf16 gain with it is again a bf16 tensor -- the layer's bf16 input. So
+    y = bf16(g * bf16(x / sqrt(mean(x^2) + eps))), with the mean and root exact in float64.
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return round_bf16(g * round_bf16(x / np.sqrt(ms + eps)))
+
+
+def block_attention(x: np.ndarray, w: dict, g_in: np.ndarray, cfg: Config = KIMI_K2, cache: tuple | None = None,
+                    rows: np.ndarray | None = None, w8a8: bool = False, absorbed: bool = False) -> dict:
+    """Attention half of a decoder block ("Attention input" page, block excerpt): the residual
+    is the block input, the layer sees its input RMSNorm (gain g_in over the hidden features,
+    eps = rms_norm_eps), and the layer output is added to the residual: h = x + MLA(norm(x)).
+
+    Same arguments as `forward`; returns h [len(rows), hidden], the normalised input xn and
+    everything `forward` returns for it.
+    """
+    xn = input_rmsnorm(x, g_in, cfg.eps)
+    out = forward(xn, w, cfg, cache=cache, rows=rows, w8a8=w8a8, absorbed=absorbed)
+    r = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    return {"h": x[r] + out["y"], "xn": xn, **out}
+
+
+# ----------------------------------------------------------------------------------------------
 # absorbed (latent-space) form -- a cross-check of the algebra, not the definition
 # ----------------------------------------------------------------------------------------------
 def attend_absorbed(q_nope: np.ndarray, q_pe: np.ndarray, c_hat: np.ndarray, k_pe: np.ndarray,

@@ -78,6 +78,11 @@ def test_calls_reject_null_context(L):
     assert L.mla_prefill(None, ctypes.byref(desc), None, None, None, None, 1, None, None, None, 0, None) == 1
     assert L.mla_decode(None, ctypes.byref(desc), None, None, 1, None, None, None, 0, None) == 1
     assert L.mla_cache_append(None, ctypes.byref(desc), 0, None, 1, None) == 1
+    assert L.mla_block_prefill(None, ctypes.byref(desc), None, None, None, None, 1, None, None, None, None, 0,
+                               None) == 1
+    assert L.mla_block_decode(None, ctypes.byref(desc), None, None, 1, None, None, None, None, 0, None) == 1
+    assert L.mla_block_prefill_workspace_bytes(None, 1, 1, 1) == 0
+    assert L.mla_block_decode_workspace_bytes(None, 1, 1) == 0
     assert L.mla_prefill_workspace_bytes(None, 1, 1, 1) == 0
     assert L.mla_decode_workspace_bytes(None, 1, 1) == 0
     assert L.mla_workspace_init(None, 0, None) == 1

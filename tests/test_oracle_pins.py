@@ -351,3 +351,64 @@ def test_w8a8_forward_quantises_projection_inputs():
     assert np.array_equal(a["ckv"], b["ckv"])
     # c_hat in W8A8 is the quantise-dequantise image of the RMSNorm output
     assert np.array_equal(b["c_hat"], fp8.fake_quant_1x128(a["c_hat"]))
+
+
+# ------------------------------------------------------------------------ decoder-block wrapper
+def test_round_bf16_matches_torch_on_float32_values():
+    """The oracle's bf16 rounding against torch's float32 -> bfloat16 cast (round to nearest even)
+    on float32 values, ties included (float64 inputs would see torch round twice)."""
+    import torch
+
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    # exact halfway cases over the normal range (the oracle rounds normal values only)
+    ties = (np.arange(0x0080, 0x7F00, 7, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    v = np.concatenate([v, ties, -ties, np.float32([0.0, 1.0, -2.5])]).astype(np.float64)
+    want = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(mla.round_bf16(v), want)
+
+
+def test_block_residual_when_o_proj_vanishes():
+    """W_o = 0: the attention adds nothing, so the block returns its input exactly."""
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=31, zero=("o",))
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((5, cfg.hidden))
+    g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
+    out = mla.block_attention(x, w, g, cfg)
+    assert np.array_equal(out["h"], x)
+
+
+@pytest.mark.parametrize("c", [4.0, 0.25])
+def test_block_input_norm_scale_invariance(c):
+    """With eps = 0 the RMSNorm output does not depend on the input's scale (and a power-of-two
+    scale leaves every bf16 rounding unchanged), so h(c x) - c x = h(x) - x exactly. Fails if the
+    norm were skipped, applied to the residual, or its output added instead of x."""
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6, eps=0.0)
+    w = tiny_weights(cfg, seed=33)
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((4, cfg.hidden))
+    g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
+    a = mla.block_attention(x, w, g, cfg)["h"] - x
+    b = mla.block_attention(c * x, w, g, cfg)["h"] - c * x
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+
+
+@pytest.mark.parametrize("t_new,l0", [(3, 0), (1, 3)])
+def test_block_brute_force_tiny(t_new, l0):
+    """The block wrapper against the scalar-loop restatement (its own RMSNorm and bf16 rounding)."""
+    cfg = TINY
+    w = tiny_weights(cfg, seed=35)
+    rng = np.random.default_rng(36 + t_new)
+    g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
+    x_prev = rng.standard_normal((l0, cfg.hidden))
+    x = rng.standard_normal((t_new, cfg.hidden))
+    cache = None
+    bcache = None
+    if l0:
+        cache = mla.kv_entries(mla.input_rmsnorm(x_prev, g, cfg.eps), w, 0, cfg)
+        bcache = [(list(cache[0][i]), list(cache[1][i])) for i in range(l0)]
+    out = mla.block_attention(x, w, g, cfg, cache=cache)
+    dims = dict(q_lora=cfg.q_lora, kv_lora=cfg.kv_lora, heads=cfg.heads, nope=cfg.nope, rope=cfg.rope, v=cfg.v)
+    hs, _ = brute.block(x.tolist(), to_lists(w), g.tolist(), dims, cfg.eps, cfg.theta, 1 / math.sqrt(cfg.qk), bcache)
+    assert np.allclose(out["h"], np.array(hs), rtol=0, atol=1e-12)
