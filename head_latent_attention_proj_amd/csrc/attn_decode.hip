@@ -351,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     // decision; every split's first block has a valid position, so mrun is finite after it)
     if (__any(bmax > mrun + 8.0f)) {
       const float mnew = fmaxf(mrun, bmax);
-      const float alpha = exp2f(mrun - mnew);
+      const float alpha = exp2_flush(mrun - mnew);
       lrun *= alpha;
 #pragma unroll
       for (int c = 0; c < 16; ++c) oacc[c] *= alpha;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(sv[kt][e] - mrun);
+        const float p = exp2_flush(sv[kt][e] - mrun);
         sv[kt][e] = p;
         psum += p;
       }
@@ -492,13 +492,22 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   // Every load is issued unconditionally (an index past the block re-reads its last chunk and is
   // not stored): with no branch among them, the compiler's wait counts stay exact and the two
   // register sets really are in flight together.
+  // Row and byte column of each of the thread's chunks are fixed; a load adds the block's row to
+  // a 32-bit offset from the sequence's first slot (the uniform base stays in scalar registers).
+  const uint8_t* seq_base = a.cache + slot0 * BF16_ENTRY_BYTES;
+  int crow[5], ccol[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int c = min(tid + 512 * i, DKB * 72 - 1);
+    crow[i] = c / 72;
+    ccol[i] = (c % 72) * 16;
+  }
   auto gload = [&](int blk, u32x4_t (&rs)[5]) {
     const int kb = c0 + blk * DKB;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-      const int c = min(tid + 512 * i, DKB * 72 - 1);
-      const int key = min(kb + c / 72, c1 - 1);  // rows past the split's end: re-read, masked later
-      rs[i] = ld16(a.cache + (slot0 + key) * BF16_ENTRY_BYTES + (c % 72) * 16);
+      const int key = min(kb + crow[i], c1 - 1);  // rows past the split's end: re-read, masked later
+      rs[i] = ld16(seq_base + (uint32_t)(key * BF16_ENTRY_BYTES + ccol[i]));
     }
   };
   auto sstore = [&](const u32x4_t (&rs)[5]) {
@@ -588,17 +597,18 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     float sv[16];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = xs4[e >> 2][e & 3];
-      v *= sl2;
-      if (kb + 8 * (e >> 2) + 4 * kg + (e & 3) >= c1) v = -INFINITY;
-      sv[e] = v;
-      bmax = fmaxf(bmax, v);
+    for (int e = 0; e < 16; ++e) sv[e] = xs4[e >> 2][e & 3] * sl2;
+    if (kb + DKB > c1) {  // the split's last block is partial (or a masked extra block): mask
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kb + 8 * (e >> 2) + 4 * kg + (e & 3) >= c1) sv[e] = -INFINITY;
     }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, sv[e]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     if (__any(bmax > m_used + 8.0f)) {  // wave-uniform
       const float mn = fmaxf(m_used, bmax);
-      const float al = exp2f(m_used - mn);
+      const float al = exp2_flush(m_used - mn);
       l_run *= al;
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[t] *= al;
@@ -607,7 +617,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      sv[e] = exp2f(sv[e] - m_used);
+      sv[e] = exp2_flush(sv[e] - m_used);
       psum += sv[e];
     }
     l_run += psum;

@@ -276,14 +276,14 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
       const float mnew = fmaxf(mrun[qt], bmax);
-      const float alpha = exp2f(mrun[qt] - mnew);
+      const float alpha = exp2_flush(mrun[qt] - mnew);
       mrun[qt] = mnew;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(sacc[kt][qt][e] - mnew);
+          const float p = exp2_flush(sacc[kt][qt][e] - mnew);
           sacc[kt][qt][e] = p;
           psum += p;
         }

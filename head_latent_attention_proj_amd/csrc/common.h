@@ -70,3 +70,8 @@ MLA_DEV T wave_sum(T v) {
 }
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// 2^x with the hardware's v_exp_f32 alone: exp2f adds a range fix-up (compare, select, scale)
+// so that results below 2^-126 come out as denormals; softmax weights that small add nothing
+// to a float32 sum, so the attention kernels take the flushed value. exp2(-inf) = 0.
+MLA_DEV float exp2_flush(float x) { return __builtin_amdgcn_exp2f(x); }
