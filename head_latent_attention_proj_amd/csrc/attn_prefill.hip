@@ -267,29 +267,42 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = sacc[kt][qt][e] * sl2;
-          if (need_mask && (kb + kt * 16 + g * 4 + e) > qpos[qt]) s = -INFINITY;
-          sacc[kt][qt][e] = s;
-          bmax = fmaxf(bmax, s);
-        }
+        for (int e = 0; e < 4; ++e) sacc[kt][qt][e] *= sl2;
+      if (need_mask) {  // wave-uniform: only blocks that reach past the wave's first query
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kb + kt * 16 + g * 4 + e > qpos[qt]) sacc[kt][qt][e] = -INFINITY;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sacc[kt][qt][e]);
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float mnew = fmaxf(mrun[qt], bmax);
-      const float alpha = exp2_flush(mrun[qt] - mnew);
-      mrun[qt] = mnew;
+      // The running maximum is raised only when some query's block maximum exceeds it by more
+      // than 8 (log2 units; wave-uniform decision): probabilities stay <= 256 and the output
+      // accumulators are rescaled rarely. The first block holds key 0, visible to every query,
+      // so mrun is finite after it.
+      if (__any(bmax > mrun[qt] + 8.0f)) {
+        const float mnew = fmaxf(mrun[qt], bmax);
+        const float alpha = exp2_flush(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        lrun[qt] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) oacc[d][qt] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2_flush(sacc[kt][qt][e] - mnew);
+          const float p = exp2_flush(sacc[kt][qt][e] - mrun[qt]);
           sacc[kt][qt][e] = p;
           psum += p;
         }
-      lrun[qt] = lrun[qt] * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) oacc[d][qt] *= alpha;
+      lrun[qt] += psum;
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
         u32x4_t w;
