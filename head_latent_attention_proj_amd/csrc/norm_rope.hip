@@ -203,34 +203,60 @@ __global__ void copy_append_kernel(uint8_t* dst, const uint8_t* src, int64_t nve
 }
 
 // One wave per 128-feature group of one row.
+// Dynamic FP8 activation quantiser: per row and aligned group of 128 features, s = amax / 448
+// (1 when the group is all zero) and code = RNE-saturating e4m3 of v / s, both in IEEE float32.
+// 16 lanes per group, 8 consecutive features per lane (one 16- or 32-byte load per operand, one
+// 8-byte store of codes), 4 groups per wave; the group maximum is exact whatever the reduction
+// order, so the codes do not depend on the layout.
 template <typename T>
-__global__ void quantize_rows_kernel(const T* x, const T* x2, int64_t ldx, int rows, int K, uint8_t* codes,
-                                     float* scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* x, const T* x2, int64_t ldx, int rows, int K,
+                                                            uint8_t* codes, float* scales) {
+  const int l16 = threadIdx.x & 15;
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int groups = K / 128;
-  if (gid >= (int64_t)rows * groups) return;
+  if (gid >= (int64_t)rows * groups) return;  // whole 16-lane groups leave together
   const int r = (int)(gid / groups), gi = (int)(gid % groups);
-  const T* src = x + r * ldx + gi * 128;
-  float v0, v1;
+  const int64_t off = (int64_t)r * ldx + gi * 128 + l16 * 8;
+  float v[8];
   if constexpr (sizeof(T) == 2) {
-    v0 = bf2f(src[lane]);
-    v1 = bf2f(src[lane + 64]);
+    const u32x4_t raw = ld16(x + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf_lo(raw[j]);
+      v[2 * j + 1] = bf_hi(raw[j]);
+    }
   } else {
-    v0 = src[lane];
-    v1 = src[lane + 64];
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(x + off);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(x + off + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
     if (x2) {
-      const T* s2 = x2 + r * ldx + gi * 128;
-      v0 += s2[lane];
-      v1 += s2[lane + 64];
+      const f32x4_t c = *reinterpret_cast<const f32x4_t*>(x2 + off);
+      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(x2 + off + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] += c[j];
+        v[4 + j] += d[j];
+      }
     }
   }
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
-  uint8_t* dst = codes + (int64_t)r * K + gi * 128;
-  dst[lane] = (uint8_t)e4m3_rne_sat(v0 / sc);
-  dst[lane + 64] = (uint8_t)e4m3_rne_sat(v1 / sc);
-  if (lane == 0) scales[(int64_t)r * groups + gi] = sc;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= e4m3_rne_sat(v[j] / sc) << (8 * j);
+    hi |= e4m3_rne_sat(v[4 + j] / sc) << (8 * j);
+  }
+  *reinterpret_cast<u32x2_t*>(codes + (int64_t)r * K + gi * 128 + l16 * 8) = u32x2_t{lo, hi};
+  if (l16 == 0) scales[(int64_t)r * groups + gi] = sc;
 }
 
 // one thread per q_nope feature (n * 64 * 128 of them)
@@ -326,7 +352,7 @@ hipError_t quantize_rows_f32(const float* x, const float* x2, int64_t ldx, int r
                              float* scales, hipStream_t s) {
   const int64_t waves = (int64_t)rows * (K / 128);
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, x2, ldx,
+  hipLaunchKernelGGL(quantize_rows_kernel<float>, dim3((unsigned)((waves + 15) / 16)), dim3(256), 0, s, x, x2, ldx,
                      rows, K, codes, scales);
   return hipGetLastError();
 }
@@ -335,7 +361,7 @@ hipError_t quantize_rows_bf16(const uint16_t* x, int64_t ldx, int rows, int K, u
                               hipStream_t s) {
   const int64_t waves = (int64_t)rows * (K / 128);
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x,
+  hipLaunchKernelGGL(quantize_rows_kernel<uint16_t>, dim3((unsigned)((waves + 15) / 16)), dim3(256), 0, s, x,
                      (const uint16_t*)nullptr, ldx, rows, K, codes, scales);
   return hipGetLastError();
 }
