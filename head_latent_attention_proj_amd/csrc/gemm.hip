@@ -9,7 +9,7 @@
 //   * gemm_tile   -- prefill-sized M: BM x BN workgroup tile staged through LDS (double
 //                    buffered, padded rows so 16-byte fragment reads are bank-conflict free),
 //                    16x16x32 bf16 MFMA, XCD-aware grouped tile order. Optional split-K.
-//   * gemm_skinny -- 16 < M <= 64 with K >= 1024: a ring of LDS stages filled by direct-to-LDS
+//   * gemm_skinny -- 16 < M <= 64 with K >= 512: a ring of LDS stages filled by direct-to-LDS
 //                    loads in MFMA operand order, several stages in flight per workgroup.
 //   * gemm_wsplit -- other decode-sized M (<= 64): operands go straight from global memory into
 //                    MFMA fragments; the K range of a 16*NT-column tile is split across the waves
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(512) void gemm_head_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// 16 < M <= 64 with long K: a ring of LDS stages filled by direct-to-LDS loads
+// 16 < M <= 64 with K >= 512: a ring of LDS stages filled by direct-to-LDS loads
 // ------------------------------------------------------------------------------------------
 // Workgroup = NW waves = 16*NW output columns over one K split. A stage covers 64 features: the
 // A tile (16*MT rows as 2*MT fragment blocks of 16 rows x 32 features, fetched by the waves in
@@ -703,7 +703,7 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
   // runs best with 128-column tiles and K split to about two workgroups per CU (40 us; the
   // 128 x 128 tile kernel 44 us), q_b (K = 1536) and kv_b-sized products with 64-column tiles
   // and no split (21.5 us against 25), q_a | kv_a with 64-column tiles and 4 splits.
-  if (M > 16 && M <= 64 && batch == 1 && K >= 1024) {
+  if (M > 16 && M <= 64 && batch == 1 && K >= 512) {
     pl.kind = 5;
     pl.mt = M <= 32 ? 2 : 4;
     pl.nw = (pl.mt == 4 && (int64_t)N * K >= ((int64_t)32 << 20)) ? 8 : 4;

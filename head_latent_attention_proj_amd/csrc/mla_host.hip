@@ -530,11 +530,13 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   set_a(ctx, g, x, HIDDEN, w + L.x8, (const float*)(w + L.x8s), HIDDEN / 128);
   g.B = ctx->w_qkva; g.ldb = HIDDEN; g.b_scale = ctx->s_qkva; g.bs_ld = HIDDEN / 128;
   g.C = w + L.cqkv; g.ldc = QKVA_N; g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
-  g.tag = mla_k::TAG_QKVA;
+  g.tag = mla_k::TAG_QKVA; g.ysplit_max = QKVA_PARTS; g.c_split_stride = (int64_t)ntok * QKVA_N;
+  const int qkva_parts = proj_ysplit(ctx, g);  // > 1 only at short prefills: the norm kernel adds them
   HIP_TRY(run_proj(ctx, g, s));
   // 2. RMSNorms, RoPE of the shared key, latent entries into the cache (FP8: quantised q_hat, c_hat)
   mla_k::NormArgs na{};
-  na.cqkv = (const float*)(w + L.cqkv); na.n_part = 1; na.g_q = ctx->g_q; na.g_kv = ctx->g_kv;
+  na.cqkv = (const float*)(w + L.cqkv); na.n_part = qkva_parts; na.part_stride = (int64_t)ntok * QKVA_N;
+  na.g_q = ctx->g_q; na.g_kv = ctx->g_kv;
   na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = ntok; na.meta = meta; na.B = B;
