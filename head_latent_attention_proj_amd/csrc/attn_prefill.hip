@@ -115,23 +115,28 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
   u32x4_t pk[4], pp[2], pv[4];
   const int kr = tid >> 4, kc = (tid & 15) * 8;   // K_nope: 16 threads per key row (256 B)
   const int pr = tid >> 3, pc = (tid & 7) * 8;    // k_pe / V^T: 8 threads per 128-byte row
+  // Bases common to the workgroup (scalar registers) plus 32-bit per-lane byte offsets: a load
+  // costs one address register and a 32-bit add instead of a 64-bit multiply-add per block.
+  const uint8_t* kn_base = (const uint8_t*)(a.knope + ((int64_t)m.kbase * 64 + h) * 128);
+  const uint8_t* pe_base = a.cache + m.slot0 * a.entry_bytes + a.kpe_off;
+  const uint8_t* vt_base = (const uint8_t*)(a.vt + (int64_t)(h * 128) * a.vt_ld + m.kbase);
   auto gload = [&](int blk) {
     if constexpr (SPLIT) return;  // split staging loads and stores in one step (stage_split)
     const int kb = blk * PKB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = min(kb + i * 16 + kr, n_keys - 1);
-      pk[i] = ld16(a.knope + ((int64_t)(m.kbase + key) * 64 + h) * 128 + kc);
+      const uint32_t key = (uint32_t)min(kb + i * 16 + kr, n_keys - 1);
+      pk[i] = ld16(kn_base + (key * (64u * 128u * 2u) + (uint32_t)kc * 2u));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = min(kb + i * 32 + pr, n_keys - 1);
-      pp[i] = ld16(a.cache + (m.slot0 + key) * a.entry_bytes + a.kpe_off + pc * 2);
+      const uint32_t key = (uint32_t)min(kb + i * 32 + pr, n_keys - 1);
+      pp[i] = ld16(pe_base + (key * (uint32_t)a.entry_bytes + (uint32_t)pc * 2u));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = i * 32 + pr;
-      pv[i] = ld16(a.vt + (int64_t)(h * 128 + row) * a.vt_ld + m.kbase + kb + pc);
+      const uint32_t row = (uint32_t)(i * 32 + pr);
+      pv[i] = ld16(vt_base + (row * (uint32_t)a.vt_ld + (uint32_t)(kb + pc)) * 2u);
     }
     if (kb + PKB > n_keys) {  // value rows past the last key are not written: zero them
 #pragma unroll
