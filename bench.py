@@ -19,6 +19,7 @@ on its own with HIP events on its stream; `cpu_baseline` is the float64 oracle's
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -157,7 +158,21 @@ def main():
     achieved = oproj_bytes / (oproj_ms * 1e-3) / 1e9
     traffic = counted_traffic()
 
-    extra = {"block_decode_B1": {
+    # latent cache of the whole 61-layer stack in one pool (host-side layout plan): bytes per position
+    pool_bytes = {}
+    for name, wd in (("bf16", binding.WDTYPE_BF16), ("fp8", binding.WDTYPE_FP8)):
+        cfg = binding.make_config(wdtype=wd)
+        caps = np.array([1], dtype=np.int32)
+        off = np.zeros(1, dtype=np.int64)
+        tot, lb, pb = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
+        binding.check(binding.lib().mla_cache_pool_plan(ctypes.byref(cfg), 61, 1, caps.ctypes.data, 1,
+                                                         off.ctypes.data, ctypes.byref(tot), ctypes.byref(lb),
+                                                         ctypes.byref(pb)))
+        pool_bytes[name] = pb.value
+    extra = {"cache_pool_61_layers": {
+        "bytes_per_position_bf16": pool_bytes["bf16"], "bytes_per_position_fp8": pool_bytes["fp8"],
+        "note": "mla_cache_pool_plan over 61 layers, one position; the rebuilt keys and values would take 2,498,560 B"},
+        "block_decode_B1": {
         "us_per_step": round(t_blk * 1e6, 3),
         "note": "decoder-block attention half h = x + MLA(RMSNorm(x)): input-norm kernel, the decode step, "
                 "residual fused into o_proj; positions 1000+ on the headline caches"}}

@@ -23,6 +23,7 @@ EXPORTED = (
     "mla_decode_workspace_bytes", "mla_workspace_init", "mla_init_weights", "mla_prefill", "mla_decode",
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
     "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
+    "mla_cache_pool_plan", "mla_cache_pool_layer",
     "mla_test_gemm_workspace_bytes", "mla_test_gemm",
 )
 STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6}
@@ -89,6 +90,11 @@ def lib() -> ctypes.CDLL:
     L.mla_block_prefill.restype = ctypes.c_int
     L.mla_block_decode.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp, vp, sz, vp]
     L.mla_block_decode.restype = ctypes.c_int
+    L.mla_cache_pool_plan.argtypes = [ctypes.POINTER(MlaConfig), i32, i32, vp, i32, vp, ctypes.POINTER(i64),
+                                      ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.mla_cache_pool_plan.restype = ctypes.c_int
+    L.mla_cache_pool_layer.argtypes = [vp, sz, sz, i32, ctypes.POINTER(MlaCacheDesc)]
+    L.mla_cache_pool_layer.restype = ctypes.c_int
     L.mla_cache_append.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), i32, vp, i32, vp]
     L.mla_cache_append.restype = ctypes.c_int
     L.mla_destroy.argtypes = [vp]
@@ -162,6 +168,49 @@ class Cache:
         """View of sequence `seq`'s used slots as [len, entry_bytes] uint8."""
         o, n = int(self.offset_h[seq]), int(self.len_h[seq])
         return self.data.view(-1, self.entry_bytes)[o:o + n]
+
+
+class CachePool:
+    """One device buffer holding the latent caches of a stack of layers (mla_cache_pool_plan): every
+    layer shares the slot layout (offsets, capacities); each layer keeps its own lengths.
+    `layer(l)` is layer l's cache, used like a Cache."""
+
+    def __init__(self, cfg: MlaConfig, n_layers: int, caps, align: int = 16, device="cuda", fill_byte: int | None = None):
+        import torch
+
+        caps = np.ascontiguousarray(caps, dtype=np.int32)
+        self.cap_h = caps
+        self.offset_h = np.zeros(len(caps), dtype=np.int64)
+        total, lb, pb = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
+        check(lib().mla_cache_pool_plan(ctypes.byref(cfg), n_layers, len(caps), caps.ctypes.data, align,
+                                        self.offset_h.ctypes.data, ctypes.byref(total), ctypes.byref(lb),
+                                        ctypes.byref(pb)))
+        self.total_slots, self.layer_bytes, self.pool_bytes = total.value, lb.value, pb.value
+        self.entry_bytes = lib().mla_cache_entry_bytes(ctypes.byref(cfg))
+        self.pool = torch.empty(self.pool_bytes, dtype=torch.uint8, device=device)
+        if fill_byte is not None:
+            self.pool.fill_(fill_byte)
+        self.offset_d = torch.from_numpy(self.offset_h).to(device)
+        self._layers = [_PoolLayerCache(self, l, device) for l in range(n_layers)]
+
+    def layer(self, l: int) -> "Cache":
+        return self._layers[l]
+
+
+class _PoolLayerCache(Cache):
+    """Layer l's view of a CachePool (same interface as Cache)."""
+
+    def __init__(self, pool: CachePool, l: int, device):
+        import torch
+
+        self.offset_h, self.offset_d, self.cap_h = pool.offset_h, pool.offset_d, pool.cap_h
+        self.len_h = np.zeros(len(pool.cap_h), dtype=np.int32)
+        self.len_d = torch.zeros(len(pool.cap_h), dtype=torch.int32, device=device)
+        self.total_slots, self.entry_bytes = pool.total_slots, pool.entry_bytes
+        self._desc = MlaCacheDesc(None, self.offset_h.ctypes.data, self.offset_d.data_ptr(), self.len_h.ctypes.data,
+                                  self.len_d.data_ptr(), self.cap_h.ctypes.data, len(pool.cap_h), pool.total_slots)
+        check(lib().mla_cache_pool_layer(_ptr(pool.pool), pool.pool_bytes, pool.layer_bytes, l, ctypes.byref(self._desc)))
+        self.data = pool.pool[l * pool.layer_bytes:(l + 1) * pool.layer_bytes]
 
 
 class Layer:

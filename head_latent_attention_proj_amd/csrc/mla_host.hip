@@ -735,6 +735,47 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
   return decode_impl(ctx, cache, seq_ids_h, seq_ids_d, B, x, y, ws, ws_bytes, stream, nullptr);
 }
 
+mla_status mla_cache_pool_plan(const mla_config* cfg, int32_t n_layers, int32_t n_seqs, const int32_t* cap_h,
+                               int32_t align, int64_t* offset_h, int64_t* total_slots, size_t* layer_bytes,
+                               size_t* pool_bytes) {
+  if (!cfg) return fail(MLA_E_ARG, "cfg is NULL");
+  const mla_status st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  if (!cap_h || !offset_h || !total_slots || !layer_bytes || !pool_bytes) return fail(MLA_E_ARG, "a pointer argument is NULL");
+  if (n_layers <= 0 || n_seqs <= 0) return fail(MLA_E_ARG, "n_layers and n_seqs must be positive");
+  if (align < 1 || align > 4096) return fail(MLA_E_ARG, "align %d outside [1, 4096]", align);
+  int64_t slots = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (cap_h[s] < 0) return fail(MLA_E_ARG, "capacity of sequence %d is negative", s);
+    if (cap_h[s] > cfg->max_positions)
+      return fail(MLA_E_CAPACITY, "capacity %d of sequence %d exceeds max_positions %d", cap_h[s], s, cfg->max_positions);
+    slots += ((int64_t)cap_h[s] + align - 1) / align * align;
+  }
+  if (slots == 0) return fail(MLA_E_ARG, "the pool would hold no slots");
+  const uint64_t lb = (uint64_t)slots * mla_cache_entry_bytes(cfg);
+  if (lb > UINT64_MAX / (uint64_t)n_layers) return fail(MLA_E_ARG, "pool size overflows");
+  int64_t off = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    offset_h[s] = off;
+    off += ((int64_t)cap_h[s] + align - 1) / align * align;
+  }
+  *total_slots = slots;
+  *layer_bytes = (size_t)lb;
+  *pool_bytes = (size_t)(lb * (uint64_t)n_layers);
+  return MLA_OK;
+}
+
+mla_status mla_cache_pool_layer(void* pool, size_t pool_bytes, size_t layer_bytes, int32_t layer, mla_cache* cache) {
+  if (!pool || !cache) return fail(MLA_E_ARG, "pool or cache is NULL");
+  if (layer < 0 || layer_bytes == 0) return fail(MLA_E_ARG, "layer %d or layer_bytes %zu invalid", layer, layer_bytes);
+  if (layer_bytes % 16) return fail(MLA_E_ALIGN, "layer_bytes %zu is not a multiple of 16", layer_bytes);
+  if ((uint64_t)layer_bytes * (uint64_t)(layer + 1) > (uint64_t)pool_bytes)
+    return fail(MLA_E_ARG, "layer %d ends past the pool's %zu bytes", layer, pool_bytes);
+  if (!aligned16(pool)) return fail(MLA_E_ALIGN, "pool is not 16-byte aligned");
+  cache->data = (uint8_t*)pool + (size_t)layer * layer_bytes;
+  return MLA_OK;
+}
+
 size_t mla_block_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32_t max_batch, int64_t max_keys) {
   const size_t n = mla_prefill_workspace_bytes(ctx, max_tokens, max_batch, max_keys);
   return n ? n + block_xn_bytes(max_tokens) : 0;

@@ -196,6 +196,30 @@ mla_status mla_block_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_i
                             int32_t B, const void* norm_weight, const void* x, void* h, void* ws, size_t ws_bytes,
                             mla_stream stream);
 
+/* ---- One cache buffer for a stack of layers. The dense-block attention page ("In numbers") prices
+ * the model's cache per position over its 61 layers: 2,498,560 B for rebuilt keys and values
+ * against 70,272 B (61 x 1,152) for the latent form used here. A pool is one caller-owned device
+ * buffer holding n_layers layer caches with one shared slot layout: sequence s owns slots
+ * offset[s] .. offset[s] + cap[s] - 1 in every layer (each sequence's run rounded up to `align`
+ * slots), and layer l's slots start at byte l * layer_bytes of the pool, so a position costs
+ * n_layers * mla_cache_entry_bytes(cfg) bytes.
+ *
+ * mla_cache_pool_plan: host-only. cap_h [n_seqs] positions per sequence (0 .. max_positions),
+ * align 1 .. 4096; writes offset_h [n_seqs] (caller-allocated), *total_slots (slots per layer),
+ * *layer_bytes (= total_slots * entry bytes, a multiple of 16) and *pool_bytes
+ * (= n_layers * layer_bytes). Errors: MLA_E_ARG (NULL, sizes), MLA_E_CAPACITY (a cap above
+ * max_positions), the config's own status. */
+mla_status mla_cache_pool_plan(const mla_config* cfg, int32_t n_layers, int32_t n_seqs, const int32_t* cap_h,
+                               int32_t align, int64_t* offset_h, int64_t* total_slots, size_t* layer_bytes,
+                               size_t* pool_bytes);
+
+/* Point cache->data at layer `layer` of a pool of pool_bytes planned with layer_bytes per layer
+ * (pool + layer * layer_bytes), after checking that the layer lies inside the pool and is 16-byte
+ * aligned. The caller fills the rest of the descriptor: offsets, capacities, n_seqs and
+ * total_slots from the plan (shared by all layers) and the layer's own len_h / len_d. Host-only;
+ * on an error *cache is unchanged. */
+mla_status mla_cache_pool_layer(void* pool, size_t pool_bytes, size_t layer_bytes, int32_t layer, mla_cache* cache);
+
 /* Append n ready-made entries (device, n * mla_cache_entry_bytes bytes, the slot format above)
  * to sequence seq_id at positions len .. len+n-1: a byte copy into the slots, then len += n.
  * Used to load a cache produced elsewhere (for example from a saved state). */

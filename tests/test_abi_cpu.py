@@ -87,3 +87,55 @@ def test_calls_reject_null_context(L):
     assert L.mla_decode_workspace_bytes(None, 1, 1) == 0
     assert L.mla_workspace_init(None, 0, None) == 1
     L.mla_destroy(None)
+
+
+def test_cache_pool_plan_matches_page_bytes(L):
+    """A 61-layer pool costs 70,272 B per position in bf16, the latent cache figure printed on the
+    dense-block attention page ("In numbers", tests/golden/page_facts.json), and 61 x 784 in the FP8
+    slot format; offsets are aligned runs per sequence."""
+    import json
+
+    import numpy as np
+
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))["cache_bytes_per_token_61_layers"]
+    n = facts["layers"]
+    for wdtype, per_layer in ((binding.WDTYPE_BF16, facts["latent_bf16"] // n), (binding.WDTYPE_FP8, 784)):
+        cfg = binding.make_config(wdtype=wdtype)
+        caps = np.array([1], dtype=np.int32)
+        off = np.zeros(1, dtype=np.int64)
+        total, lb, pb = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert L.mla_cache_pool_plan(ctypes.byref(cfg), n, 1, caps.ctypes.data, 1, off.ctypes.data,
+                                     ctypes.byref(total), ctypes.byref(lb), ctypes.byref(pb)) == 0
+        assert (total.value, lb.value, pb.value) == (1, per_layer, n * per_layer)
+    assert n * 1152 == facts["latent_bf16"]
+    cfg = binding.make_config()
+    caps = np.array([5, 0, 17, 16], dtype=np.int32)
+    off = np.zeros(4, dtype=np.int64)
+    total, lb, pb = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.mla_cache_pool_plan(ctypes.byref(cfg), 3, 4, caps.ctypes.data, 16, off.ctypes.data,
+                                 ctypes.byref(total), ctypes.byref(lb), ctypes.byref(pb)) == 0
+    assert off.tolist() == [0, 16, 16, 48] and total.value == 64
+    assert lb.value == 64 * 1152 and pb.value == 3 * 64 * 1152
+
+
+def test_cache_pool_rejects_bad_arguments(L):
+    import numpy as np
+
+    cfg = binding.make_config(max_positions=4096)
+    off = np.zeros(2, dtype=np.int64)
+    total, lb, pb = ctypes.c_int64(), ctypes.c_size_t(), ctypes.c_size_t()
+    args = lambda caps, n_layers=2, align=16: (ctypes.byref(cfg), n_layers, len(caps), caps.ctypes.data, align,
+                                              off.ctypes.data, ctypes.byref(total), ctypes.byref(lb), ctypes.byref(pb))
+    assert L.mla_cache_pool_plan(*args(np.array([8, 5000], dtype=np.int32))) == 3  # MLA_E_CAPACITY
+    assert L.mla_cache_pool_plan(*args(np.array([8, -1], dtype=np.int32))) == 1
+    assert L.mla_cache_pool_plan(*args(np.array([0, 0], dtype=np.int32))) == 1
+    assert L.mla_cache_pool_plan(*args(np.array([8, 8], dtype=np.int32), n_layers=0)) == 1
+    assert L.mla_cache_pool_plan(*args(np.array([8, 8], dtype=np.int32), align=0)) == 1
+    desc = binding.MlaCacheDesc()
+    buf = ctypes.create_string_buffer(4096 + 16)
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1152, 3, ctypes.byref(desc)) == 1  # past the end
+    assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1000, 0, ctypes.byref(desc)) == 7  # MLA_E_ALIGN
+    assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1152, 2, None) == 1
+    assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1152, 1, ctypes.byref(desc)) == 0
+    assert desc.data == base + 1152
