@@ -287,6 +287,37 @@ def main():
         }
         del cp8, lf
 
+    # achievable peaks on this GPU, for context next to the published ones: a plain 1 GiB device copy
+    # (bytes read + written per second) and a library bf16 GEMM (hipBLASLt through torch.matmul, 8192^3)
+    if not args.no_extra:
+        log("timing achievable peaks")
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        a_ = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        b_ = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a_, b_)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a_, b_)
+        e1.record()
+        torch.cuda.synchronize()
+        mm_tfs = 2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del a_, b_
+        extra["achievable_peaks"] = {
+            "device_copy_GBps": round(copy_gbs, 1), "hipblaslt_bf16_gemm_8192_TFps": round(mm_tfs, 1),
+            "note": "measured here for context; roofline fractions use the published 8 TB/s and 2.5 PF/s"}
+
     # a plain 64 MiB device copy: the reference point that scales rocprofv3's FETCH_SIZE / WRITE_SIZE
     # counters to bytes (its algorithmic traffic is exactly 64 MiB read + 64 MiB written)
     cp_src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
