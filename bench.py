@@ -185,12 +185,14 @@ def main():
             yb = torch.empty_like(xb)
             sid = np.zeros(1, dtype=np.int32)
             qs = np.array([0, T], dtype=np.int32)
+            sid_dev = torch.from_numpy(sid).cuda()
+            qs_dev = torch.from_numpy(qs).cuda()
 
-            def prefill_step(i, T=T, xb=xb, pc=pc, yb=yb, sid=sid, qs=qs):
+            def prefill_step(i, T=T, xb=xb, pc=pc, yb=yb, sid=sid, qs=qs, sid_dev=sid_dev, qs_dev=qs_dev):
                 c = i % args.copies
                 pc[c].len_h[0] = 0
                 pc[c].len_d.zero_()
-                layers[c].prefill(pc[c], sid, qs, xb, y=yb)
+                layers[c].prefill(pc[c], sid, qs, xb, y=yb, seq_ids_d=sid_dev, q_start_d=qs_dev)
 
             t = timed_loop(torch, prefill_step, steps, 2)
             fl = prefill_flops(T)
@@ -273,10 +275,13 @@ def main():
         qs8 = np.arange(5, dtype=np.int32) * T8
         sids = np.arange(4, dtype=np.int32)
 
+        sids_dev = torch.from_numpy(np.ascontiguousarray(sids, dtype=np.int32)).cuda()
+        qs8_dev = torch.from_numpy(np.ascontiguousarray(qs8, dtype=np.int32)).cuda()
+
         def pre8(i):
             cp8.len_h[:] = 0
             cp8.len_d.zero_()
-            lf.prefill(cp8, sids, qs8, xp8, y=yp8)
+            lf.prefill(cp8, sids, qs8, xp8, y=yp8, seq_ids_d=sids_dev, q_start_d=qs8_dev)
 
         t = timed_loop(torch, pre8, 3, 1)
         fl = 4 * prefill_flops(T8)

@@ -264,8 +264,9 @@ class Layer:
     def decode_workspace_bytes(self, max_batch: int, max_keys: int) -> int:
         return lib().mla_decode_workspace_bytes(self.ctx, max_batch, max_keys)
 
-    def prefill(self, cache: Cache, seq_ids, q_start, x, y=None, stream=None):
-        """x: [sum T, 7168] bf16 cuda; q_start: B+1 row offsets. Returns y [sum T, 7168] bf16."""
+    def prefill(self, cache: Cache, seq_ids, q_start, x, y=None, seq_ids_d=None, q_start_d=None, stream=None):
+        """x: [sum T, 7168] bf16 cuda; q_start: B+1 row offsets. Returns y [sum T, 7168] bf16.
+        seq_ids_d / q_start_d: optional device copies of seq_ids / q_start (int32), made here if absent."""
         import torch
 
         seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
@@ -275,8 +276,8 @@ class Layer:
         ws = self.workspace(self.prefill_workspace_bytes(int(q_start[-1]), B, keys), stream)
         if y is None:
             y = torch.empty_like(x)
-        sid_d = torch.from_numpy(seq_ids).to(x.device)
-        qs_d = torch.from_numpy(q_start).to(x.device)
+        sid_d = seq_ids_d if seq_ids_d is not None else torch.from_numpy(seq_ids).to(x.device)
+        qs_d = q_start_d if q_start_d is not None else torch.from_numpy(q_start).to(x.device)
         check(lib().mla_prefill(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(sid_d),
                                 q_start.ctypes.data, _ptr(qs_d), B, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
                                 _stream(stream)))
