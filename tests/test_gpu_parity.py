@@ -33,7 +33,7 @@ def run_prefill(torch, L, lens_t, seed, caps=None, fill_byte=None):
     return cache, q_start, xbits, y
 
 
-@pytest.mark.parametrize("lens_t", [[64], [200], [77, 130, 1]])
+@pytest.mark.parametrize("lens_t", [[64], [200], [77, 130, 1], [24], [20, 13]])
 def test_prefill_matches_oracle(torch_cuda, lens_t):
     log(f"prefill lens={lens_t}")
     L = layer()
@@ -118,6 +118,36 @@ def test_decode_varlen_batch(torch_cuda):
         assert_close(y[b:b + 1], ref["y"], f"seq {s} (L={lens[s]})")
     assert list(cache.len_h) == [n + 1 for n in lens]
     assert list(cache.len_d.cpu().numpy()) == [n + 1 for n in lens]
+
+
+@pytest.mark.parametrize("B", [24, 40])
+def test_decode_mid_batch(torch_cuda, B):
+    """Decode at 17..64 sequences (the LDS-ring projections, their K-split parts and reduction, the
+    per-head absorb and W_UV products), cached lengths 0..600 in a shuffled batch order."""
+    rng = np.random.default_rng(3100 + B)
+    lens = [int(v) for v in rng.integers(0, 601, size=B)]
+    lens[0] = 0
+    log(f"decode mid batch B={B}")
+    L = layer()
+    _, w64 = weights()
+    cache = binding.Cache(L, [n + 1 for n in lens])
+    ents = {}
+    for s, n in enumerate(lens):
+        if n:
+            ents[s] = synth.make_cache_entries(n, seed=3200 + s)
+            L.cache_append(cache, s, binding.bf16_tensor(ents[s]))
+    order = rng.permutation(B).astype(np.int32)
+    xn = synth.make_hidden(B, seed=3300 + B)
+    y = y_of(L.decode(cache, order, binding.bf16_tensor(xn)))
+    torch_cuda.cuda.synchronize()
+    for b, s in enumerate(order):
+        kw = {}
+        if lens[s]:
+            e = synth.bf16_bits_to_f64(ents[s])
+            kw = dict(cache=(e[:, :512], e[:, 512:]))
+        ref = omla.forward(synth.bf16_bits_to_f64(xn[b:b + 1]), w64, **kw)
+        assert_close(y[b:b + 1], ref["y"], f"row {b} seq {s} (L={lens[s]})")
+    assert list(cache.len_h) == [n + 1 for n in lens]
 
 
 @pytest.mark.parametrize("lens", [[700, 0], [64, 1, 1500], [33, 2000, 65, 129]])
