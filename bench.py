@@ -178,7 +178,7 @@ def main():
                 "residual fused into o_proj; positions 1000+ on the headline caches"}}
     if not args.no_extra:
         # ---------------- prefill T=64 and T=8192
-        for T, steps in ((64, 30), (8192, 5)):
+        for T, steps, warm in ((64, 30, 5), (8192, 10, 5)):
             log(f"timing prefill T={T}")
             xb = binding.bf16_tensor(synth.make_hidden(T, seed=1003))
             pc = [binding.Cache(L, [T]) for L in layers]
@@ -194,7 +194,7 @@ def main():
                 pc[c].len_d.zero_()
                 layers[c].prefill(pc[c], sid, qs, xb, y=yb, seq_ids_d=sid_dev, q_start_d=qs_dev)
 
-            t = timed_loop(torch, prefill_step, steps, 2)
+            t = timed_loop(torch, prefill_step, steps, warm)
             fl = prefill_flops(T)
             extra[f"prefill_T{T}"] = {
                 "ms": round(t * 1e3, 4), "tokens_per_s": round(T / t, 1),

@@ -339,13 +339,14 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = sv[kt][e] * sl2;
+        float s = sv[kt][e];  // unscaled: the scale is applied in the exponent's fma
         if (kb + kt * 16 + g * 4 + e >= c1) s = -INFINITY;
         sv[kt][e] = s;
         bmax = fmaxf(bmax, s);
       }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax *= sl2;  // the scale (positive) commutes with the maximum
     // the running maximum is raised only when a block's maximum exceeds it by more than 8 (log2
     // units): probabilities stay <= 256 and the accumulators are rescaled rarely (wave-uniform
     // decision; every split's first block has a valid position, so mrun is finite after it)
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2_flush(sv[kt][e] - mrun);
+        const float p = exp2_flush(fmaf(sv[kt][e], sl2, -mrun));
         sv[kt][e] = p;
         psum += p;
       }
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     float sv[16];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = xs4[e >> 2][e & 3] * sl2;
+    for (int e = 0; e < 16; ++e) sv[e] = xs4[e >> 2][e & 3];  // unscaled: see the exponent below
     if (kb + DKB > c1) {  // the split's last block is partial (or a masked extra block): mask
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -606,6 +607,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
 #pragma unroll
     for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, sv[e]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax *= sl2;  // the scale (positive) commutes with the maximum; exponents take it in a fma
     if (__any(bmax > m_used + 8.0f)) {  // wave-uniform
       const float mn = fmaxf(m_used, bmax);
       const float al = exp2_flush(m_used - mn);
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      sv[e] = exp2_flush(sv[e] - m_used);
+      sv[e] = exp2_flush(fmaf(sv[e], sl2, -m_used));
       psum += sv[e];
     }
     l_run += psum;

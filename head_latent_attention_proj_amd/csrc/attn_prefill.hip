@@ -268,11 +268,9 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
     bf16x8_t pf[2][2], pl[SPLIT ? 2 : 1][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
+      // scores stay unscaled here: the scale (softmax scale times log2 e, positive) commutes with
+      // the maximum and is applied inside each exponent's fused multiply-add
       float bmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[kt][qt][e] *= sl2;
       if (need_mask) {  // wave-uniform: only blocks that reach past the wave's first query
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -286,6 +284,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
         for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sacc[kt][qt][e]);
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      bmax *= sl2;
       // The running maximum is raised only when some query's block maximum exceeds it by more
       // than 8 (log2 units; wave-uniform decision): probabilities stay <= 256 and the output
       // accumulators are rescaled rarely. The first block holds key 0, visible to every query,
@@ -303,7 +302,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2_flush(sacc[kt][qt][e] - mrun[qt]);
+          const float p = exp2_flush(fmaf(sacc[kt][qt][e], sl2, -mrun[qt]));
           sacc[kt][qt][e] = p;
           psum += p;
         }
