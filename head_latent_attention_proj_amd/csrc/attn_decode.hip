@@ -673,12 +673,21 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // wave w: heads 8w .. 8w+7, lane = 16-byte piece of the half row
+    for (int i = 0; i < 8; ++i) {  // wave w: heads 8w .. 8w+7, lane = 4 features of the half row
       const int hh = wave * 8 + i;
-      *reinterpret_cast<f32x4_t*>(a.part_o + (prow + hh) * KV_LORA + 256 * half + 4 * lane) =
-          *reinterpret_cast<const f32x4_t*>(st + hh * ST_LD + 4 * lane);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + hh * ST_LD + 4 * lane);
+      *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.part_o) + (prow + hh) * KV_LORA + 256 * half + 4 * lane) =
+          u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
+}
+
+// Eight consecutive bf16 split-partial features (bf16 path: the attention kernel stores its
+// unnormalised partial outputs in bf16) as two float32 quads.
+MLA_DEV void load_part_bf16(const float* part, int64_t idx, f32x4_t& v0, f32x4_t& v1) {
+  const u32x4_t raw = ld16(reinterpret_cast<const uint16_t*>(part) + idx);
+  v0 = f32x4_t{bf_lo(raw[0]), bf_hi(raw[0]), bf_lo(raw[1]), bf_hi(raw[1])};
+  v1 = f32x4_t{bf_lo(raw[2]), bf_hi(raw[2]), bf_lo(raw[3]), bf_hi(raw[3])};
 }
 
 // Merge of the splits, float32. One workgroup per (head h, sequence b): 4 groups of 64 threads
@@ -710,8 +719,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
       const int sp = min(s0 + 4 * u, ns - 1);  // past the end: re-read (not used)
       const int64_t p = base + (int64_t)sp * 64;
       ml[u] = *reinterpret_cast<const f32x2_t*>(a.part_ml + p * 2);
-      v0[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f);
-      v1[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f + 4);
+      if constexpr (FP8) {
+        v0[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f);
+        v1[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f + 4);
+      } else {
+        load_part_bf16(a.part_o, p * KV_LORA + f, v0[u], v1[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -798,8 +811,7 @@ __global__ __launch_bounds__(512) void decode_merge_uv_kernel(DecodeAttnArgs a) 
       const int sp = min(s0 + 8 * u, ns - 1);  // past the end: re-read (not used)
       const int64_t p = base + (int64_t)sp * 64;
       ml[u] = *reinterpret_cast<const f32x2_t*>(a.part_ml + p * 2);
-      v0[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f);
-      v1[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * KV_LORA + f + 4);
+      load_part_bf16(a.part_o, p * KV_LORA + f, v0[u], v1[u]);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {

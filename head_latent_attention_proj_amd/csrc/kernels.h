@@ -172,7 +172,7 @@ struct DecodeAttnArgs {
   int chunk;               // positions per split
   int max_splits;          // splits per sequence in the grid
   float scale;
-  float* part_o;           // [B][max_splits][64][512] fp32
+  float* part_o;           // [B][max_splits][64][512] unnormalised split outputs: fp32 (FP8), bf16 (bf16 weights)
   float* part_ml;          // [B][max_splits][64][2] (running max, sum)
   const float* w_uv_s;     // FP8: kv_b block scales [128][4] (W_UV,h blocks are rows 2h+1)
   uint16_t* o_lat;         // merged latent output, bf16 [B][64][512] (FP8: high parts, then residuals)
