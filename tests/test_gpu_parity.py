@@ -256,3 +256,33 @@ def test_errors_leave_state_untouched(torch_cuda):
     with pytest.raises(binding.MlaError) as ei:
         small.prefill(c2, [0], [0, 5], x[:5].contiguous())
     assert ei.value.status == 3
+
+
+def test_resume_from_snapshot_is_bit_identical(torch_cuda):
+    """All layer state is the caller's cache and length arrays: snapshot them after a prefill,
+    decode two steps, restore the snapshot (into the same buffers) and decode again; the outputs
+    and the cache bytes match bit for bit."""
+    import torch
+
+    log("snapshot / restore / decode again")
+    L = layer()
+    xbits = synth.make_hidden(52, seed=1006)
+    xt = binding.bf16_tensor(xbits)
+    cache = binding.Cache(L, [64, 16])
+    L.prefill(cache, [0, 1], [0, 40, 50], xt[:50])
+    torch_cuda.cuda.synchronize()
+    snap = (cache.data.clone(), cache.len_h.copy(), cache.len_d.clone())
+
+    def two_steps():
+        out = [binding.tensor_to_bf16_bits(L.decode(cache, [0, 1], xt[50:52].contiguous())) for _ in range(2)]
+        torch.cuda.synchronize()
+        return out, cache.data.clone()
+
+    y1, c1 = two_steps()
+    cache.data.copy_(snap[0])
+    cache.len_h[:] = snap[1]
+    cache.len_d.copy_(snap[2])
+    y2, c2 = two_steps()
+    assert all(np.array_equal(a, b) for a, b in zip(y1, y2))
+    assert torch.equal(c1, c2)
+    assert cache.len_h.tolist() == [42, 12]
