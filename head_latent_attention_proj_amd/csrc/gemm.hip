@@ -16,7 +16,7 @@
 //                    of one workgroup (each wave streams its own contiguous slice of the weight
 //                    rows), and the waves' partial tiles are summed through LDS in a fixed order.
 //                    No cross-workgroup synchronisation, no float atomics: deterministic.
-//   * gemm_head   -- per-head batched products at 16 < M <= 64 with K of 128 or 512.
+//   * gemm_head   -- per-head batched products at M <= 64 with K of 128 or 512.
 //   * gemm_rows   -- one or two rows of A: each load of a wave reads 1 KB (or 256 B) runs of
 //                    single weight rows, dot products on the VALU with x staged in LDS.
 //   Split-K of the tile kernel (few tiles, small M) writes fp32 partials and a separate
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, Norm
 }
 
 // ------------------------------------------------------------------------------------------
-// Per-head products at 16 < M <= 64 with short K (decode W_UK absorb and W_UV, batch 17..64)
+// Per-head products at M <= 64 with short K (decode W_UK absorb and W_UV)
 // ------------------------------------------------------------------------------------------
 // Workgroup = (head, 128 output columns); x_h (M x K, K = 32 KS) is staged in LDS once and
 // every wave streams 16 weight rows over the whole K with all of its loads issued up front;
@@ -690,10 +690,11 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
     pl.ksplit = K;
     pl.ysplit = 1;
   }
-  // Per-head products, 16 < M <= 64, K of 128 or 512: x staged once per (head, 128 columns).
+  // Per-head products, M <= 64, K of 128 or 512: x staged once per (head, 128 columns).
   // Measured on MI355X at M = 64: W_UK absorb and W_UV run in a fraction of the streaming
-  // kernel's time, whose 16-column tiles re-read x for every tile.
-  if (M > 16 && M <= 64 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
+  // kernel's time, whose 16-column tiles re-read x for every tile; at M = 1 (decode of one
+  // sequence) the absorb's 256 workgroups of 8 waves beat 2048 single-wave ones by ~1 us.
+  if (M <= 64 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
     pl.kind = 4;
     pl.tiles = N / 128;
     return pl;
