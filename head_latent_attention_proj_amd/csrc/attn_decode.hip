@@ -477,9 +477,12 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   const int l32 = lane & 31, kg = lane >> 5;
   const int head = hg * 32 + l32;
 
-  // LDS: cache block (+ a scratch row) and the partial-score exchange; after the block loop the
-  // same bytes stage the output rows
-  constexpr int SC_BYTES = (DKB + 1) * LDC2 * 2;
+  // LDS: two cache blocks (+ a scratch row each; consecutive blocks alternate, so a block is
+  // stored while no wave can still read the buffer: its previous block was last read before the
+  // score exchange of the block in between) and the partial-score exchange; after the block loop
+  // the same bytes stage the output rows
+  constexpr int SC_ELEMS = (DKB + 1) * LDC2;
+  constexpr int SC_BYTES = 2 * SC_ELEMS * 2;
   constexpr int XSL = 20;  // floats per lane in the score exchange: 16 + 4 (80-byte rows: the
                            // eight lanes of one 128-byte LDS cycle hit distinct banks)
   constexpr int XS_BYTES = 8 * 64 * XSL * 4;
@@ -511,11 +514,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
       rs[i] = ld16(seq_base + (uint32_t)(key * BF16_ENTRY_BYTES + ccol[i]));
     }
   };
-  auto sstore = [&](const u32x4_t (&rs)[5]) {
+  auto sstore = [&](uint16_t* sCb, const u32x4_t (&rs)[5]) {
 #pragma unroll
     for (int i = 0; i < 5; ++i) {  // chunks past the block go to a scratch row (no branch)
       const int c = tid + 512 * i;
-      st16(c < DKB * 72 ? sC + (c / 72) * LDC2 + (c % 72) * 8 : sC + DKB * LDC2 + (tid & 63) * 8, rs[i]);
+      st16(c < DKB * 72 ? sCb + (c / 72) * LDC2 + (c % 72) * 8 : sCb + DKB * LDC2 + (tid & 63) * 8, rs[i]);
     }
   };
   u32x4_t rA[5], rB[5];
@@ -560,9 +563,12 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x16_t{};
 
+  // One barrier between a block's store and its use; the exchange barrier of each block also
+  // orders every read of the other buffer (two blocks back) before it is stored again, and every
+  // read of the exchange area (one block back) before it is written again.
   auto step = [&](int blk, u32x4_t (&rs)[5]) {
-    __syncthreads();  // the previous block's LDS reads are done
-    sstore(rs);
+    uint16_t* sCb = sC + (blk & 1) * SC_ELEMS;
+    sstore(sCb, rs);
     __syncthreads();
     // unconditional (past the end: the last block again, from cache) so that no branch sits
     // among the loads and the compiler's wait counts stay exact
@@ -572,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     // partial S^T[pos][head] over this wave's 144 features (two chains, added at the end)
     f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
     {
-      const uint16_t* ap = sC + l32 * LDC2 + 144 * fq + 8 * kg;
+      const uint16_t* ap = sCb + l32 * LDC2 + 144 * fq + 8 * kg;
 #pragma unroll
       for (int ks = 0; ks < 9; ks += 2) {
         s0 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap + 16 * ks)), qf[ks], s0);
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
 
     // O^T[feature][head] over this wave's 128 latent features: 4 tiles x 2 position steps
     const int r = lane & 15, cc = 16 * ((lane >> 4) & 1);
-    const uint16_t* tp = sC + (4 * kg + (r >> 2)) * LDC2 + 128 * fq + cc + 4 * (r & 3);
+    const uint16_t* tp = sCb + (4 * kg + (r >> 2)) * LDC2 + 128 * fq + cc + 4 * (r & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
