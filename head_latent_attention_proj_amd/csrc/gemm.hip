@@ -461,18 +461,18 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, Norm
 // ------------------------------------------------------------------------------------------
 // Per-head products at M <= 64 with short K (decode W_UK absorb and W_UV)
 // ------------------------------------------------------------------------------------------
-// Workgroup = (head, 128 output columns); x_h (M x K, K = 32 KS) is staged in LDS once and
+// Workgroup = (head, 16 NWV output columns); x_h (M x K, K = 32 KS) is staged in LDS once and
 // every wave streams 16 weight rows over the whole K with all of its loads issued up front;
 // 16x16x32 MFMA, A fragments from LDS (rows >= M are copies of row M - 1 and never stored).
-template <int KS, int TAG>
-__global__ __launch_bounds__(512) void gemm_head_kernel(GemmArgs p) {
+template <int KS, int NWV, int TAG>
+__global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
   constexpr int LDX = KS * 32 + 8;  // padded LDS row: consecutive rows in distinct 16-byte bank groups
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * LDX];
   const int batch = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.y * 128 + wave * 16;
+  const int n0 = blockIdx.y * (16 * NWV) + wave * 16;
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
   u32x4_t wb[KS];
@@ -481,16 +481,17 @@ __global__ __launch_bounds__(512) void gemm_head_kernel(GemmArgs p) {
   for (int ks = 0; ks < KS; ++ks) wb[ks] = ld16(wr + 32 * ks);
   {
     constexpr int CH = KS * 4;              // 16-byte chunks per row
-    constexpr int PER = 64 * CH / 512;      // chunks per thread
+    constexpr int NT = 64 * NWV;
+    constexpr int PER = 64 * CH / NT;       // chunks per thread
     u32x4_t xv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + 512 * i, row = c / CH, ch = c % CH;
+      const int c = tid + NT * i, row = c / CH, ch = c % CH;
       xv[i] = ld16(A + (int64_t)min(row, p.M - 1) * p.lda + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + 512 * i, row = c / CH, ch = c % CH;
+      const int c = tid + NT * i, row = c / CH, ch = c % CH;
       st16(xs + row * LDX + ch * 8, xv[i]);
     }
   }
@@ -696,7 +697,8 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
   // sequence) the absorb's 256 workgroups of 8 waves beat 2048 single-wave ones by ~1 us.
   if (M <= 64 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
     pl.kind = 4;
-    pl.tiles = N / 128;
+    pl.nw = K == 512 ? 4 : 8;  // W_UV (one 128-column tile per head): two workgroups per head, ~1 us faster at M = 64
+    pl.tiles = N / (16 * pl.nw);
     return pl;
   }
   // 16 < M <= 64 with long K (single products: the projections at decode batch 17..64 and at
@@ -801,8 +803,13 @@ template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   if (pl.kind == 4) {
     dim3 grid(a.batch, pl.tiles);
-    if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, TAG>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_head_kernel<16, TAG>), grid, dim3(512), 0, s, a);
+    if (pl.nw == 8) {
+      if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 8, TAG>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gemm_head_kernel<16, 8, TAG>), grid, dim3(512), 0, s, a);
+    } else {
+      if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 4, TAG>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gemm_head_kernel<16, 4, TAG>), grid, dim3(256), 0, s, a);
+    }
     return;
   }
   if (pl.kind == 3) {
