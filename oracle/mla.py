@@ -37,18 +37,71 @@ class Config:
     v: int = 128
     eps: float = 1e-6          # rms_norm_eps (also the RMSNorm default in the rmsnorm excerpt)
     theta: float = 50000.0     # rope_theta
-    scale: float | None = None  # softmax scale; None -> 1/sqrt(nope + rope)
+    scale: float | None = None  # softmax scale; None -> 1/sqrt(nope + rope) [x YaRN factor^2]
+    # YaRN RoPE (rope_scaling in the same config excerpt); rope_factor <= 1 means plain RoPE
+    rope_factor: float = 1.0
+    rope_orig_max: int = 4096   # original_max_position_embeddings
+    beta_fast: float = 1.0
+    beta_slow: float = 1.0
+    mscale: float = 1.0
+    mscale_all_dim: float = 1.0
 
     @property
     def qk(self) -> int:
         return self.nope + self.rope
 
     @property
+    def yarn(self) -> bool:
+        return self.rope_factor > 1.0
+
+    @property
     def sigma(self) -> float:
-        return self.scale if self.scale is not None else 1.0 / np.sqrt(float(self.qk))
+        if self.scale is not None:
+            return self.scale
+        base = 1.0 / np.sqrt(float(self.qk))
+        if self.yarn:
+            f = yarn_attention_factor(self.rope_factor, self.mscale_all_dim)
+            base *= f * f
+        return base
+
+    @property
+    def rope_gain(self) -> float:
+        """Multiplier on the rotary cos/sin (1 without YaRN)."""
+        if not self.yarn:
+            return 1.0
+        return yarn_attention_factor(self.rope_factor, self.mscale) / yarn_attention_factor(self.rope_factor, self.mscale_all_dim)
 
 
 KIMI_K2 = Config()
+# The released configuration's rope_scaling (config excerpt on the "KV cache" page): YaRN with
+# factor 32 over an original 4,096 positions, beta_fast = beta_slow = 1, mscale = mscale_all_dim = 1.
+KIMI_K2_YARN = Config(rope_factor=32.0)
+
+
+def yarn_attention_factor(s: float, m: float) -> float:
+    """YaRN's attention temperature factor sqrt(1/t) = 0.1 m ln(s) + 1 (YaRN paper, Peng et al.
+    2023, section 3.4, with m the config's mscale coefficient); 1 when s <= 1."""
+    return 1.0 if s <= 1.0 else 0.1 * m * np.log(s) + 1.0
+
+
+def yarn_frequencies(rope: int, theta: float, s: float, orig_max: int, beta_fast: float,
+                     beta_slow: float) -> np.ndarray:
+    """Per-pair rotary frequencies under YaRN's "NTK-by-parts" rule (YaRN paper, section 3.2).
+
+    Pair i has base frequency theta_i = theta^(-2i/rope), wavelength 2 pi / theta_i and
+    r_i = orig_max / wavelength_i turns over the original context. A pair that turns often
+    (r >= beta_fast) keeps theta_i; one that turns less than beta_slow times is interpolated to
+    theta_i / s; in between the two are blended linearly in r. With beta_fast == beta_slow (the
+    released configuration) the blend is a step at r = beta_fast.
+    """
+    i = np.arange(rope // 2, dtype=np.float64)
+    freq = theta ** (-2.0 * i / rope)
+    r = orig_max * freq / (2.0 * np.pi)
+    if beta_fast > beta_slow:
+        gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    else:
+        gamma = (r >= beta_fast).astype(np.float64)
+    return (1.0 - gamma) * freq / s + gamma * freq
 
 
 def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
@@ -66,14 +119,21 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return g * (x / np.sqrt(ms + eps))
 
 
-def rope_cos_sin(pos: np.ndarray, rope: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
+def rope_cos_sin(pos: np.ndarray, rope: int, theta: float, cfg: Config | None = None) -> tuple[np.ndarray, np.ndarray]:
     """cos/sin of the rotary angles, [len(pos), rope/2] ("32 pairs" input on the dense-block
     attention page). Pair i has frequency theta^(-2i/rope); the angle is position * frequency.
+    With a YaRN config (cfg.rope_factor > 1) the frequencies are yarn_frequencies() and cos/sin
+    carry cfg.rope_gain.
     """
-    i = np.arange(rope // 2, dtype=np.float64)
-    freq = theta ** (-2.0 * i / rope)
+    if cfg is not None and cfg.yarn:
+        freq = yarn_frequencies(rope, theta, cfg.rope_factor, cfg.rope_orig_max, cfg.beta_fast, cfg.beta_slow)
+        gain = cfg.rope_gain
+    else:
+        i = np.arange(rope // 2, dtype=np.float64)
+        freq = theta ** (-2.0 * i / rope)
+        gain = 1.0
     ang = np.asarray(pos, dtype=np.float64)[:, None] * freq[None, :]
-    return np.cos(ang), np.sin(ang)
+    return gain * np.cos(ang), gain * np.sin(ang)
 
 
 def rope_rotate(v: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
@@ -106,7 +166,7 @@ def query_path(x: np.ndarray, w: dict, pos: np.ndarray, cfg: Config = KIMI_K2, w
     cq = linear(_act(x, w8a8), w["q_a"])
     q_hat = rmsnorm(cq, w["q_a_norm"], cfg.eps)
     q = linear(_act(q_hat, w8a8), w["q_b"]).reshape(x.shape[0], cfg.heads, cfg.qk)
-    cos, sin = rope_cos_sin(pos, cfg.rope, cfg.theta)
+    cos, sin = rope_cos_sin(pos, cfg.rope, cfg.theta, cfg)
     return {
         "cq": cq,
         "q_hat": q_hat,
@@ -129,7 +189,7 @@ def latent_path(x: np.ndarray, w: dict, pos: np.ndarray, cfg: Config = KIMI_K2, 
     c_hat = rmsnorm(c, w["kv_a_norm"], cfg.eps)
     if w8a8:
         c_hat = _fp8.fake_quant_1x128(c_hat)
-    cos, sin = rope_cos_sin(pos, cfg.rope, cfg.theta)
+    cos, sin = rope_cos_sin(pos, cfg.rope, cfg.theta, cfg)
     return {"ckv": ckv, "c_hat": c_hat, "k_pe": rope_rotate(k_pe, cos, sin)}
 
 

@@ -154,6 +154,95 @@ def test_rope_relative_position_invariance():
     assert np.allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, q[:, 0::2] ** 2 + q[:, 1::2] ** 2, rtol=1e-13)
 
 
+# ------------------------------------------------------------------------------------ YaRN RoPE
+# The config excerpt ("KV cache" page) sets rope_scaling to YaRN: factor 32, original 4,096
+# positions, beta_fast = beta_slow = 1, mscale = mscale_all_dim = 1. The pages give only these
+# parameters; the rule itself is the YaRN paper's (Peng et al. 2023): per-pair interpolation by
+# turns over the original context ("NTK-by-parts") and the attention factor 0.1 m ln(s) + 1.
+def _plain_freq(cfg):
+    return cfg.theta ** (-2.0 * np.arange(cfg.rope // 2) / cfg.rope)
+
+
+def test_yarn_factor_one_is_plain_rope():
+    pos = np.array([0, 3, 4095, 4096, 70000])
+    plain = mla.rope_cos_sin(pos, 64, 50000.0)
+    for cfg in (mla.Config(rope_factor=1.0), mla.Config(rope_factor=0.5)):
+        c, s_ = mla.rope_cos_sin(pos, 64, 50000.0, cfg)
+        assert np.array_equal(c, plain[0]) and np.array_equal(s_, plain[1])
+        assert cfg.sigma == mla.KIMI_K2.sigma and cfg.rope_gain == 1.0
+
+
+def test_yarn_released_config_is_a_step_at_one_turn():
+    cfg = mla.KIMI_K2_YARN
+    f = mla.yarn_frequencies(cfg.rope, cfg.theta, cfg.rope_factor, cfg.rope_orig_max, cfg.beta_fast, cfg.beta_slow)
+    # a pair completes one turn over 4,096 positions when theta^(-2i/64) = 2 pi / 4096, i.e. at
+    # i = 32 ln(4096 / 2 pi) / ln(50000) = 19.16: pairs 0..19 turn more often and keep their
+    # frequency, pairs 20..31 are slowed by the factor 32
+    i_turn = 32 * math.log(4096 / (2 * math.pi)) / math.log(50000.0)
+    assert 19 < i_turn < 20
+    ratio = f / _plain_freq(cfg)
+    assert np.array_equal(ratio[:20], np.ones(20))
+    assert np.allclose(ratio[20:], 1 / 32, rtol=1e-15)
+
+
+def test_yarn_interpolated_pairs_replay_plain_rope_at_scaled_positions():
+    # an interpolated pair at position 32 p has the plain angle of position p; an extrapolated
+    # pair has the plain angle at the same position
+    cfg = mla.KIMI_K2_YARN
+    p = np.array([1, 100, 4095])
+    cy, sy = mla.rope_cos_sin(32 * p, cfg.rope, cfg.theta, cfg)
+    cp, sp = mla.rope_cos_sin(p, cfg.rope, cfg.theta)
+    assert np.allclose(cy[:, 20:], cp[:, 20:], atol=1e-12) and np.allclose(sy[:, 20:], sp[:, 20:], atol=1e-12)
+    cy1, _ = mla.rope_cos_sin(p, cfg.rope, cfg.theta, cfg)
+    assert np.array_equal(cy1[:, :20], cp[:, :20])
+
+
+def test_yarn_ramp_between_thresholds():
+    # the paper's LLaMA thresholds (1 and 32 turns): frequencies fall monotonically from the
+    # plain ones (pairs turning >= 32 times) to plain / s (pairs turning <= once)
+    cfg = mla.Config(rope_factor=16.0, beta_fast=32.0, beta_slow=1.0)
+    f = mla.yarn_frequencies(cfg.rope, cfg.theta, cfg.rope_factor, cfg.rope_orig_max, cfg.beta_fast, cfg.beta_slow)
+    base = _plain_freq(cfg)
+    turns = cfg.rope_orig_max * base / (2 * math.pi)
+    ratio = f / base
+    assert np.all(np.diff(ratio) <= 1e-15)
+    assert np.array_equal(ratio[turns >= 32], np.ones(int((turns >= 32).sum())))
+    assert np.allclose(ratio[turns <= 1], 1 / 16, rtol=1e-15)
+    mid = (turns > 1) & (turns < 32)
+    assert mid.sum() >= 3 and np.all((ratio[mid] > 1 / 16) & (ratio[mid] < 1))
+    # at r = (1 + 32) / 2 the blend would be exactly halfway: check the pair closest to it lies
+    # on the right side of the midpoint value
+    j = int(np.argmin(np.abs(turns - 16.5)))
+    half = (1 + 1 / 16) / 2
+    assert (ratio[j] - half) * (turns[j] - 16.5) >= 0
+
+
+def test_yarn_attention_factor_and_scale():
+    cfg = mla.KIMI_K2_YARN
+    f = 1 + 0.5 * math.log(2)  # 0.1 * ln 32 + 1, ln 32 = 5 ln 2
+    assert mla.yarn_attention_factor(32.0, 1.0) == pytest.approx(f, rel=1e-15)
+    assert cfg.sigma == pytest.approx(f * f / math.sqrt(192), rel=1e-15)
+    assert cfg.rope_gain == 1.0
+    assert mla.yarn_attention_factor(1.0, 1.0) == 1.0
+    g = mla.Config(rope_factor=32.0, mscale=2.0, mscale_all_dim=1.0)
+    assert g.rope_gain == pytest.approx((1 + math.log(2)) / f, rel=1e-15)
+    assert mla.Config(rope_factor=32.0, scale=0.125).sigma == 0.125
+
+
+def test_yarn_scores_depend_on_relative_position():
+    cfg = mla.KIMI_K2_YARN
+    rng = np.random.default_rng(15)
+    q = rng.standard_normal((1, cfg.rope))
+    k = rng.standard_normal((1, cfg.rope))
+    def score(pq, pk):
+        cq, sq = mla.rope_cos_sin(np.array([pq]), cfg.rope, cfg.theta, cfg)
+        ck, sk = mla.rope_cos_sin(np.array([pk]), cfg.rope, cfg.theta, cfg)
+        return float((mla.rope_rotate(q, cq, sq) @ mla.rope_rotate(k, ck, sk).T)[0, 0])
+    base = score(5000, 4990)
+    for delta in (1, 1000, 100000):
+        assert abs(score(5000 + delta, 4990 + delta) - base) < 1e-9 * (1 + abs(base))
+
+
 # ------------------------------------------------------------------------------------ P6 brute force
 @pytest.mark.parametrize("t_new,l0", [(1, 0), (5, 0), (1, 4), (3, 2)])
 def test_brute_force_tiny(t_new, l0):
