@@ -33,7 +33,9 @@ class MlaConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("q_lora", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
                 ("heads", ctypes.c_int32), ("qk_nope", ctypes.c_int32), ("qk_rope", ctypes.c_int32),
                 ("v_head", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float), ("max_positions", ctypes.c_int32), ("wdtype", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("max_positions", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+                ("rope_factor", ctypes.c_float), ("rope_orig_max", ctypes.c_int32), ("rope_beta_fast", ctypes.c_float),
+                ("rope_beta_slow", ctypes.c_float), ("rope_mscale", ctypes.c_float), ("rope_mscale_all_dim", ctypes.c_float)]
 
 
 class MlaWeights(ctypes.Structure):
@@ -116,9 +118,19 @@ def check(status: int) -> None:
         raise MlaError(status, lib().mla_last_error().decode())
 
 
+# rope_scaling of the released configuration (config excerpt on the "KV cache" page)
+KIMI_K2_YARN = {"factor": 32.0, "original_max_position_embeddings": 4096, "beta_fast": 1.0, "beta_slow": 1.0,
+                "mscale": 1.0, "mscale_all_dim": 1.0}
+
+
 def make_config(max_positions: int = 131072, wdtype: int = WDTYPE_BF16, softmax_scale: float = 0.0,
-                eps: float = 1e-6, theta: float = 50000.0) -> MlaConfig:
-    return MlaConfig(7168, 1536, 512, 64, 128, 64, 128, eps, theta, softmax_scale, max_positions, wdtype)
+                eps: float = 1e-6, theta: float = 50000.0, rope_scaling: dict | None = None) -> MlaConfig:
+    """Layer config; rope_scaling (keys as in the config excerpt's rope_scaling) selects YaRN RoPE."""
+    y = rope_scaling or {}
+    return MlaConfig(7168, 1536, 512, 64, 128, 64, 128, eps, theta, softmax_scale, max_positions, wdtype,
+                     float(y.get("factor", 0.0)), int(y.get("original_max_position_embeddings", 0)),
+                     float(y.get("beta_fast", 0.0)), float(y.get("beta_slow", 0.0)),
+                     float(y.get("mscale", 0.0)), float(y.get("mscale_all_dim", 0.0)))
 
 
 def _stream(stream):
@@ -216,11 +228,12 @@ class _PoolLayerCache(Cache):
 class Layer:
     """One MLA layer: a library context over caller-owned (torch) weights."""
 
-    def __init__(self, weights: dict, max_positions: int = 131072, wdtype: int = WDTYPE_BF16, stream=None):
+    def __init__(self, weights: dict, max_positions: int = 131072, wdtype: int = WDTYPE_BF16, stream=None,
+                 rope_scaling: dict | None = None):
         import torch
 
         L = lib()
-        self.cfg = make_config(max_positions, wdtype)
+        self.cfg = make_config(max_positions, wdtype, rope_scaling=rope_scaling)
         self.weights = weights  # keep the referenced tensors alive
         w = MlaWeights()
         for name in ("q_a", "q_a_norm", "q_b", "kv_a", "kv_a_norm", "kv_b", "o"):

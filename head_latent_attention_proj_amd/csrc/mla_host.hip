@@ -106,6 +106,13 @@ mla_status check_config(const mla_config* c) {
     return fail(MLA_E_ARG, "rms_eps, rope_theta or softmax_scale out of range");
   if (c->max_positions < 1 || c->max_positions > 131072)
     return fail(MLA_E_ARG, "max_positions must be in [1, 131072]");
+  if (!std::isfinite(c->rope_factor))
+    return fail(MLA_E_ARG, "rope_factor must be finite");
+  if (c->rope_factor > 1.f &&
+      (c->rope_orig_max < 1 || !(c->rope_beta_slow > 0.f) || !(c->rope_beta_fast >= c->rope_beta_slow) ||
+       !std::isfinite(c->rope_beta_fast) || !(c->rope_mscale >= 0.f) || !(c->rope_mscale_all_dim >= 0.f) ||
+       !std::isfinite(c->rope_mscale) || !std::isfinite(c->rope_mscale_all_dim)))
+    return fail(MLA_E_ARG, "YaRN RoPE: need rope_orig_max > 0, rope_beta_fast >= rope_beta_slow > 0, mscales >= 0");
   if (c->wdtype != MLA_WDTYPE_BF16 && c->wdtype != MLA_WDTYPE_FP8_E4M3_B128)
     return fail(MLA_E_ARG, "unknown weight format %d", c->wdtype);
   return MLA_OK;
@@ -394,15 +401,30 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
                        (uint16_t*)(pk + L.uvw));
     HIP_TRY(hipGetLastError());
   }
-  // RoPE table: angle = position * theta^(-2i/64), computed in double, stored float32
+  // RoPE table: angle = position * frequency of pair i, computed in double, stored float32.
+  // Plain RoPE: frequency theta^(-2i/64). YaRN (rope_factor > 1; the rule of the YaRN paper,
+  // Peng et al. 2023, with the config's rope_scaling values): a pair making r turns over the
+  // original context keeps its frequency when r >= beta_fast, is slowed by the factor when
+  // r < beta_slow, and in between blends the two linearly in r; cos/sin carry the ratio of the
+  // attention factors f(mscale) / f(mscale_all_dim), f(m) = 0.1 m ln(factor) + 1.
+  const bool yarn = cfg->rope_factor > 1.f;
+  const double yf = cfg->rope_factor;
+  auto attn_factor = [&](double m) { return 0.1 * m * std::log(yf) + 1.0; };
+  const double gain = yarn ? attn_factor(cfg->rope_mscale) / attn_factor(cfg->rope_mscale_all_dim) : 1.0;
   const int P = cfg->max_positions;
   std::vector<float> cs((size_t)P * 64);
   for (int i = 0; i < 32; ++i) {
-    const double freq = std::pow((double)cfg->rope_theta, -2.0 * i / 64.0);
+    double freq = std::pow((double)cfg->rope_theta, -2.0 * i / 64.0);
+    if (yarn) {
+      const double turns = (double)cfg->rope_orig_max * freq / (2.0 * M_PI);
+      const double lo = cfg->rope_beta_slow, hi = cfg->rope_beta_fast;
+      const double keep = hi > lo ? std::min(1.0, std::max(0.0, (turns - lo) / (hi - lo))) : (turns >= hi ? 1.0 : 0.0);
+      freq = keep * freq + (1.0 - keep) * freq / yf;
+    }
     for (int p = 0; p < P; ++p) {
       const double ang = (double)p * freq;
-      cs[(size_t)p * 32 + i] = (float)std::cos(ang);
-      cs[(size_t)P * 32 + (size_t)p * 32 + i] = (float)std::sin(ang);
+      cs[(size_t)p * 32 + i] = (float)(gain * std::cos(ang));
+      cs[(size_t)P * 32 + (size_t)p * 32 + i] = (float)(gain * std::sin(ang));
     }
   }
   HIP_TRY(hipMemcpyAsync(pk + L.rope, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, s));
@@ -411,7 +433,10 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
   mla_ctx* c = new mla_ctx;
   c->cfg = *cfg;
   c->fp8 = fp8;
-  c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(1.0 / std::sqrt((double)QK));
+  {
+    const double f = yarn ? attn_factor(cfg->rope_mscale_all_dim) : 1.0;
+    c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(f * f / std::sqrt((double)QK));
+  }
   c->g_q = (const uint16_t*)(pk + L.g_q);
   c->g_kv = (const uint16_t*)(pk + L.g_kv);
   c->w_qkva = pk + L.qkva;

@@ -79,6 +79,22 @@ typedef struct {
                            without defining it */
   int32_t max_positions;/* positions a sequence may hold, 1..131072 (max_position_embeddings) */
   int32_t wdtype;       /* MLA_WDTYPE_* */
+  /* YaRN RoPE (rope_scaling in the config excerpt on the "KV cache" page: factor 32, original
+   * 4096 positions, beta_fast = beta_slow = 1, mscale = mscale_all_dim = 1). The pages give the
+   * parameters only; the rule is the published YaRN method (Peng et al. 2023): pair i of base
+   * frequency theta_i makes r_i = rope_orig_max * theta_i / (2 pi) turns over the original
+   * context; pairs with r_i >= beta_fast keep theta_i, pairs with r_i < beta_slow use
+   * theta_i / rope_factor, pairs in between blend the two linearly in r_i (a step at beta_fast
+   * when the two thresholds are equal). With f(m) = 0.1 m ln(rope_factor) + 1, cos/sin carry
+   * f(rope_mscale) / f(rope_mscale_all_dim) and a softmax_scale of 0 selects
+   * f(rope_mscale_all_dim)^2 / sqrt(qk_nope + qk_rope). rope_factor <= 1 (or 0, as a
+   * zero-filled struct has) selects plain RoPE and ignores the other five fields. */
+  float rope_factor;
+  int32_t rope_orig_max;   /* > 0 when rope_factor > 1 */
+  float rope_beta_fast;    /* >= rope_beta_slow > 0 when rope_factor > 1 */
+  float rope_beta_slow;
+  float rope_mscale;       /* >= 0 */
+  float rope_mscale_all_dim;
 } mla_config;
 
 /* Device weights, [out, in] row-major. bf16 format: every pointer is bf16, *_s are NULL.

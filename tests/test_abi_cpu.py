@@ -56,6 +56,18 @@ def test_config_validation_without_gpu(L):
     assert L.mla_cache_entry_bytes(ctypes.byref(bad)) == 0
     bad = binding.make_config(wdtype=7)
     assert L.mla_cache_entry_bytes(ctypes.byref(bad)) == 0
+    # YaRN RoPE: the released rope_scaling validates; a zero-filled tail (plain RoPE) too
+    yarn = binding.make_config(max_positions=4096, rope_scaling=binding.KIMI_K2_YARN)
+    assert L.mla_cache_entry_bytes(ctypes.byref(yarn)) == 1152
+    assert yarn.rope_factor == 32.0 and yarn.rope_orig_max == 4096
+    for key, val in (("original_max_position_embeddings", 0), ("beta_slow", 0.0), ("beta_fast", 0.5),
+                     ("mscale", -1.0), ("factor", float("inf"))):
+        bad = binding.make_config(rope_scaling={**binding.KIMI_K2_YARN, key: val})
+        assert L.mla_cache_entry_bytes(ctypes.byref(bad)) == 0, key
+    assert b"rope" in L.mla_last_error()
+    # factor <= 1 ignores the other fields
+    off = binding.make_config(rope_scaling={"factor": 1.0, "beta_slow": -3.0})
+    assert L.mla_cache_entry_bytes(ctypes.byref(off)) == 1152
 
 
 def test_init_rejects_null_and_unsupported_before_any_hip_call(L):
