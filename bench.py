@@ -50,6 +50,15 @@ def prefill_flops(T):
     return proj + att
 
 
+def chunk_prefill_flops(T, L0):
+    """Prefill of T tokens onto L0 cached positions as this path runs it: the projections of the T
+    tokens, kv_b over all L0 + T latent rows (the cached prefix is up-projected again), and 640
+    flop per head per causal pair (query t sees L0 + t + 1 keys)."""
+    proj = 2 * T * (7168 * 2112 + 1536 * 12288 + 8192 * 7168) + 2 * (L0 + T) * 512 * 16384
+    att = 640 * 64 * (T * L0 + T * (T + 1) // 2)
+    return proj + att
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -202,6 +211,55 @@ def main():
                 "note": "includes one zero-fill of the device length per step",
             }
             del pc, xb, yb
+        # ---------------- chunked prefill: 512 new tokens onto 3,584 cached positions
+        log("timing chunked prefill T=512 onto 3584 cached positions")
+        T, L0c = 512, 3584
+        ent_c = binding.bf16_tensor(synth.make_cache_entries(L0c, seed=2003))
+        ccs = []
+        for L in layers:
+            cc = binding.Cache(L, [L0c + T])
+            L.cache_append(cc, 0, ent_c)
+            ccs.append(cc)
+        xb = binding.bf16_tensor(synth.make_hidden(T, seed=1005))
+        yb = torch.empty_like(xb)
+        sid = np.zeros(1, dtype=np.int32)
+        qs = np.array([0, T], dtype=np.int32)
+        sid_dev = torch.from_numpy(sid).cuda()
+        qs_dev = torch.from_numpy(qs).cuda()
+
+        def chunk_step(i):
+            c = i % args.copies
+            ccs[c].len_h[0] = L0c
+            ccs[c].len_d.fill_(L0c)
+            layers[c].prefill(ccs[c], sid, qs, xb, y=yb, seq_ids_d=sid_dev, q_start_d=qs_dev)
+
+        t = timed_loop(torch, chunk_step, 20, 5)
+        fl = chunk_prefill_flops(T, L0c)
+        extra["prefill_chunk_T512_on_L3584"] = {
+            "ms": round(t * 1e3, 4), "tokens_per_s": round(T / t, 1),
+            "tflops": round(fl / t / 1e12, 2), "mfma_frac": round(fl / t / BF16_PEAK, 4),
+            "note": "512 new tokens of one sequence after 3,584 cached positions (synthetic entries); kv_b "
+                    "rebuilds keys and values for all 4,096 rows; includes one fill of the device length per step"}
+        del ccs, xb, yb, ent_c
+        # ---------------- YaRN RoPE (the released rope_scaling): the decode B=1 step again
+        log("timing YaRN decode B=1")
+        ylayers = [binding.Layer(L.weights, max_positions=16384, rope_scaling=binding.KIMI_K2_YARN) for L in layers]
+        ycaches = []
+        for L in ylayers:
+            cache = binding.Cache(L, [P0 + args.steps + args.warmup + 2])
+            L.prefill(cache, [0], [0, P0], x_fill)
+            ycaches.append(cache)
+
+        def yarn_step(i):
+            c = i % args.copies
+            ylayers[c].decode(ycaches[c], sid_h, x_new, y=y_new, seq_ids_d=sid_d)
+
+        t = timed_loop(torch, yarn_step, args.steps, args.warmup)
+        extra["yarn_decode_B1"] = {
+            "us_per_step": round(t * 1e6, 3),
+            "note": "decode B=1 at position 1000 with YaRN RoPE (factor 32, original 4096, beta 1/1, mscale 1/1): "
+                    "only the rotary table and the softmax scale differ, so the kernels are the headline's"}
+        del ylayers, ycaches
         # ---------------- decode B=64, lengths U[1024, 8192]
         log("timing decode B=64 varlen")
         B = 64
