@@ -149,6 +149,30 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
   }
 
   if (splits == 1) {
+    if (p.epi == EPI_KVB && (p.key_base & 3) == 0) {
+      // kv_b: a lane's four accumulators are four consecutive keys of one feature, i.e. four
+      // adjacent elements of a value row of V^T: stored as one 8-byte write instead of four
+      // 2-byte writes to four places (the content-key half keeps the generic store)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int mb = m0 + wm * WTM + i * 16 + g * 4;
+          const int n = n0 + wn * WTN + j * 16 + l16;
+          if (n >= p.N) continue;
+          if ((n & 255) >= 128 && mb + 3 < p.M) {
+            f32x4_t v = acc[i][j];
+            if (p.c_scale) v *= p.c_scale[batch * p.cs_stride + (n >> 7)];
+            *reinterpret_cast<u32x2_t*>(p.vt + (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb) =
+                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (mb + e < p.M) epi_store(p, batch, mb + e, n, acc[i][j][e]);
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll

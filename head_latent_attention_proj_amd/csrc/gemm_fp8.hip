@@ -325,6 +325,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
   }
 
   if (splits == 1) {
+    if (p.epi == EPI_KVB && (p.key_base & 3) == 0) {
+      // kv_b: a lane's four accumulators are four consecutive keys of one feature, i.e. four
+      // adjacent elements of a value row of V^T (and of its residual plane): one 8-byte write
+      // each instead of four 2-byte writes to four places
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int mb = m0 + wm * WTM + i * 16 + g * 4;
+          const int n = n0 + wn * WTN + j * 16 + l16;
+          if (n >= p.N) continue;
+          if ((n & 255) >= 128 && mb + 3 < p.M) {
+            const f32x4_t v = acc[i][j];
+            const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+            const int64_t at = (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb;
+            *reinterpret_cast<u32x2_t*>(p.vt + at) = u32x2_t{h01, h23};
+            if (p.vt_lo)
+              *reinterpret_cast<u32x2_t*>(p.vt_lo + at) =
+                  u32x2_t{pack_bf16x2(v[0] - bf_lo(h01), v[1] - bf_hi(h01)), pack_bf16x2(v[2] - bf_lo(h23), v[3] - bf_hi(h23))};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (mb + e < p.M) epi_store8(p, batch, mb + e, n, acc[i][j][e]);
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
