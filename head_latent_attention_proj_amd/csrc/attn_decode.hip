@@ -52,11 +52,12 @@ MLA_DEV u32x2_t ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-// four E4M3FN codes (one 32-bit word) -> two packed bf16 pairs (exact)
+// four E4M3FN codes (one 32-bit word) -> two packed bf16 pairs (exact: every E4M3 value is a
+// bf16 value; gfx950 converts a code pair to a bf16 pair in one instruction, unit scale)
 MLA_DEV u32x2_t e4m3x4_to_bf16(uint32_t w) {
-  const float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, 0), f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-  const float f2 = __builtin_amdgcn_cvt_f32_fp8((int)w, 2), f3 = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-  return u32x2_t{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // 8 waves: wave = hg + 4*lh, head group hg (heads hg*16 .. +15), half lh. A wave forms the
