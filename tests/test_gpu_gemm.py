@@ -46,6 +46,29 @@ def test_gemm_matches_float64(M, N, K):
     assert err.max() <= 2e-5 * scale * 8
 
 
+@pytest.mark.parametrize("M,N,K", [
+    # bf16 outputs of the tile kernels: 128 x 128 and 256 x 256 tiles with ragged M (the LDS-staged
+    # row-chunk epilogue), N not a multiple of 8 (the per-value epilogue), and a split-K product
+    # (the reduction's epilogue)
+    (2100, 4096, 512), (4100, 8192, 128), (2100, 4100, 256), (200, 1536, 512),
+])
+def test_gemm_bf16_output_matches_float64(M, N, K):
+    import torch
+
+    log(f"gemm bf16 out M={M} N={N} K={K}")
+    a = bf16_rand((M, K), 3 + M)
+    b = bf16_rand((N, K), 4 + N, std=0.02)
+    A, B = binding.bf16_tensor(a), binding.bf16_tensor(b)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    binding.Gemm()(A, B, C, M, N, K)
+    torch.cuda.synchronize()
+    ref = omla.linear(synth.bf16_bits_to_f64(a), synth.bf16_bits_to_f64(b))
+    got = C.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))  # every element written
+    # bf16 rounding of the float32 sum: half a unit in the last place, plus the float32 sum's error
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(K))
+
+
 @pytest.mark.parametrize("Bt", [1, 2, 5, 33, 64])
 def test_gemm_bf16_output_and_batched_strides(Bt):
     """Per-head batched product with row/batch strides (the decode absorption layout)."""
