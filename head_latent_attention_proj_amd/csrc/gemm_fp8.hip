@@ -325,6 +325,34 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
   }
 
   if (splits == 1) {
+    if (p.epi == EPI_BF16 && !p.resid && (p.N & 7) == 0 && (p.ldc & 7) == 0 && (p.sC & 7) == 0 &&
+        (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+      // bf16 output through LDS: each wave writes its WTM x WTN results to a private region of the
+      // (then free) tile buffers and stores whole 16-byte pieces of output rows, eight lanes per
+      // 128-byte row segment, instead of one 2-byte store per value
+      constexpr int LDW = WTN + 8;
+      static_assert(WM * WN * WTM * LDW * 2 <= 2 * (BM + BN) * LDK, "epilogue staging fits the tile buffers");
+      uint16_t* sw = reinterpret_cast<uint16_t*>(smem) + wave * (WTM * LDW);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = f2bf(acc[i][j][e]);
+      __syncthreads();
+      const int lr8 = lane >> 3, lc8 = (lane & 7) * 8;
+      const int n = n0 + wn * WTN + lc8;
+      if (n < p.N) {  // N is a multiple of 8: a piece is whole or wholly outside
+        uint16_t* cb = (uint16_t*)p.C + batch * p.sC + n;
+#pragma unroll
+        for (int k = 0; k < WTM / 8; ++k) {
+          const int r = k * 8 + lr8;
+          const int m = m0 + wm * WTM + r;
+          if (m < p.M) st16(cb + (int64_t)m * p.ldc, ld16(sw + r * LDW + lc8));
+        }
+      }
+      return;
+    }
     if (p.epi == EPI_KVB && (p.key_base & 3) == 0) {
       // kv_b: a lane's four accumulators are four consecutive keys of one feature, i.e. four
       // adjacent elements of a value row of V^T (and of its residual plane): one 8-byte write
