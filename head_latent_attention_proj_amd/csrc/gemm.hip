@@ -177,10 +177,60 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
       }
       return;
     }
+    if (p.epi == EPI_KVB && (p.key_base & 3) == 0 && !p.c_scale && (p.N & 7) == 0) {
+      // kv_b: a wave's 64 columns lie in one half of a head's 256 (wave-uniform). Content keys
+      // go through LDS as for bf16 outputs and leave as 16-byte pieces of K_nope rows; values go
+      // straight to V^T, a lane's four accumulators (four consecutive keys of one feature) as one
+      // 8-byte store. Every wave reaches the barrier.
+      static_assert(WTN == 64 && WM * WN * WTM * (WTN + 8) <= 2 * (BM + BN) * LDK, "kv_b epilogue layout");
+      constexpr int LDW = WTN + 8;
+      uint16_t* sw = smem + wave * (WTM * LDW);
+      const int nw0 = n0 + wn * WTN;
+      const bool khalf = (nw0 & 255) < 128;
+      if (khalf) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = f2bf(acc[i][j][e]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int mb = m0 + wm * WTM + i * 16 + g * 4;
+            const int n = nw0 + j * 16 + l16;
+            if (n >= p.N) continue;
+            if (mb + 3 < p.M) {
+              const f32x4_t v = acc[i][j];
+              *reinterpret_cast<u32x2_t*>(p.vt + (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb) =
+                  u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (mb + e < p.M) epi_store(p, batch, mb + e, n, acc[i][j][e]);
+            }
+          }
+      }
+      __syncthreads();
+      if (khalf) {
+        const int lr8 = lane >> 3, lc8 = (lane & 7) * 8;
+        const int n = nw0 + lc8;
+        if (n < p.N) {
+          uint16_t* kb0 = p.knope + (n >> 8) * 128 + (n & 255);
+#pragma unroll
+          for (int k = 0; k < WTM / 8; ++k) {
+            const int r = k * 8 + lr8;
+            const int m = m0 + wm * WTM + r;
+            if (m < p.M) st16(kb0 + (p.key_base + m) * 8192, ld16(sw + r * LDW + lc8));
+          }
+        }
+      }
+      return;
+    }
     if (p.epi == EPI_KVB && (p.key_base & 3) == 0) {
-      // kv_b: a lane's four accumulators are four consecutive keys of one feature, i.e. four
-      // adjacent elements of a value row of V^T: stored as one 8-byte write instead of four
-      // 2-byte writes to four places (the content-key half keeps the generic store)
+      // kv_b with an output scale: V^T as 8-byte pieces as above, content keys value by value
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
