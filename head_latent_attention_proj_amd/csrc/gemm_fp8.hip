@@ -353,6 +353,74 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
       }
       return;
     }
+    if constexpr (WTN == 64 && WM * WN * WTM * (WTN + 8) * 4 <= 2 * (BM + BN) * LDK) {
+      if (p.epi == EPI_KVB && (p.key_base & 3) == 0 && (p.N & 7) == 0) {
+        // kv_b: a wave's 64 columns lie in one half of a head's 256 (wave-uniform). Content keys
+        // and their bf16 residuals go through LDS (two planes per wave) and leave as 16-byte
+        // pieces of K_nope rows; values go straight to V^T as 8-byte pieces (four consecutive
+        // keys of one feature per lane). Every wave reaches the barrier.
+        constexpr int LDW = WTN + 8;
+        uint16_t* shi = reinterpret_cast<uint16_t*>(smem) + wave * (2 * WTM * LDW);
+        uint16_t* slo = shi + WTM * LDW;
+        const int nw0 = n0 + wn * WTN;
+        const bool khalf = (nw0 & 255) < 128;
+        if (khalf) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float v = acc[i][j][e];
+                const uint16_t h = f2bf(v);
+                const int at = (i * 16 + g * 4 + e) * LDW + j * 16 + l16;
+                shi[at] = h;
+                slo[at] = f2bf(v - bf2f(h));
+              }
+        } else {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int mb = m0 + wm * WTM + i * 16 + g * 4;
+              const int n = nw0 + j * 16 + l16;
+              if (n >= p.N) continue;
+              if (mb + 3 < p.M) {
+                const f32x4_t v = acc[i][j];
+                const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+                const int64_t at = (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb;
+                *reinterpret_cast<u32x2_t*>(p.vt + at) = u32x2_t{h01, h23};
+                if (p.vt_lo)
+                  *reinterpret_cast<u32x2_t*>(p.vt_lo + at) =
+                      u32x2_t{pack_bf16x2(v[0] - bf_lo(h01), v[1] - bf_hi(h01)), pack_bf16x2(v[2] - bf_lo(h23), v[3] - bf_hi(h23))};
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (mb + e < p.M) epi_store8(p, batch, mb + e, n, acc[i][j][e]);
+              }
+            }
+        }
+        __syncthreads();
+        if (khalf) {
+          const int lr8 = lane >> 3, lc8 = (lane & 7) * 8;
+          const int n = nw0 + lc8;
+          if (n < p.N) {
+            const int64_t col = (n >> 8) * 128 + (n & 255);
+#pragma unroll
+            for (int k = 0; k < WTM / 8; ++k) {
+              const int r = k * 8 + lr8;
+              const int m = m0 + wm * WTM + r;
+              if (m < p.M) {
+                const int64_t at = (p.key_base + m) * 8192 + col;
+                st16(p.knope + at, ld16(shi + r * LDW + lc8));
+                if (p.knope_lo) st16(p.knope_lo + at, ld16(slo + r * LDW + lc8));
+              }
+            }
+          }
+        }
+        return;
+      }
+    }
     if (p.epi == EPI_KVB && (p.key_base & 3) == 0) {
       // kv_b: a lane's four accumulators are four consecutive keys of one feature, i.e. four
       // adjacent elements of a value row of V^T (and of its residual plane): one 8-byte write
