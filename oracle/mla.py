@@ -318,13 +318,18 @@ def block_attention(x: np.ndarray, w: dict, g_in: np.ndarray, cfg: Config = KIMI
     is the block input, the layer sees its input RMSNorm (gain g_in over the hidden features,
     eps = rms_norm_eps), and the layer output is added to the residual: h = x + MLA(norm(x)).
 
+    The block's output is the model's hidden state, a tensor of the model dtype (bf16: the
+    config excerpt's torch_dtype): h is the bf16 rounding of the exact sum x + y, where the
+    layer output y itself stays unrounded (float64) as everywhere in the oracle. A stack of
+    blocks therefore passes bf16 hidden states from one block to the next, as the model does.
+
     Same arguments as `forward`; returns h [len(rows), hidden], the normalised input xn and
-    everything `forward` returns for it.
+    everything `forward` returns for it (y is the unrounded layer output).
     """
     xn = input_rmsnorm(x, g_in, cfg.eps)
     out = forward(xn, w, cfg, cache=cache, rows=rows, w8a8=w8a8, absorbed=absorbed)
     r = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
-    return {"h": x[r] + out["y"], "xn": xn, **out}
+    return {"h": round_bf16(x[r] + out["y"]), "xn": xn, **out}
 
 
 # ----------------------------------------------------------------------------------------------

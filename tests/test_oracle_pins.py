@@ -458,11 +458,11 @@ def test_round_bf16_matches_torch_on_float32_values():
 
 
 def test_block_residual_when_o_proj_vanishes():
-    """W_o = 0: the attention adds nothing, so the block returns its input exactly."""
+    """W_o = 0: the attention adds nothing, so the block returns its (bf16) input exactly."""
     cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
     w = tiny_weights(cfg, seed=31, zero=("o",))
     rng = np.random.default_rng(32)
-    x = rng.standard_normal((5, cfg.hidden))
+    x = mla.round_bf16(rng.standard_normal((5, cfg.hidden)))
     g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
     out = mla.block_attention(x, w, g, cfg)
     assert np.array_equal(out["h"], x)
@@ -471,16 +471,47 @@ def test_block_residual_when_o_proj_vanishes():
 @pytest.mark.parametrize("c", [4.0, 0.25])
 def test_block_input_norm_scale_invariance(c):
     """With eps = 0 the RMSNorm output does not depend on the input's scale (and a power-of-two
-    scale leaves every bf16 rounding unchanged), so h(c x) - c x = h(x) - x exactly. Fails if the
-    norm were skipped, applied to the residual, or its output added instead of x."""
+    scale leaves every bf16 rounding unchanged), so the layer output y is the same for x and c x,
+    and h(c x) is c x + y rounded to bf16: a bf16 value within half a bf16 unit of c x + y. Fails
+    if the norm were skipped, applied to the residual, or its output added instead of x."""
     cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6, eps=0.0)
     w = tiny_weights(cfg, seed=33)
     rng = np.random.default_rng(34)
     x = rng.standard_normal((4, cfg.hidden))
     g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
-    a = mla.block_attention(x, w, g, cfg)["h"] - x
-    b = mla.block_attention(c * x, w, g, cfg)["h"] - c * x
-    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+    a = mla.block_attention(x, w, g, cfg)
+    b = mla.block_attention(c * x, w, g, cfg)
+    assert np.max(np.abs(a["y"] - b["y"])) <= 1e-12 * np.max(np.abs(a["y"]))
+    want = c * x + a["y"]
+    half_unit = np.ldexp(1.0, np.frexp(want)[1] - 9)  # half of 2^(e-8), the bf16 spacing at want
+    assert np.all(np.abs(b["h"] - want) <= half_unit)
+    bits = b["h"].astype(np.float32).view(np.uint32)
+    assert np.all(b["h"].astype(np.float32) == b["h"]) and np.all(bits & 0xFFFF == 0)
+
+
+def test_block_output_is_bf16_like_torch():
+    """The block output h = x + y is a bf16 tensor (the model dtype): the oracle's rounding of the
+    exact sum of a bf16 x and a float32-representable y equals torch's float32 add of the two
+    followed by one cast to bfloat16, wherever that float32 sum is exact (most elements here;
+    elsewhere torch would round twice)."""
+    import torch
+
+    cfg = mla.Config(hidden=64, q_lora=32, kv_lora=16, heads=4, nope=8, rope=8, v=6)
+    w = tiny_weights(cfg, seed=37)
+    rng = np.random.default_rng(38)
+    x = mla.round_bf16(4.0 * rng.standard_normal((6, cfg.hidden)))
+    g = 1.0 + 0.1 * rng.standard_normal(cfg.hidden)
+    out = mla.block_attention(x, w, g, cfg)
+    y32 = out["y"].astype(np.float32)
+    # the oracle's h from the float32 image of y (so that torch sees the same summands)
+    want = mla.round_bf16(x + y32.astype(np.float64))
+    s32 = torch.from_numpy(x.astype(np.float32)) + torch.from_numpy(y32)
+    exact_sum = s32.double().numpy() == x + y32.astype(np.float64)
+    assert exact_sum.mean() > 0.5
+    assert np.array_equal(s32.to(torch.bfloat16).double().numpy()[exact_sum], want[exact_sum])
+    # and the oracle's own h is the rounding of the unrounded sum, within half a unit of it
+    exact = x + out["y"]
+    assert np.all(np.abs(out["h"] - exact) <= np.ldexp(1.0, np.frexp(exact)[1] - 9))
 
 
 @pytest.mark.parametrize("t_new,l0", [(3, 0), (1, 3)])
@@ -501,3 +532,79 @@ def test_block_brute_force_tiny(t_new, l0):
     dims = dict(q_lora=cfg.q_lora, kv_lora=cfg.kv_lora, heads=cfg.heads, nope=cfg.nope, rope=cfg.rope, v=cfg.v)
     hs, _ = brute.block(x.tolist(), to_lists(w), g.tolist(), dims, cfg.eps, cfg.theta, 1 / math.sqrt(cfg.qk), bcache)
     assert np.allclose(out["h"], np.array(hs), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------ W8A8 wiring, brute force
+W8 = mla.Config(hidden=256, q_lora=128, kv_lora=128, heads=2, nope=64, rope=64, v=64)
+
+
+def _w8_weights(seed):
+    w = tiny_weights(W8, seed=seed)
+    return {k: (v if k.endswith("norm") else 0.1 * v) for k, v in w.items()}
+
+
+def _w8_case(t_new, l0, seed):
+    w = _w8_weights(seed)
+    rng = np.random.default_rng(seed + 1)
+    x_prev = rng.standard_normal((l0, W8.hidden))
+    x = rng.standard_normal((t_new, W8.hidden))
+    cache = mla.kv_entries(x_prev, w, 0, W8, w8a8=True) if l0 else None
+    bcache = [(list(cache[0][i]), list(cache[1][i])) for i in range(l0)] if l0 else None
+    dims = dict(q_lora=W8.q_lora, kv_lora=W8.kv_lora, heads=W8.heads, nope=W8.nope, rope=W8.rope, v=W8.v)
+
+    def run_brute(points):
+        return brute.forward(x.tolist(), to_lists(w), dims, W8.eps, W8.theta, W8.sigma, bcache, w8a8=points)
+
+    return mla.forward(x, w, W8, cache=cache, w8a8=True), run_brute
+
+
+@pytest.mark.parametrize("t_new,l0", [(3, 0), (1, 3)])
+def test_w8a8_forward_against_scalar_brute_force(t_new, l0):
+    """The W8A8 layer (every projection input quantised: x into q_a and kv_a, q_hat into q_b,
+    c_hat into kv_b, o into o_proj) against the scalar restatement with its own quantiser, at
+    dimensions that are multiples of the 128-feature group. Prefill (T = 3) and a decode step
+    onto a W8A8 cache."""
+    out, run_brute = _w8_case(t_new, l0, seed=40 + l0)
+    ys, ents = run_brute(brute.W8A8_POINTS)
+    tol = 1e-12 * max(1.0, float(np.max(np.abs(out["y"]))))
+    assert np.allclose(out["y"], np.array(ys), rtol=0, atol=tol)
+    assert np.allclose(out["c_hat"], np.array([e[0] for e in ents]), rtol=0, atol=1e-12)
+    assert np.allclose(out["k_pe"], np.array([e[1] for e in ents]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dropped", brute.W8A8_POINTS)
+def test_w8a8_each_quantised_input_is_observable(dropped):
+    """Leaving any one of the four quantisation points out of the brute force moves the output
+    far beyond rounding: a wiring mistake at that point in the oracle would fail the test above."""
+    out, run_brute = _w8_case(2, 2, seed=44)
+    ys, _ = run_brute(tuple(p for p in brute.W8A8_POINTS if p != dropped))
+    assert np.max(np.abs(out["y"] - np.array(ys))) > 1e-6 * np.max(np.abs(out["y"]))
+
+
+def test_scalar_quantiser_matches_worked_e4m3_values():
+    """The brute force's scalar e4m3 rounding: exact codes, a tie to the even significand,
+    the subnormal spacing 2^-9, saturation at 448."""
+    assert brute._e4m3(448.0) == 448.0 and brute._e4m3(1000.0) == 448.0 and brute._e4m3(-460.0) == -448.0
+    assert brute._e4m3(0.65625) == 0.625            # halfway between 0.625 (m=2) and 0.6875 (m=3)
+    assert brute._e4m3(0.71875) == 0.75             # halfway between 0.6875 (m=3) and 0.75 (m=4)
+    assert brute._e4m3(3 * 2.0 ** -10) == 2.0 ** -8  # 1.5 subnormal steps: tie to the even step 2
+    assert brute._e4m3(2.0 ** -9) == 2.0 ** -9 and brute._e4m3(2.0 ** -11) == 0.0
+    assert brute._e4m3(240.0) == 240.0 and brute._e4m3(250.0) == 256.0
+
+
+@pytest.mark.parametrize("w8a8", [False, True])
+def test_kv_entries_chunks_equal_one_pass(w8a8):
+    """Cache filling in chunks (here 3 tokens, so 7 tokens cross two chunk boundaries) gives the
+    entries the scalar brute force computes for positions 0..6 in one pass."""
+    w = _w8_weights(46)
+    x = np.random.default_rng(47).standard_normal((7, W8.hidden))
+    c, k = mla.kv_entries(x, w, 0, W8, w8a8=w8a8, chunk=3)
+    dims = dict(q_lora=W8.q_lora, kv_lora=W8.kv_lora, heads=W8.heads, nope=W8.nope, rope=W8.rope, v=W8.v)
+    _, ents = brute.forward(x.tolist(), to_lists(w), dims, W8.eps, W8.theta, W8.sigma,
+                            w8a8=brute.W8A8_POINTS if w8a8 else ())
+    assert np.allclose(c, np.array([e[0] for e in ents]), rtol=0, atol=1e-12)
+    assert np.allclose(k, np.array([e[1] for e in ents]), rtol=0, atol=1e-12)
+    # a later start position: chunks continue the positions
+    c5, k5 = mla.kv_entries(x, w, 5, W8, w8a8=w8a8, chunk=3)
+    lat = mla.latent_path(x, w, 5 + np.arange(7), W8, w8a8=w8a8)
+    assert np.allclose(c5, lat["c_hat"], rtol=0, atol=1e-12) and np.allclose(k5, lat["k_pe"], rtol=0, atol=1e-12)
