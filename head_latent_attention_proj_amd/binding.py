@@ -20,7 +20,7 @@ WDTYPE_FP8 = 1
 
 EXPORTED = (
     "mla_packed_weight_bytes", "mla_cache_entry_bytes", "mla_prefill_workspace_bytes",
-    "mla_decode_workspace_bytes", "mla_workspace_init", "mla_init_weights", "mla_prefill", "mla_decode",
+    "mla_decode_workspace_bytes", "mla_init_weights", "mla_prefill", "mla_decode",
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
     "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
     "mla_cache_pool_plan", "mla_cache_pool_layer",
@@ -75,8 +75,6 @@ def lib() -> ctypes.CDLL:
     L.mla_prefill_workspace_bytes.restype = sz
     L.mla_decode_workspace_bytes.argtypes = [vp, i32, i64]
     L.mla_decode_workspace_bytes.restype = sz
-    L.mla_workspace_init.argtypes = [vp, sz, vp]
-    L.mla_workspace_init.restype = ctypes.c_int
     L.mla_init_weights.argtypes = [ctypes.POINTER(MlaConfig), ctypes.POINTER(MlaWeights), vp, sz, vp,
                                    ctypes.POINTER(vp)]
     L.mla_init_weights.restype = ctypes.c_int
@@ -229,11 +227,11 @@ class Layer:
     """One MLA layer: a library context over caller-owned (torch) weights."""
 
     def __init__(self, weights: dict, max_positions: int = 131072, wdtype: int = WDTYPE_BF16, stream=None,
-                 rope_scaling: dict | None = None):
+                 rope_scaling: dict | None = None, softmax_scale: float = 0.0):
         import torch
 
         L = lib()
-        self.cfg = make_config(max_positions, wdtype, rope_scaling=rope_scaling)
+        self.cfg = make_config(max_positions, wdtype, softmax_scale=softmax_scale, rope_scaling=rope_scaling)
         self.weights = weights  # keep the referenced tensors alive
         w = MlaWeights()
         for name in ("q_a", "q_a_norm", "q_b", "kv_a", "kv_a_norm", "kv_b", "o"):
@@ -268,7 +266,6 @@ class Layer:
 
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-            check(lib().mla_workspace_init(_ptr(self._ws), self._ws.numel(), _stream(stream)))
         return self._ws
 
     def prefill_workspace_bytes(self, max_tokens: int, max_batch: int, max_keys: int) -> int:
@@ -397,7 +394,6 @@ class Gemm:
             raise MlaError(1, "invalid GEMM shape")
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=A.device)
-            check(lib().mla_workspace_init(_ptr(self._ws), self._ws.numel(), _stream(stream)))
         out_bf16 = 1 if C.dtype == torch.bfloat16 else 0
         check(lib().mla_test_gemm(M, N, K, batch, _ptr(A), lda or K, sA, _ptr(B), ldb or K, sB, _ptr(C),
                                   ldc or N, sC, out_bf16, STAGE[stage], _ptr(self._ws), self._ws.numel(),

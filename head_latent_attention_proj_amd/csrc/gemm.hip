@@ -955,7 +955,6 @@ int64_t gemm_part_floats(int M, int N, int K, int batch) {
   return pl.splits > 1 ? (int64_t)pl.splits * batch * M * N : 0;
 }
 
-int gemm_counters(int, int, int, int) { return 0; }
 
 // The rows kernel addresses each operand through a buffer descriptor: windows under 2 GiB.
 bool rows_ok(const GemmArgs& a) {

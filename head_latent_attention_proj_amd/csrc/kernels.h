@@ -49,11 +49,9 @@ struct GemmArgs {
   // (batch 1; the decoder block's residual connection fused into o_proj)
   const uint16_t* resid = nullptr;
   int64_t ldr = 0;
-  // split-K scratch (workspace): fp32 partials and per-tile arrival counters (kept zeroed)
+  // split-K scratch (workspace): fp32 partials, summed by a fixed-order reduction kernel
   float* part = nullptr;
-  int* counters = nullptr;
   int64_t part_cap = 0;     // floats available in `part`
-  int counter_cap = 0;      // counters available
 };
 
 // Chooses a tile kernel (large M) or the in-workgroup split-K kernel (small M). Returns a
@@ -64,9 +62,8 @@ int gemm_ysplit(const GemmArgs& a);
 hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s);
 int64_t gemm_fp8_part_floats(int M, int N, int K, int batch);
 int gemm_fp8_ysplit(const GemmArgs& a);
-// Bytes of split-K partials / counters the skinny path may need for an (M, N, K, batch) GEMM.
+// Floats of split-K partials a (M, N, K, batch) GEMM may need.
 int64_t gemm_part_floats(int M, int N, int K, int batch);
-int gemm_counters(int M, int N, int K, int batch);
 
 // ---------------------------------------------------------------------------------------------
 // Per-call sequence metadata (device, filled by plan_kernel at the start of a prefill)

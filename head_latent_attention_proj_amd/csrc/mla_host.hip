@@ -143,9 +143,9 @@ PackedLayout packed_layout(const mla_config* c) {
 }
 
 // ---- workspace planning ----------------------------------------------------------------------
-constexpr int N_COUNTERS = 16384;
 constexpr int QKVA_PARTS = 4;  // K splits of the fused q_a|kv_a projection at decode sizes
 constexpr int DECODE_MAX_WG = 2048;
+constexpr int MAX_BATCH = 4096;  // sequences per prefill or decode call (MLA_E_UNSUPPORTED above)
 
 struct DecodePlan {
   int chunk = 32, max_splits = 1;
@@ -168,7 +168,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n, bool fp8) {
   DecodePlan p;
   p.chunk = (int)std::max<int64_t>(64, round_up((total + D - 1) / D, 32));
   p.max_splits = (max_len + p.chunk - 1) / p.chunk;
-  while ((int64_t)B * p.max_splits > DECODE_MAX_WG) {
+  while ((int64_t)B * p.max_splits > DECODE_MAX_WG && p.max_splits > 1) {
     p.chunk *= 2;
     p.max_splits = (max_len + p.chunk - 1) / p.chunk;
   }
@@ -176,7 +176,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n, bool fp8) {
 }
 
 struct WsLayout {
-  size_t counters, cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
+  size_t cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
   size_t knope_lo, vt_lo, qs;  // FP8 only: residual planes, split q_nope
   size_t o_lat;                // decode: merged latent attention output (bf16; FP8: 2 planes)
   size_t x8, x8s, qh8s, o32, o8, o8s, total;
@@ -213,7 +213,6 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
     off = round_up(off + bytes, 256);
     return o;
   };
-  L.counters = take(N_COUNTERS * sizeof(int));
   L.cqkv = take((size_t)ntok * QKVA_N * 4 * QKVA_PARTS);
   L.q_hat = take((size_t)ntok * Q_LORA * 2);  // bf16, or FP8 codes
   L.q = take((size_t)ntok * QB_N * (fp8 ? 4 : 2));  // FP8: float32 q
@@ -246,8 +245,6 @@ mla_k::GemmArgs gemm_common(uint8_t* ws, const WsLayout& L) {
   mla_k::GemmArgs g;
   g.part = (float*)(ws + L.gpart);
   g.part_cap = L.gpart_floats;
-  g.counters = (int*)(ws + L.counters);
-  g.counter_cap = N_COUNTERS;
   return g;
 }
 
@@ -344,14 +341,6 @@ size_t mla_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t
   for (int m = 1; m <= max_batch; ++m) gp = std::max(gp, max_gemm_part(m, 0, true, ctx->fp8));
   const int64_t splits = std::min<int64_t>((int64_t)max_batch * ((max_keys + 31) / 32), DECODE_MAX_WG);
   return ws_layout(max_batch, max_batch, 0, (int)std::max<int64_t>(splits, max_batch), gp, ctx->fp8).total;
-}
-
-mla_status mla_workspace_init(void* ws, size_t ws_bytes, mla_stream stream) {
-  if (!ws) return fail(MLA_E_ARG, "workspace is NULL");
-  if (!aligned16(ws)) return fail(MLA_E_ALIGN, "workspace is not 16-byte aligned");
-  if (ws_bytes < N_COUNTERS * sizeof(int)) return fail(MLA_E_WORKSPACE, "workspace smaller than its control block");
-  HIP_TRY(mla_k::fill_zero_i32((int*)ws, N_COUNTERS, (hipStream_t)stream));
-  return MLA_OK;
 }
 
 mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* packed, size_t packed_bytes,
@@ -501,10 +490,11 @@ bool partial_overlap(const void* a, const void* b, size_t bytes) {
 mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
                         const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
                         void* ws, size_t ws_bytes, mla_stream stream, const void* norm_w) {
+  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
+  if (B > MAX_BATCH) return fail(MLA_E_UNSUPPORTED, "B = %d exceeds the %d sequences a call may hold", B, MAX_BATCH);
   if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
   mla_status st = check_cache(ctx, cache);
   if (st != MLA_OK) return st;
-  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
   if (!seq_ids_h || !seq_ids_d || !q_start_h || !q_start_d || !x || !y || !ws)
     return fail(MLA_E_ARG, "a pointer argument is NULL");
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MLA_E_ALIGN, "x, y or ws is not 16-byte aligned");
@@ -622,10 +612,11 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
 // One decode step; norm_w as in prefill_impl.
 mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
                        const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream, const void* norm_w) {
+  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
+  if (B > MAX_BATCH) return fail(MLA_E_UNSUPPORTED, "B = %d exceeds the %d sequences a call may hold", B, MAX_BATCH);
   if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
   mla_status st = check_cache(ctx, cache);
   if (st != MLA_OK) return st;
-  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
   if (!seq_ids_h || !seq_ids_d || !x || !y || !ws) return fail(MLA_E_ARG, "a pointer argument is NULL");
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MLA_E_ALIGN, "x, y or ws is not 16-byte aligned");
   std::vector<int> lens(B);
@@ -684,8 +675,11 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     HIP_TRY(mla_k::gemm_bf16_qnorm(g, na, s));
   } else {
     HIP_TRY(mla_k::norm_rope_append(na, s));
-    HIP_TRY(run_proj(ctx, g, s));
   }
+  // the entries are appended and len_d advanced by the kernel just enqueued: the host mirror
+  // follows at once, so the two stay equal even if a later launch fails
+  for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
+  if (fp8 || !mla_k::gemm_bf16_fuses_qnorm(g)) HIP_TRY(run_proj(ctx, g, s));
   // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched). FP8: W_UK as its exact code
   //    values with the block scale of (head, latent block) on the output; q_nope is float32 and
   //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out, and
@@ -741,7 +735,6 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   g.C = y; g.ldc = HIDDEN; g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
   g.resid = (const uint16_t*)resid; g.ldr = HIDDEN;
   HIP_TRY(run_proj(ctx, g, s));
-  for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += 1;
   return MLA_OK;
 }
 
@@ -830,7 +823,7 @@ mla_status mla_block_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_i
 
 size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch) {
   if (M <= 0 || N <= 0 || K <= 0 || batch <= 0 || K % 128) return 0;
-  return round_up(N_COUNTERS * sizeof(int), 256) + (size_t)mla_k::gemm_part_floats(M, N, K, batch) * 4;
+  return std::max<size_t>(256, (size_t)mla_k::gemm_part_floats(M, N, K, batch) * 4);
 }
 
 mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const void* A, int64_t lda, int64_t sA,
@@ -849,9 +842,7 @@ mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const v
   g.tag = stage;
   g.A = A; g.lda = lda; g.sA = sA; g.B = B; g.ldb = ldb; g.sB = sB; g.C = C; g.ldc = ldc; g.sC = sC;
   g.M = M; g.N = N; g.K = K; g.batch = batch; g.epi = out_bf16 ? mla_k::EPI_BF16 : mla_k::EPI_F32;
-  g.counters = (int*)ws;
-  g.counter_cap = N_COUNTERS;
-  g.part = (float*)((uint8_t*)ws + round_up(N_COUNTERS * sizeof(int), 256));
+  g.part = (float*)ws;
   g.part_cap = mla_k::gemm_part_floats(M, N, K, batch);
   HIP_TRY(mla_k::gemm_bf16(g, (hipStream_t)stream));
   return MLA_OK;

@@ -20,8 +20,9 @@
  *     "Key content up-projection" page, Parameters). bf16 tensors are IEEE bfloat16 bits.
  *   - "device" pointers are HIP device memory; "host" pointers are ordinary host memory.
  *     The caller owns every buffer; the library never allocates or frees device memory.
- *   - Every call validates all arguments on the host BEFORE it enqueues any work. On an error
- *     nothing is enqueued and no buffer (cache, lengths, outputs) is modified. Calls do not
+ *   - Every call validates all arguments on the host BEFORE it enqueues any work. On a
+ *     validation error nothing is enqueued and no buffer (cache, lengths, outputs) is modified
+ *     (for a HIP failure after the first enqueue see MLA_E_HIP). Calls do not
  *     throw; they return a status and leave a human-readable detail in mla_last_error()
  *     (thread-local).
  *   - Work is enqueued on the given stream (a hipStream_t, NULL = the default stream) and is
@@ -50,9 +51,15 @@ typedef enum {
   MLA_E_CAPACITY = 3,    /* len + new > cap of the sequence, or > max_positions. The pages'
                             code does not enforce max_position_embeddings ("KV cache" page);
                             this library does, so a slot is never written out of range. */
-  MLA_E_UNSUPPORTED = 4, /* dimensions or a weight format the kernels are not built for */
+  MLA_E_UNSUPPORTED = 4, /* dimensions or a weight format the kernels are not built for, or more
+                            than 4096 sequences in one prefill or decode call */
   MLA_E_WORKSPACE = 5,   /* workspace / packed buffer smaller than the call needs */
-  MLA_E_HIP = 6,         /* a HIP runtime call failed (detail in mla_last_error) */
+  MLA_E_HIP = 6,         /* a HIP runtime call failed (detail in mla_last_error). Validation has
+                            passed by then, so work enqueued before the failure stays enqueued
+                            and the call is partly applied; the host and device lengths stay
+                            equal either way: both advance with the launch that appends the
+                            entries (decode) or the final commit launch (prefill), and neither
+                            advances if the failure comes before it */
   MLA_E_ALIGN = 7        /* a device pointer is not 16-byte aligned */
 } mla_status;
 
@@ -153,10 +160,6 @@ size_t mla_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32
  * most max_keys positions in total after the step (sum over b of len_b + 1). */
 size_t mla_decode_workspace_bytes(const mla_ctx* ctx, int32_t max_batch, int64_t max_keys);
 
-/* Zero the workspace's control block (split-K counters). Call once after allocating a
- * workspace, before its first use; the kernels leave it zeroed after every call. */
-mla_status mla_workspace_init(void* ws, size_t ws_bytes, mla_stream stream);
-
 /* Validate cfg and weights, build the packed buffer (device, packed_bytes >=
  * mla_packed_weight_bytes(cfg)) on `stream`, and return a host context in *out.
  * The RoPE table is computed on the host in double precision and stored as float32.
@@ -172,7 +175,8 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
  *   q_start_h/_d  host/device [B+1], q_start[0] = 0, non-decreasing, T_b >= 1
  *   x             device [q_start[B], 7168] bf16, y device [q_start[B], 7168] bf16
  *   ws            device workspace of ws_bytes >= mla_prefill_workspace_bytes(ctx, q_start[B], B,
- *                 sum over b of len + T_b), initialised once with mla_workspace_init. */
+ *                 sum over b of len + T_b). The workspace holds only scratch values of the call: it needs
+ *                 no initialisation and its contents between calls do not matter. */
 mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
                        const int32_t* q_start_h, const int32_t* q_start_d, int32_t B, const void* x, void* y,
                        void* ws, size_t ws_bytes, mla_stream stream);
@@ -184,7 +188,7 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
  * W_UK, scores use [q_lat | q_pe] . [c_hat | k_pe], the value mix stays latent and W_UV is
  * applied after the softmax merge (algebraically the pages' scores and mix).
  *   x, y device [B, 7168] bf16; ws of ws_bytes >= mla_decode_workspace_bytes(ctx, B,
- *   sum over b of len + 1), initialised once with mla_workspace_init. */
+ *   sum over b of len + 1) (scratch only, as for prefill). */
 mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
                       int32_t B, const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream);
 
@@ -199,7 +203,7 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
  *   x, h         device [rows, 7168] bf16; h may be x itself (in place) or a buffer that does
  *                not overlap it (a partial overlap gives MLA_E_ARG)
  *   ws           workspace of ws_bytes >= mla_block_prefill_workspace_bytes(...) (or
- *                _decode_), initialised once with mla_workspace_init; its first
+ *                _decode_); its first
  *                rows * 7168 * 2 bytes (rounded up to 256) hold xn, the rest is the layer's.
  * Everything else (cache, positions, validation before any enqueue, errors) is exactly as for
  * mla_prefill / mla_decode. */

@@ -18,7 +18,7 @@ enum {
   MLA_STAGE_ABSORB = 5, MLA_STAGE_UV = 6
 };
 
-/* Workspace bytes mla_test_gemm needs for this shape (split-K partials and counters). */
+/* Workspace bytes mla_test_gemm needs for this shape (split-K partials). */
 size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch);
 
 /* The projection kernel on its own: for b < batch, C[b] = A[b] B[b]^T, i.e. y = x W^T of an
@@ -26,8 +26,7 @@ size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t ba
  * attention_bias is false in the config). A [M, K] (row stride lda, batch stride sA) and
  * B [N, K] (ldb, sB) are device bf16; C [M, N] (ldc, sC) is device float32 (out_bf16 = 0) or
  * bf16 (out_bf16 = 1); strides in elements. K must be a multiple of 128, lda/ldb multiples of 8.
- * ws: device workspace of ws_bytes >= mla_test_gemm_workspace_bytes(), initialised once with
- * mla_workspace_init. The same kernels and launch plan as the layer's projections are used. */
+ * ws: device workspace of ws_bytes >= mla_test_gemm_workspace_bytes() (scratch only). The same kernels and launch plan as the layer's projections are used. */
 mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const void* A, int64_t lda, int64_t sA,
                          const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC, int32_t out_bf16,
                          int32_t stage, void* ws, size_t ws_bytes, mla_stream stream);

@@ -33,6 +33,42 @@ def assert_close(gpu, ref, what: str, max_abs: float = MAX_ABS, rel_l2: float = 
     assert ma <= max_abs and rl <= rel_l2, f"{what}: max-abs {ma:.3e} rel-L2 {rl:.3e}"
 
 
+def bf16_unit(ref: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |ref| (2^(e-7) for 2^e <= |ref| < 2^(e+1); 8 significant
+    bits). Zero maps to the smallest normal spacing."""
+    a = np.maximum(np.abs(np.asarray(ref, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 7)
+
+
+def assert_bf16_rounding_of(gpu, ref, what: str, rel_floor: float = 1e-4):
+    """A bf16 value the GPU rounded from a float32 computation of an exact oracle value: within
+    one bf16 unit of the oracle (half a unit for the rounding, the rest for the float32 sums),
+    plus rel_floor of the largest |ref| for elements so close to zero that float32 summation
+    error exceeds their own bf16 spacing."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    bound = bf16_unit(ref) + rel_floor * float(np.max(np.abs(ref)))
+    worst = float(np.max(err / bound))
+    log(f"  {what}: max |err| / (1 bf16 unit + floor) = {worst:.3f}")
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert worst <= 1.0, f"{what}: an element is more than one bf16 unit from the oracle ({worst:.3f})"
+
+
+def assert_close_carried(gpu, ref, carried, what: str):
+    """A later layer of a stack: its bf16 output against the oracle's unrounded value, where the
+    residual stream also carries the earlier layers' difference `carried` (elementwise) into
+    this output unchanged. Each element within carried + the bar's max-abs; relative L2 <= 1e-2."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    _, rl = metrics(gpu, ref)
+    worst = float(np.max(err - np.asarray(carried)))
+    log(f"  {what}: max(|err| - carried) {worst:.3e} rel-L2 {rl:.3e}")
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert worst <= MAX_ABS and rl <= REL_L2, f"{what}: max(|err| - carried) {worst:.3e} rel-L2 {rl:.3e}"
+
+
 @functools.lru_cache(maxsize=1)
 def weights():
     bits = synth.make_weights_bf16(seed=0)

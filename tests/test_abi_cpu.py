@@ -97,7 +97,9 @@ def test_calls_reject_null_context(L):
     assert L.mla_block_decode_workspace_bytes(None, 1, 1) == 0
     assert L.mla_prefill_workspace_bytes(None, 1, 1, 1) == 0
     assert L.mla_decode_workspace_bytes(None, 1, 1) == 0
-    assert L.mla_workspace_init(None, 0, None) == 1
+    # more than 4096 sequences in one call: rejected before anything else is looked at
+    assert L.mla_decode(None, ctypes.byref(desc), None, None, 4097, None, None, None, 0, None) == 4
+    assert L.mla_prefill(None, ctypes.byref(desc), None, None, None, None, 4097, None, None, None, 0, None) == 4
     L.mla_destroy(None)
 
 

@@ -2,8 +2,9 @@
 h = x + MLA(xn), xn the block's input RMSNorm in bf16 ("Attention input" page, block and
 rmsnorm excerpts), against the float64 oracle's block_attention on the same seeded inputs.
 
-Bar: max-abs-err <= 2e-2 and relative L2 <= 1e-2 on h (bf16), and on h - x (the attention's
-contribution, which the residual would otherwise dominate) relative L2 <= 1e-2.
+Bar: max-abs-err <= 2e-2 and relative L2 <= 1e-2 on h (bf16) against the oracle's unrounded
+x + y, and on h - x (the attention's contribution, which the residual would otherwise dominate)
+against y.
 """
 import functools
 
@@ -26,8 +27,10 @@ def norm_gain():
 
 
 def check_block(h_gpu, x64, ref, what):
-    assert_close(h_gpu, ref["h"], f"{what} h")
-    assert_close(h_gpu - x64, ref["h"] - x64, f"{what} h - x", max_abs=2e-2, rel_l2=1e-2)
+    # the oracle's h is its bf16 rounding of x + y; the GPU's h is its own rounding of x + y_gpu, so
+    # each is held against the unrounded sum (the GPU's rounding counts as its error)
+    assert_close(h_gpu, x64 + ref["y"], f"{what} h")
+    assert_close(h_gpu - x64, ref["y"], f"{what} h - x", max_abs=2e-2, rel_l2=1e-2)
 
 
 @pytest.mark.parametrize("in_place", [False, True])

@@ -10,8 +10,9 @@ launch configuration the benchmark times.
     sequences with 16384 cached positions each, and prefill of 4 sequences of 4096 tokens.
 
 Long caches hold synthetic entries (the latent stands for RMSNorm outputs, the rotary key for a
-projection of N(0,1) inputs); for FP8 one sequence's 16384 entries are quantised by the oracle's
-quantiser and copied to all 128 sequences, each of which gets its own new token.
+projection of N(0,1) inputs); for FP8 the oracle's quantiser packs the entries, the sampled
+sequences and their neighbours get caches of their own and the others share one, and every
+sequence gets its own new token.
 Bar: max-abs-err <= 2e-2 and relative L2 <= 1e-2 on the bf16 outputs.
 """
 import functools
@@ -22,7 +23,7 @@ import pytest
 from head_latent_attention_proj_amd import binding, synth
 from oracle import mla as omla
 
-from gpu_common import assert_close, entries_f64, layer, log, weights, y_of
+from gpu_common import assert_bf16_rounding_of, assert_close, entries_f64, layer, log, weights, y_of
 from test_gpu_fp8 import fp8_setup, pack_fp8_entries
 
 pytestmark = pytest.mark.gpu
@@ -43,8 +44,8 @@ def test_prefill_8192_tokens_sampled_rows():
     ref = omla.forward(synth.bf16_bits_to_f64(xbits), w64, rows=rows, absorbed=True)
     assert_close(y[rows], ref["y"], f"y at rows {rows.tolist()}")
     c_gpu, k_gpu = entries_f64(cache.slots(0).cpu().numpy()[rows])
-    assert_close(c_gpu, ref["c_hat"][rows], "cached c_hat at the sampled positions")
-    assert_close(k_gpu, ref["k_pe"][rows], "cached k_pe at the sampled positions")
+    assert_bf16_rounding_of(c_gpu, ref["c_hat"][rows], "cached c_hat at the sampled positions")
+    assert_bf16_rounding_of(k_gpu, ref["k_pe"][rows], "cached k_pe at the sampled positions")
 
 
 def test_decode_64_sequences_lengths_1024_to_8192():
@@ -84,22 +85,35 @@ def test_fp8_decode_128_sequences_16384_positions():
     import torch
 
     B, P = 128, 16384
-    log(f"full-size FP8 decode B={B}, {P} cached positions each")
+    own = (0, 1, 76, 77, 78, 126, 127)  # the sampled sequences and their neighbours
+    log(f"full-size FP8 decode B={B}, {P} cached positions each; distinct caches for {own}")
     wq, w64, _ = fp8_setup()
     L = fp8_long_layer()
-    e = synth.bf16_bits_to_f64(synth.make_cache_entries(P, seed=5300))
-    raw, c_dq = pack_fp8_entries(e[:, :512], e[:, 512:])
-    kpe = e[:, 512:].astype(np.float32).astype(np.float64)
     cache = binding.Cache(L, [P + 1] * B)
-    raw_t = torch.from_numpy(raw).cuda()
+
+    def entries(seed):
+        e = synth.bf16_bits_to_f64(synth.make_cache_entries(P, seed=seed))
+        raw, c_dq = pack_fp8_entries(e[:, :512], e[:, 512:])
+        return torch.from_numpy(raw).cuda(), (c_dq, e[:, 512:].astype(np.float32).astype(np.float64))
+
+    base_t, base_ref = entries(5300)
+    refs = {}
     for s in range(B):
-        L.cache_append(cache, s, raw_t)
+        if s in own:
+            t, refs[s] = entries(5301 + s)
+            L.cache_append(cache, s, t)
+        else:
+            L.cache_append(cache, s, base_t)
+    refs[40] = base_ref
     xn = synth.make_hidden(B, seed=5400)
-    y = y_of(L.decode(cache, np.arange(B), binding.bf16_tensor(xn)))
+    order = np.random.default_rng(9).permutation(B).astype(np.int32)  # batch order != sequence ids
+    y = y_of(L.decode(cache, order, binding.bf16_tensor(xn[order])))
     torch.cuda.synchronize()
-    for s in (0, 77, B - 1):
-        ref = omla.forward(synth.bf16_bits_to_f64(xn[s:s + 1]), w64, cache=(c_dq, kpe), w8a8=True, absorbed=True)
-        assert_close(y[s:s + 1], ref["y"], f"seq {s} (L={P})")
+    pos_of = {int(s): i for i, s in enumerate(order)}
+    for s in (0, 77, B - 1, 40):
+        ref = omla.forward(synth.bf16_bits_to_f64(xn[s:s + 1]), w64, cache=refs[s], w8a8=True, absorbed=True)
+        assert_close(y[pos_of[s]:pos_of[s] + 1], ref["y"], f"seq {s} (L={P})")
+    assert np.all(cache.len_d.cpu().numpy() == P + 1)
 
 
 def test_fp8_prefill_4_sequences_4096_tokens():

@@ -1,7 +1,7 @@
 """GPU parity of the projection kernel (mla_test_gemm) against float64 matmul of the same bf16 bits.
 
 Covers the skinny (decode-sized M) and tile (prefill-sized M) kernels, split-K with its
-last-arrival reduction, batched per-head products with strides, and ragged M/N tails.
+fixed-order reduction kernel, batched per-head products with strides, and ragged M/N tails.
 """
 import numpy as np
 import pytest

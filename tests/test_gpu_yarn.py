@@ -10,7 +10,7 @@ import pytest
 from head_latent_attention_proj_amd import binding, synth
 from oracle import mla as omla
 
-from gpu_common import assert_close, entries_f64, log, weights, y_of
+from gpu_common import assert_bf16_rounding_of, assert_close, entries_f64, log, weights, y_of
 
 pytestmark = pytest.mark.gpu
 YARN = omla.KIMI_K2_YARN
@@ -48,9 +48,9 @@ def test_yarn_prefill_then_decode(torch_cuda, yarn_layer):
     # the cached shared keys are rotated with the YaRN table (and differ from plain RoPE's)
     c_gpu, k_gpu = entries_f64(cache.slots(0).cpu().numpy()[:42])
     c_ref, k_ref = omla.kv_entries(x64, w64, cfg=YARN)
-    # (bf16 slots: half an ulp is 1.6e-2 at |x| ~ 6, hence the wider bound, as for plain RoPE)
-    assert_close(k_gpu, k_ref, "YaRN cached k_pe", max_abs=3e-2)
-    assert_close(c_gpu, c_ref, "YaRN cached c_hat", max_abs=3e-2)
+    # bf16 slots: each value within one bf16 unit of the oracle's
+    assert_bf16_rounding_of(k_gpu, k_ref, "YaRN cached k_pe")
+    assert_bf16_rounding_of(c_gpu, c_ref, "YaRN cached c_hat")
     # the slowed pairs (20..31, features 40..63) have turned visibly less than under plain RoPE
     _, k_plain = omla.kv_entries(x64, w64)
     assert np.max(np.abs(k_ref[20:, 40:] - k_plain[20:, 40:])) > 0.05
