@@ -24,7 +24,7 @@ EXPORTED = (
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
     "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
     "mla_cache_pool_plan", "mla_cache_pool_layer",
-    "mla_test_gemm_workspace_bytes", "mla_test_gemm",
+    "mla_test_gemm_workspace_bytes", "mla_test_gemm", "mla_decode_static",
 )
 STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6}
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.mla_prefill.restype = ctypes.c_int
     L.mla_decode.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp, sz, vp]
     L.mla_decode.restype = ctypes.c_int
+    L.mla_decode_static.argtypes = [vp, ctypes.POINTER(MlaCacheDesc), vp, vp, i32, vp, vp, vp]
+    L.mla_decode_static.restype = ctypes.c_int
     L.mla_block_prefill_workspace_bytes.argtypes = [vp, i32, i32, i64]
     L.mla_block_prefill_workspace_bytes.restype = sz
     L.mla_block_decode_workspace_bytes.argtypes = [vp, i32, i64]
@@ -308,6 +310,22 @@ class Layer:
             seq_ids_d = torch.from_numpy(seq_ids).to(x.device)
         check(lib().mla_decode(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(seq_ids_d), B,
                                _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+        self._keep = (seq_ids_d,)
+        return y
+
+    def decode_static(self, cache: Cache, seq_ids, x, y=None, seq_ids_d=None, stream=None):
+        """mla_decode_static: the same step as decode() on the library's own static scratch (no
+        workspace, nothing allocated by the call itself). Returns y [B, 7168] bf16."""
+        import torch
+
+        seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        B = len(seq_ids)
+        if y is None:
+            y = torch.empty_like(x)
+        if seq_ids_d is None:
+            seq_ids_d = torch.from_numpy(seq_ids).to(x.device)
+        check(lib().mla_decode_static(self.ctx, ctypes.byref(cache.desc), seq_ids.ctypes.data, _ptr(seq_ids_d), B,
+                                      _ptr(x), _ptr(y), _stream(stream)))
         self._keep = (seq_ids_d,)
         return y
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -17,6 +18,14 @@
 #include "kernels.h"
 
 using namespace mla_dims;
+
+// ---- the allocation-free decode (mla_decode_static): its workspace is this file-scope device
+// array, one copy per GPU the library runs on, held until the process ends. In host code the
+// name `scratch` is only a host-side stand-in; kernels receive the device address obtained from
+// hipGetSymbolAddress for the current device.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+static_assert(STATIC_SCRATCH_BYTES == MLA_STATIC_SCRATCH_BYTES, "header and library agree on the size");
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -70,6 +79,27 @@ __global__ void widen_uv_kernel(const uint8_t* kvb, uint16_t* uvw) {
   const int d = idx / KV_LORA, c = idx % KV_LORA;
   uvw[(int64_t)h * VD * KV_LORA + idx] =
       f2bf(__builtin_amdgcn_cvt_f32_fp8((int)kvb[((int64_t)h * 256 + 128 + d) * KV_LORA + c], 0));
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of this GPU's scratch array, resolved once per device with that device current.
+mla_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MLA_E_UNSUPPORTED, "device %d beyond the %d the library tracks", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(MLA_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
 }
 
 }  // namespace
@@ -418,6 +448,11 @@ mla_status mla_init_weights(const mla_config* cfg, const mla_weights* w, void* p
   }
   HIP_TRY(hipMemcpyAsync(pk + L.rope, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, s));
   HIP_TRY(hipStreamSynchronize(s));
+  {  // resolve this device's static scratch address now, so the allocation-free decode need not
+    void* unused = nullptr;
+    const mla_status ss = scratch_for_current_device(&unused);
+    if (ss != MLA_OK) return ss;
+  }
 
   mla_ctx* c = new mla_ctx;
   c->cfg = *cfg;
@@ -619,7 +654,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   if (st != MLA_OK) return st;
   if (!seq_ids_h || !seq_ids_d || !x || !y || !ws) return fail(MLA_E_ARG, "a pointer argument is NULL");
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MLA_E_ALIGN, "x, y or ws is not 16-byte aligned");
-  std::vector<int> lens(B);
+  int lens[MAX_BATCH];  // no host allocation on the decode path (see mla_decode_static)
   for (int b = 0; b < B; ++b) {
     for (int c = 0; c < b; ++c)
       if (seq_ids_h[c] == seq_ids_h[b]) return fail(MLA_E_ARG, "sequence id %d appears twice", seq_ids_h[b]);
@@ -627,7 +662,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     if (st != MLA_OK) return st;
     lens[b] = cache->len_h[seq_ids_h[b]] + 1;
   }
-  const DecodePlan dp = plan_decode(B, lens.data(), B, ctx->fp8);
+  const DecodePlan dp = plan_decode(B, lens, B, ctx->fp8);
   const int64_t gp = max_gemm_part(B, 0, true, ctx->fp8);
   const WsLayout L = ws_layout(B, B, 0, B * dp.max_splits, gp, ctx->fp8);
   const size_t xn_bytes = norm_w ? block_xn_bytes(B) : 0;
@@ -751,6 +786,17 @@ mla_status mla_prefill(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
 mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d, int32_t B,
                       const void* x, void* y, void* ws, size_t ws_bytes, mla_stream stream) {
   return decode_impl(ctx, cache, seq_ids_h, seq_ids_d, B, x, y, ws, ws_bytes, stream, nullptr);
+}
+
+mla_status mla_decode_static(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
+                             int32_t B, const void* x, void* y, mla_stream stream) {
+  if (B <= 0) return fail(MLA_E_ARG, "B must be positive");
+  if (B > MAX_BATCH) return fail(MLA_E_UNSUPPORTED, "B = %d exceeds the %d sequences a call may hold", B, MAX_BATCH);
+  if (!ctx) return fail(MLA_E_ARG, "ctx is NULL");
+  void* ws = nullptr;
+  const mla_status st = scratch_for_current_device(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl(ctx, cache, seq_ids_h, seq_ids_d, B, x, y, ws, STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 mla_status mla_cache_pool_plan(const mla_config* cfg, int32_t n_layers, int32_t n_seqs, const int32_t* cap_h,
