@@ -24,9 +24,10 @@ EXPORTED = (
     "mla_cache_append", "mla_destroy", "mla_status_str", "mla_last_error",
     "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
     "mla_cache_pool_plan", "mla_cache_pool_layer",
-    "mla_test_gemm_workspace_bytes", "mla_test_gemm", "mla_decode_static",
+    "mla_test_gemm_workspace_bytes", "mla_test_gemm", "mla_decode_static", "mla_test_probe_stage",
 )
-STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6}
+STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6, "decode_attn": 7,
+         "prefill_attn": 8}
 
 
 class MlaConfig(ctypes.Structure):
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
     L.mla_test_gemm_workspace_bytes.restype = sz
     L.mla_test_gemm.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32, vp, sz, vp]
     L.mla_test_gemm.restype = ctypes.c_int
+    L.mla_test_probe_stage.argtypes = [i32, vp, vp]
+    L.mla_test_probe_stage.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -370,6 +373,13 @@ class Layer:
         """entries: cuda tensor holding n * entry_bytes bytes in the slot format."""
         n = entries.numel() * entries.element_size() // self.entry_bytes
         check(lib().mla_cache_append(self.ctx, ctypes.byref(cache.desc), seq, _ptr(entries), n, _stream(stream)))
+
+
+def probe_stage(stage: str, ev_before, ev_after) -> None:
+    """Arm mla_test_probe_stage for the next layer call on this thread: the two torch.cuda.Event
+    objects (each recorded once before, so that they exist) are recorded around `stage`."""
+    check(lib().mla_test_probe_stage(STAGE[stage], ctypes.c_void_p(ev_before.cuda_event),
+                                     ctypes.c_void_p(ev_after.cuda_event)))
 
 
 def weights_to_device(wbits: dict, device="cuda") -> dict:

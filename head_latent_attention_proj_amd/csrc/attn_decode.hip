@@ -889,18 +889,22 @@ __global__ __launch_bounds__(512) void decode_merge_uv_kernel(DecodeAttnArgs a) 
 
 }  // namespace
 
-hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s) {
+hipError_t decode_attention_splits(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  dim3 g1(a.max_splits, a.B), g2(64, a.B);
-  if (a.fp8) {
+  dim3 g1(a.max_splits, a.B);
+  if (a.fp8)
     hipLaunchKernelGGL(decode_attn_kernel<true>, g1, dim3(512), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  else
+    hipLaunchKernelGGL(decode_attn_bf16_kernel, g1, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t decode_attention_merge(const DecodeAttnArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  dim3 g2(64, a.B);
+  if (a.fp8) {
     hipLaunchKernelGGL(decode_merge_kernel<true>, g2, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(decode_attn_bf16_kernel, g1, dim3(512), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (a.w_uv) {
       if (a.B > MERGE_UV_MAX_B) return hipErrorInvalidValue;
       hipLaunchKernelGGL(decode_merge_uv_kernel, dim3(128, a.B), dim3(512), 0, s, a);

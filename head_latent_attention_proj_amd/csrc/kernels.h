@@ -180,9 +180,10 @@ struct DecodeAttnArgs {
   uint16_t* o;
 };
 constexpr int MERGE_UV_MAX_B = 4;
-// Split attention + merge. Output: o_lat (see DecodeAttnArgs), W_UV applied by the caller; or,
-// with w_uv set, o.
-hipError_t decode_attention(const DecodeAttnArgs& a, hipStream_t s);
+// Split attention (partials) and the merge of the splits, as two launches. Output of the merge:
+// o_lat (see DecodeAttnArgs), W_UV applied by the caller; or, with w_uv set, o.
+hipError_t decode_attention_splits(const DecodeAttnArgs& a, hipStream_t s);
+hipError_t decode_attention_merge(const DecodeAttnArgs& a, hipStream_t s);
 
 // FP8 activation quantiser for a bf16/fp32 matrix [rows, K] (K multiple of 128).
 // x2 (optional): a second matrix added to x element-wise before quantising (same layout).

@@ -49,6 +49,23 @@ mla_status fail(mla_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---- stage probe (mla_test_probe_stage): one-shot, per thread. The next call on this thread
+// that launches the armed stage records ev0 on its stream right before that stage's launches
+// and ev1 right after them, then disarms.
+thread_local int g_probe_stage = 0;
+thread_local hipEvent_t g_probe_ev0 = nullptr, g_probe_ev1 = nullptr;
+
+#define PROBED(stage, expr)                                     \
+  do {                                                          \
+    const bool on_ = g_probe_stage == (stage);                  \
+    if (on_) HIP_TRY(hipEventRecord(g_probe_ev0, s));           \
+    HIP_TRY(expr);                                              \
+    if (on_) {                                                  \
+      HIP_TRY(hipEventRecord(g_probe_ev1, s));                  \
+      g_probe_stage = 0;                                        \
+    }                                                           \
+  } while (0)
+
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // ---- per-head W_UK^T: ukT[h][c][d] = W_UK,h[d][c] = kv_b[h*256 + d][c]  (d < 128, c < 512), as bf16.
@@ -627,7 +644,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   pa.kpe_off = fp8 ? KV_LORA + 16 : KV_LORA * 2;
   pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
   pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o); pa.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr;
-  HIP_TRY(mla_k::prefill_attention(pa, s));
+  PROBED(MLA_STAGE_PREFILL_ATTN, mla_k::prefill_attention(pa, s));
   // 6. o_proj
   if (fp8)
     HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), nullptr, O_IN, ntok, O_IN, w + L.o8,
@@ -637,7 +654,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
   g.C = y; g.ldc = HIDDEN; g.M = ntok; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
   g.resid = (const uint16_t*)resid; g.ldr = HIDDEN;
-  HIP_TRY(run_proj(ctx, g, s));
+  PROBED(MLA_STAGE_OPROJ, run_proj(ctx, g, s));
   // 7. lengths
   HIP_TRY(mla_k::commit_lengths(seq_ids_d, q_start_d, cache->len_d, B, s));
   for (int b = 0; b < B; ++b) cache->len_h[seq_ids_h[b]] += q_start_h[b + 1] - q_start_h[b];
@@ -744,7 +761,8 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   if (fuse_uv) {
     da.w_uv = (const uint16_t*)ctx->w_uv; da.uv_head_stride = ctx->uv_head_stride; da.o = (uint16_t*)(w + L.o);
   }
-  HIP_TRY(mla_k::decode_attention(da, s));
+  PROBED(MLA_STAGE_DECODE_ATTN, mla_k::decode_attention_splits(da, s));
+  HIP_TRY(mla_k::decode_attention_merge(da, s));
   // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (already
   //    scaled by the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the
   //    exact code values, two float32 products that the quantiser adds.
@@ -769,7 +787,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;
   g.C = y; g.ldc = HIDDEN; g.M = B; g.N = HIDDEN; g.K = O_IN; g.epi = mla_k::EPI_BF16; g.tag = mla_k::TAG_OPROJ;
   g.resid = (const uint16_t*)resid; g.ldr = HIDDEN;
-  HIP_TRY(run_proj(ctx, g, s));
+  PROBED(MLA_STAGE_OPROJ, run_proj(ctx, g, s));
   return MLA_OK;
 }
 
@@ -870,6 +888,20 @@ mla_status mla_block_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_i
 size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch) {
   if (M <= 0 || N <= 0 || K <= 0 || batch <= 0 || K % 128) return 0;
   return std::max<size_t>(256, (size_t)mla_k::gemm_part_floats(M, N, K, batch) * 4);
+}
+
+mla_status mla_test_probe_stage(int32_t stage, void* ev_before, void* ev_after) {
+  if (stage == MLA_STAGE_NONE) {
+    g_probe_stage = 0;
+    return MLA_OK;
+  }
+  if (stage != MLA_STAGE_OPROJ && stage != MLA_STAGE_DECODE_ATTN && stage != MLA_STAGE_PREFILL_ATTN)
+    return fail(MLA_E_ARG, "stage %d cannot be probed", stage);
+  if (!ev_before || !ev_after) return fail(MLA_E_ARG, "an event is NULL");
+  g_probe_ev0 = (hipEvent_t)ev_before;
+  g_probe_ev1 = (hipEvent_t)ev_after;
+  g_probe_stage = stage;
+  return MLA_OK;
 }
 
 mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const void* A, int64_t lda, int64_t sA,

@@ -15,8 +15,19 @@ extern "C" {
  * identical; the symbol lets traces attribute time to a stage). */
 enum {
   MLA_STAGE_NONE = 0, MLA_STAGE_QKVA = 1, MLA_STAGE_QB = 2, MLA_STAGE_KVB = 3, MLA_STAGE_OPROJ = 4,
-  MLA_STAGE_ABSORB = 5, MLA_STAGE_UV = 6
+  MLA_STAGE_ABSORB = 5, MLA_STAGE_UV = 6, MLA_STAGE_DECODE_ATTN = 7, MLA_STAGE_PREFILL_ATTN = 8
 };
+
+/* Stage probe for measurement: arms a one-shot probe on the calling thread. The next layer call
+ * (prefill, decode, their block and static forms) made from this thread that launches `stage`
+ * records ev_before (a hipEvent_t) on the call's stream right before that stage's launches and
+ * ev_after right after them, then disarms; their elapsed time is the stage's duration on the
+ * stream. Stages: MLA_STAGE_OPROJ (o_proj with its split-K reduction, if any),
+ * MLA_STAGE_DECODE_ATTN (the split attention over the latent cache, without the merge),
+ * MLA_STAGE_PREFILL_ATTN (causal prefill attention); MLA_STAGE_NONE disarms. The events are the
+ * caller's and must stay valid until the call has been enqueued. MLA_E_ARG for another stage or
+ * a NULL event. */
+mla_status mla_test_probe_stage(int32_t stage, void* ev_before, void* ev_after);
 
 /* Workspace bytes mla_test_gemm needs for this shape (split-K partials). */
 size_t mla_test_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t batch);
