@@ -164,7 +164,7 @@ def main():
     w8_bytes = sum(int(v.nbytes) for v in wq.values())
     cache8 = 784 * B8 * (P8 + 1)
     head_bytes = w8_bytes + cache8 + 2 * 2 * 7168 * B8
-    head_roof = roofline("decode_attn_kernel<true> (FP8 latent cache, split attention)", "hbm", cache8, t_attn8,
+    head_roof = roofline("decode_attn_fp8_kernel (FP8 latent cache, split attention)", "hbm", cache8, t_attn8,
                          "bytes: 784 per cached position (all 64 heads), 128 x 16385 positions")
     head_roof["traffic"] = counted_traffic("fp8_decode_attn")
     head_roof["step_share"] = round(t_attn8 / t_head, 3)

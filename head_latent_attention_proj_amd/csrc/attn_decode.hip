@@ -12,10 +12,15 @@
 // features ("KV cache" page: 20,480 vs 576 values per position).
 //
 // FP8 cache entries hold the latent as E4M3FN codes with one float32 scale per 128 features
-// (the quantised RMSNorm output, which is exactly what kv_b consumes). Codes are widened to bf16
-// exactly while staging; the group scales are applied per position to the partial scores of
-// each group and to the probabilities of the value mix, so no product is rounded before its
-// scale is applied.
+// (the quantised RMSNorm output, which is exactly what kv_b consumes). Codes are widened exactly
+// to fp16 while staging (every E4M3 value is an fp16 value); the group scales are applied per
+// position to the partial scores of each group and to the probabilities of the value mix.
+// Operand precision (chosen from a CPU emulation of this kernel's roundings against the W8A8
+// float64 layer, whose o_proj input quantiser turns any error of o into flipped codes): the
+// queries and the rotary key are fp16 (11 significant bits; one MFMA per score product), the
+// probabilities times the group scales are carried as fp16 high + residual parts (about 22 bits),
+// because a single rounding of them moves the output of a one- or two-key decode by up to
+// 1.9e-2 max-abs.
 //
 // Work layout: one workgroup = (sequence, split of `chunk` positions), 8 waves = 4 head groups of
 // 16 x 2 feature halves. Heads are the MFMA column dimension, so one 32-position block staged in
@@ -52,20 +57,24 @@ MLA_DEV u32x2_t ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-// four E4M3FN codes (one 32-bit word) -> two packed bf16 pairs (exact: every E4M3 value is a
-// bf16 value; gfx950 converts a code pair to a bf16 pair in one instruction, unit scale)
-MLA_DEV u32x2_t e4m3x4_to_bf16(uint32_t w) {
-  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+// four E4M3FN codes (one 32-bit word) -> two packed fp16 pairs (exact; gfx950 converts a code
+// pair to an fp16 pair in one instruction, unit scale)
+MLA_DEV u32x2_t e4m3x4_to_f16(uint32_t w) {
+  const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
   return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// 8 waves: wave = hg + 4*lh, head group hg (heads hg*16 .. +15), half lh. A wave forms the
-// partial scores of its 16 heads over features [lh*288, lh*288+288) and, after the two halves
-// are added through LDS, mixes latent features [lh*256, lh*256+256). Two waves per SIMD hide
-// each other's LDS and memory latency; per-wave registers stay well under 256.
-template <bool FP8>
-__global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
+// Probabilities enter the value mix times the position's group scale and this power of two, so that
+// their fp16 high and residual parts stay in fp16's normal range (p <= 2^8 after the lazy rescale,
+// group scales of RMSNorm outputs far below 1); the partial outputs are scaled back on the way out.
+constexpr float P_PRESCALE = 64.0f;
+
+// FP8 cache entries. 8 waves: wave = hg + 4*lh, head group hg (heads hg*16 .. +15), half lh. A
+// wave forms the partial scores of its 16 heads over features [lh*288, lh*288+288) and, after the
+// two halves are added through LDS, mixes latent features [lh*256, lh*256+256). Two waves per SIMD
+// hide each other's LDS and memory latency.
+__global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs a) {
   using namespace mla_dims;
   const int split = blockIdx.x, b = blockIdx.y;
   const int seq = a.seq_ids[b];
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int64_t slot0 = a.offset[seq];
   const int nblk = cdiv(c1 - c0, DKB);
   const int eb = a.entry_bytes;
-  const int kpe_off = FP8 ? KV_LORA + 16 : KV_LORA * 2;
+  constexpr int kpe_off = KV_LORA + 16;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -84,98 +93,54 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const int head = hg * 16 + l16;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];
-  __shared__ __attribute__((aligned(16))) float xS[8][64][12];  // partial scores [wave][lane][8 + pad]
-  __shared__ __attribute__((aligned(16))) float sScale[4][DKB];  // FP8 group scales [group][position]
-  // FP8: low bf16 halves of the float32 rotary key (high halves sit in sC)
-  __shared__ __attribute__((aligned(16))) uint16_t sKlo[FP8 ? DKB * 72 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];      // fp16 [position][576 + pad]
+  __shared__ __attribute__((aligned(16))) float xS[8][64][12];         // partial scores [wave][lane][8 + pad]
+  __shared__ __attribute__((aligned(16))) float sScale[4][DKB];        // group scales [group][position]
 
-  // ---- staging through registers, one block ahead.
-  // bf16: latent part as position pairs, item i (0..1) of a thread is pair kp = lane & 15 and
-  //       16-byte chunk ch = (lane >> 4) + 4*(wave + 8*i) (8 features);
-  // FP8:  pair kp = tid & 15 and code chunk cc = tid >> 4 (16 features);
-  // k_pe: bf16 threads 0..255 one chunk each, FP8 (float32) every thread one chunk of 4 features;
-  // FP8 scales: threads 256..287 one position each.
-  u32x4_t rl[2][2], rp, rs;
+  // ---- staging through registers, one block ahead: codes as position pairs (pair kp = tid & 15,
+  // 16-code chunk cc = tid >> 4), the rotary key (every thread one chunk of 4 float32 features),
+  // group scales (threads 256..287 one position each)
+  u32x4_t rl[2], rp, rs;
   auto gload = [&](int blk) {
     const int kb = c0 + blk * DKB;
-    if constexpr (FP8) {
-      const int kp = tid & 15, cc = tid >> 4;
+    const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int key = min(kb + 2 * kp + u, c1 - 1);  // past the split's end: re-read (masked)
-        rl[0][u] = ld16(a.cache + (slot0 + key) * eb + cc * 16);
-      }
-      if (tid >= 256 && tid < 256 + DKB) {
-        const int key = min(kb + (tid - 256), c1 - 1);
-        rs = ld16(a.cache + (slot0 + key) * eb + KV_LORA);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int kp = lane & 15;
-        const int ch = (lane >> 4) + 4 * (wave + 8 * i);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int key = min(kb + 2 * kp + u, c1 - 1);
-          rl[i][u] = ld16(a.cache + (slot0 + key) * eb + ch * 16);
-        }
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int key = min(kb + 2 * kp + u, c1 - 1);  // past the split's end: re-read (masked)
+      rl[u] = ld16(a.cache + (slot0 + key) * eb + cc * 16);
     }
-    if constexpr (FP8) {
-      const int key = min(kb + (tid >> 4), c1 - 1);
-      rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 15) * 16);
-    } else if (tid < 256) {
-      const int key = min(kb + (tid >> 3), c1 - 1);
-      rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 7) * 16);
+    if (tid >= 256 && tid < 256 + DKB) {
+      const int key = min(kb + (tid - 256), c1 - 1);
+      rs = ld16(a.cache + (slot0 + key) * eb + KV_LORA);
     }
-  };
-  auto put_pair = [&](int kp, int f0, const u32x4_t& x4, const u32x4_t& y4) {
-    // 8 bf16 features f0.. of positions 2kp (x4) and 2kp+1 (y4), row-major (the value mix reads
-    // columns with transpose reads)
-    st16(sC + (2 * kp) * LDC + f0, x4);
-    st16(sC + (2 * kp + 1) * LDC + f0, y4);
+    const int key = min(kb + (tid >> 4), c1 - 1);
+    rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 15) * 16);
   };
   auto sstore = [&]() {
-    if constexpr (FP8) {
-      const int kp = tid & 15, cc = tid >> 4;
+    const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {  // codes 8*hlf .. 8*hlf+7 of the chunk
-        const u32x2_t x01 = e4m3x4_to_bf16(rl[0][0][2 * hlf]), x23 = e4m3x4_to_bf16(rl[0][0][2 * hlf + 1]);
-        const u32x2_t y01 = e4m3x4_to_bf16(rl[0][1][2 * hlf]), y23 = e4m3x4_to_bf16(rl[0][1][2 * hlf + 1]);
-        put_pair(kp, cc * 16 + hlf * 8, u32x4_t{x01[0], x01[1], x23[0], x23[1]},
-                 u32x4_t{y01[0], y01[1], y23[0], y23[1]});
-      }
-      if (tid >= 256 && tid < 256 + DKB) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[q]);
-      }
-      // rotary key: 4 float32 features -> bf16 high halves (sC) and low halves (sKlo)
-      const int pos = tid >> 4, f4 = (tid & 15) * 4;
-      float v[4], r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = __uint_as_float(rp[j]);
-        r[j] = v[j] - bf2f(f2bf(v[j]));
-      }
-      *reinterpret_cast<u32x2_t*>(sC + pos * LDC + KV_LORA + f4) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *reinterpret_cast<u32x2_t*>(sKlo + pos * 72 + f4) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int kp = lane & 15;
-        const int ch = (lane >> 4) + 4 * (wave + 8 * i);
-        put_pair(kp, ch * 8, rl[i][0], rl[i][1]);
-      }
-      if (tid < 256) st16(sC + (tid >> 3) * LDC + KV_LORA + (tid & 7) * 8, rp);
+    for (int hlf = 0; hlf < 2; ++hlf) {  // codes 8*hlf .. 8*hlf+7 of the chunk, positions 2kp and 2kp+1
+      const u32x2_t x01 = e4m3x4_to_f16(rl[0][2 * hlf]), x23 = e4m3x4_to_f16(rl[0][2 * hlf + 1]);
+      const u32x2_t y01 = e4m3x4_to_f16(rl[1][2 * hlf]), y23 = e4m3x4_to_f16(rl[1][2 * hlf + 1]);
+      st16(sC + (2 * kp) * LDC + cc * 16 + hlf * 8, u32x4_t{x01[0], x01[1], x23[0], x23[1]});
+      st16(sC + (2 * kp + 1) * LDC + cc * 16 + hlf * 8, u32x4_t{y01[0], y01[1], y23[0], y23[1]});
     }
+    if (tid >= 256 && tid < 256 + DKB) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[q]);
+    }
+    // rotary key: 4 float32 features -> fp16
+    const int pos = tid >> 4, f4 = (tid & 15) * 4;
+    *reinterpret_cast<u32x2_t*>(sC + pos * LDC + KV_LORA + f4) =
+        u32x2_t{pack_f16x2(__uint_as_float(rp[0]), __uint_as_float(rp[1])),
+                pack_f16x2(__uint_as_float(rp[2]), __uint_as_float(rp[3]))};
   };
   gload(0);  // in flight during the query set-up
 
-  // ---- query fragments (B operand): column = head, features lh*288 + ks*32 + g*8 .. +7;
-  // features >= 512 are the rotary part, rotated here at the query's position
-  // FP8: the queries are float32 and are carried as hi + lo bf16 fragments (about 16 bits)
-  bf16x8_t qf[9], ql_[FP8 ? 9 : 1];
+  // ---- query fragments (B operand), fp16: column = head, features lh*288 + ks*32 + g*8 .. +7;
+  // the latent part is the sum of the two float32 absorbed products, features >= 512 are the rotary
+  // part, rotated here at the query's position
+  f16x8_t qf[9];
   {
     const int pos = L - 1;
 #pragma unroll
@@ -183,39 +148,20 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
       const int f = lh * HALF + ks * 32 + g * 8;
       float v[8];
       if (f < KV_LORA) {
-        if constexpr (FP8) {
-          const float* qlf = (const float*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f;
-          const float* qlr = qlf + a.q_lat_lo;
-          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qlf), v1 = *reinterpret_cast<const f32x4_t*>(qlf + 4);
-          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(qlr), r1 = *reinterpret_cast<const f32x4_t*>(qlr + 4);
+        const float* qlf = (const float*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f;
+        const float* qlr = qlf + a.q_lat_lo;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qlf), v1 = *reinterpret_cast<const f32x4_t*>(qlf + 4);
+        const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(qlr), r1 = *reinterpret_cast<const f32x4_t*>(qlr + 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[j] = v0[j] + r0[j];
-            v[4 + j] = v1[j] + r1[j];
-          }
-        } else {
-          qf[ks] = as_bf16x8(ld16((const uint16_t*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f));
-          continue;
+        for (int j = 0; j < 4; ++j) {
+          v[j] = v0[j] + r0[j];
+          v[4 + j] = v1[j] + r1[j];
         }
       } else {
         const int pair0 = (f - KV_LORA) >> 1;
-        float x[8];
-        if constexpr (FP8) {
-          const float* qpf = (const float*)a.q + ((int64_t)b * 64 + head) * QK + NOPE + (f - KV_LORA);
-          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qpf), v1 = *reinterpret_cast<const f32x4_t*>(qpf + 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[j] = v0[j];
-            x[4 + j] = v1[j];
-          }
-        } else {
-          const u32x4_t raw = ld16((const uint16_t*)a.q + ((int64_t)b * 64 + head) * QK + NOPE + (f - KV_LORA));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bf_lo(raw[j]);
-            x[2 * j + 1] = bf_hi(raw[j]);
-          }
-        }
+        const float* qpf = (const float*)a.q + ((int64_t)b * 64 + head) * QK + NOPE + (f - KV_LORA);
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qpf), v1 = *reinterpret_cast<const f32x4_t*>(qpf + 4);
+        const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float c = a.rope_cs[(int64_t)pos * 32 + pair0 + j];
@@ -224,14 +170,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
           v[2 * j + 1] = x[2 * j] * sn + x[2 * j + 1] * c;
         }
       }
-      u32x4_t hi, lo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-        lo[j] = pack_bf16x2(v[2 * j] - bf_lo(hi[j]), v[2 * j + 1] - bf_hi(hi[j]));
-      }
-      qf[ks] = as_bf16x8(hi);
-      if constexpr (FP8) ql_[ks] = as_bf16x8(lo);
+      qf[ks] = as_f16x8(u32x4_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                                pack_f16x2(v[6], v[7])});
     }
   }
 
@@ -248,79 +188,57 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     if (blk + 1 < nblk) gload(blk + 1);
     const int kb = c0 + blk * DKB;
 
-    // partial S^T[key][head] over this wave's 288 features, two key tiles; in FP8 each 128-wide
-    // feature group is summed on its own and multiplied by its per-position scale
+    // partial S^T[key][head] over this wave's 288 features, two key tiles; each 128-wide feature
+    // group is summed on its own and multiplied by its per-position scale
     f32x4_t sacc[2];
     sacc[0] = sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       const uint16_t* r0 = sC + l16 * LDC + lh * HALF + g * 8;
       const uint16_t* r1 = r0 + 16 * LDC;
-      if constexpr (FP8) {
-        // The half (lh) is wave-uniform; each half gets its own fully unrolled loop so that the
-        // 128-feature group boundaries are compile-time: a group's partial scores are summed on
-        // their own and scaled by the positions' group scales (read once per block as 16-byte
-        // vectors), and the next step's fragments are read before this step's products.
-        auto qk_half = [&](auto lhc) {
-          constexpr int LH = decltype(lhc)::value;
-          constexpr int G0 = (LH * HALF) >> 7;
-          f32x4_t sc0[3], sc1[3];  // this half's groups (at most three below the rotary part)
+      // The half (lh) is wave-uniform; each half gets its own fully unrolled loop so that the
+      // 128-feature group boundaries are compile-time; the group scales of the positions are read
+      // once per block as 16-byte vectors, and the next step's fragments before this step's products.
+      auto qk_half = [&](auto lhc) {
+        constexpr int LH = decltype(lhc)::value;
+        constexpr int G0 = (LH * HALF) >> 7;
+        f32x4_t sc0[3], sc1[3];  // this half's groups (at most three below the rotary part)
 #pragma unroll
-          for (int gi = 0; gi < 3; ++gi) {
-            const int grp = min(G0 + gi, 3);
-            sc0[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][g * 4]);
-            sc1[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][16 + g * 4]);
-          }
-          f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
-          bf16x8_t k0 = as_bf16x8(ld16(r0)), k1 = as_bf16x8(ld16(r1));
-#pragma unroll
-          for (int ks = 0; ks < 9; ++ks) {
-            const int f = LH * HALF + ks * 32;
-            const int grp = f < KV_LORA ? (f >> 7) : 4;
-            bf16x8_t n0 = k0, n1 = k1;
-            if (ks + 1 < 9) {
-              n0 = as_bf16x8(ld16(r0 + ks * 32 + 32));
-              n1 = as_bf16x8(ld16(r1 + ks * 32 + 32));
-            }
-            t0 = mfma_bf16_16x16x32(k0, qf[ks], t0);
-            t1 = mfma_bf16_16x16x32(k1, qf[ks], t1);
-            t0 = mfma_bf16_16x16x32(k0, ql_[ks], t0);
-            t1 = mfma_bf16_16x16x32(k1, ql_[ks], t1);
-            if (grp == 4) {  // float32 rotary key: add its low halves against the high query
-              const int fp = f - KV_LORA + g * 8;
-              t0 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + l16 * 72 + fp)), qf[ks], t0);
-              t1 = mfma_bf16_16x16x32(as_bf16x8(ld16(sKlo + (16 + l16) * 72 + fp)), qf[ks], t1);
-            }
-            const int fn = f + 32;
-            const int gnext = ks + 1 < 9 ? (fn < KV_LORA ? (fn >> 7) : 4) : -1;
-            if (gnext != grp) {  // group done: scale (rotary part: scale 1) and add
-              if (grp < 4) {
-                sacc[0] += t0 * sc0[grp - G0];
-                sacc[1] += t1 * sc1[grp - G0];
-              } else {
-                sacc[0] += t0;
-                sacc[1] += t1;
-              }
-              t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-            k0 = n0;
-            k1 = n1;
-          }
-        };
-        if (lh == 0) qk_half(std::integral_constant<int, 0>{});
-        else qk_half(std::integral_constant<int, 1>{});
-      } else {
-        bf16x8_t k0[9], k1[9];
+        for (int gi = 0; gi < 3; ++gi) {
+          const int grp = min(G0 + gi, 3);
+          sc0[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][g * 4]);
+          sc1[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][16 + g * 4]);
+        }
+        f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
+        f16x8_t k0 = as_f16x8(ld16(r0)), k1 = as_f16x8(ld16(r1));
 #pragma unroll
         for (int ks = 0; ks < 9; ++ks) {
-          k0[ks] = as_bf16x8(ld16(r0 + ks * 32));
-          k1[ks] = as_bf16x8(ld16(r1 + ks * 32));
+          const int f = LH * HALF + ks * 32;
+          const int grp = f < KV_LORA ? (f >> 7) : 4;
+          f16x8_t n0 = k0, n1 = k1;
+          if (ks + 1 < 9) {
+            n0 = as_f16x8(ld16(r0 + ks * 32 + 32));
+            n1 = as_f16x8(ld16(r1 + ks * 32 + 32));
+          }
+          t0 = mfma_f16_16x16x32(k0, qf[ks], t0);
+          t1 = mfma_f16_16x16x32(k1, qf[ks], t1);
+          const int fn = f + 32;
+          const int gnext = ks + 1 < 9 ? (fn < KV_LORA ? (fn >> 7) : 4) : -1;
+          if (gnext != grp) {  // group done: scale (rotary part: scale 1) and add
+            if (grp < 4) {
+              sacc[0] += t0 * sc0[grp - G0];
+              sacc[1] += t1 * sc1[grp - G0];
+            } else {
+              sacc[0] += t0;
+              sacc[1] += t1;
+            }
+            t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+          k0 = n0;
+          k1 = n1;
         }
-#pragma unroll
-        for (int ks = 0; ks < 9; ++ks) {
-          sacc[0] = mfma_bf16_16x16x32(k0[ks], qf[ks], sacc[0]);
-          sacc[1] = mfma_bf16_16x16x32(k1[ks], qf[ks], sacc[1]);
-        }
-      }
+      };
+      if (lh == 0) qk_half(std::integral_constant<int, 0>{});
+      else qk_half(std::integral_constant<int, 1>{});
     }
     // add the other half's partial scores (same order in both waves of a pair)
     // 16-byte LDS accesses on 48-byte lane rows (eight lanes of one LDS cycle in distinct banks)
@@ -340,10 +258,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = sv[kt][e];  // unscaled: the scale is applied in the exponent's fma
-        if (kb + kt * 16 + g * 4 + e >= c1) s = -INFINITY;
-        sv[kt][e] = s;
-        bmax = fmaxf(bmax, s);
+        float sc = sv[kt][e];  // unscaled: the scale is applied in the exponent's fma
+        if (kb + kt * 16 + g * 4 + e >= c1) sc = -INFINITY;
+        sv[kt][e] = sc;
+        bmax = fmaxf(bmax, sc);
       }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
@@ -364,40 +282,36 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2_flush(fmaf(sv[kt][e], sl2, -mrun));
-        sv[kt][e] = p;
-        psum += p;
+        const float pv = exp2_flush(fmaf(sv[kt][e], sl2, -mrun));
+        sv[kt][e] = pv;
+        psum += pv;
       }
     lrun += psum;
-    // probabilities as the B operand of the value mix (FP8: one copy per 128-feature group,
-    // each position's probability times that position's group scale)
-    // FP8 also keeps the low bf16 halves (pl) so the mix is exact to about 16 bits
-    bf16x8_t pf[2], pl[2];
+    // probabilities as the B operand of the value mix: one copy per 128-feature group of this
+    // wave's half, each position's probability times that position's group scale (and the
+    // prescale), as fp16 high parts (pf) and residuals (pl)
+    f16x8_t pf[2], pl[2];
 #pragma unroll
-    for (int q = 0; q < (FP8 ? 2 : 1); ++q) {
-      float s[2][4];
+    for (int q = 0; q < 2; ++q) {
+      float s_[2][4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (FP8) sc = *reinterpret_cast<const f32x4_t*>(&sScale[2 * lh + q][kt * 16 + g * 4]);
+        const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sScale[2 * lh + q][kt * 16 + g * 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[kt][e] = sv[kt][e] * sc[e];
+        for (int e = 0; e < 4; ++e) s_[kt][e] = sv[kt][e] * (sc[e] * P_PRESCALE);
       }
       u32x4_t w, r;
-      w[0] = pack_bf16x2(s[0][0], s[0][1]);
-      w[1] = pack_bf16x2(s[0][2], s[0][3]);
-      w[2] = pack_bf16x2(s[1][0], s[1][1]);
-      w[3] = pack_bf16x2(s[1][2], s[1][3]);
-      pf[q] = as_bf16x8(w);
-      if constexpr (FP8) {
-        r[0] = pack_bf16x2(s[0][0] - bf_lo(w[0]), s[0][1] - bf_hi(w[0]));
-        r[1] = pack_bf16x2(s[0][2] - bf_lo(w[1]), s[0][3] - bf_hi(w[1]));
-        r[2] = pack_bf16x2(s[1][0] - bf_lo(w[2]), s[1][1] - bf_hi(w[2]));
-        r[3] = pack_bf16x2(s[1][2] - bf_lo(w[3]), s[1][3] - bf_hi(w[3]));
-        pl[q] = as_bf16x8(r);
-      }
+      w[0] = pack_f16x2(s_[0][0], s_[0][1]);
+      w[1] = pack_f16x2(s_[0][2], s_[0][3]);
+      w[2] = pack_f16x2(s_[1][0], s_[1][1]);
+      w[3] = pack_f16x2(s_[1][2], s_[1][3]);
+      r[0] = pack_f16x2(s_[0][0] - f16_lo(w[0]), s_[0][1] - f16_hi(w[0]));
+      r[1] = pack_f16x2(s_[0][2] - f16_lo(w[1]), s_[0][3] - f16_hi(w[1]));
+      r[2] = pack_f16x2(s_[1][0] - f16_lo(w[2]), s_[1][1] - f16_hi(w[2]));
+      r[3] = pack_f16x2(s_[1][2] - f16_lo(w[3]), s_[1][3] - f16_hi(w[3]));
+      pf[q] = as_f16x8(w);
+      pl[q] = as_f16x8(r);
     }
-    if constexpr (!FP8) pf[1] = pf[0];
     // O^T[dim][head] += C^T[dim][keys] P^T[keys][head] over this wave's 256 latent features;
     // lane group g holds keys g*4..+3 and 16+g*4..+3
     {
@@ -415,21 +329,22 @@ __global__ __launch_bounds__(512, 1) void decode_attn_kernel(DecodeAttnArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const bf16x8_t vt = as_bf16x8(u32x4_t{lo[c][0], lo[c][1], hi[c][0], hi[c][1]});
-          oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pf[c0_ >> 3], oacc[c0_ + c]);
-          if constexpr (FP8) oacc[c0_ + c] = mfma_bf16_16x16x32(vt, pl[c0_ >> 3], oacc[c0_ + c]);
+          const f16x8_t vt = as_f16x8(u32x4_t{lo[c][0], lo[c][1], hi[c][0], hi[c][1]});
+          oacc[c0_ + c] = mfma_f16_16x16x32(vt, pf[c0_ >> 3], oacc[c0_ + c]);
+          oacc[c0_ + c] = mfma_f16_16x16x32(vt, pl[c0_ >> 3], oacc[c0_ + c]);
         }
       }
     }
   }
 
-  // ---- split outputs: unnormalised o (relative to mrun), running max and sum per head
+  // ---- split outputs: unnormalised o (relative to mrun, prescale taken out), running max and sum
   lrun += __shfl_xor(lrun, 16);
   lrun += __shfl_xor(lrun, 32);
   const int64_t pidx = ((int64_t)b * a.max_splits + split) * 64 + head;
   float* po = a.part_o + pidx * KV_LORA + lh * 256;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) *reinterpret_cast<f32x4_t*>(po + c * 16 + g * 4) = oacc[c];
+  for (int c = 0; c < 16; ++c)
+    *reinterpret_cast<f32x4_t*>(po + c * 16 + g * 4) = oacc[c] * (1.0f / P_PRESCALE);
   if (lh == 0 && g == 0) {
     a.part_ml[pidx * 2] = mrun;
     a.part_ml[pidx * 2 + 1] = lrun;
@@ -893,7 +808,7 @@ hipError_t decode_attention_splits(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   dim3 g1(a.max_splits, a.B);
   if (a.fp8)
-    hipLaunchKernelGGL(decode_attn_kernel<true>, g1, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(decode_attn_fp8_kernel, g1, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL(decode_attn_bf16_kernel, g1, dim3(512), 0, s, a);
   return hipGetLastError();

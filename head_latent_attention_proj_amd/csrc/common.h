@@ -7,6 +7,8 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -54,6 +56,21 @@ MLA_DEV f32x4_t mfma_bf16_16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f
 }
 
 MLA_DEV bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// fp16 (IEEE binary16, 11 significant bits) pair packed in a uint32, round to nearest even
+MLA_DEV uint32_t pack_f16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+MLA_DEV float f16_lo(uint32_t u) { return (float)__builtin_bit_cast(f16x2_t, u)[0]; }
+MLA_DEV float f16_hi(uint32_t u) { return (float)__builtin_bit_cast(f16x2_t, u)[1]; }
+MLA_DEV f16x8_t as_f16x8(const u32x4_t& v) { return __builtin_bit_cast(f16x8_t, v); }
+
+// D = A(16x32) * B(32x16) + C with fp16 operands, float32 accumulation; the lane layout is that of
+// mfma_bf16_16x16x32.
+MLA_DEV f32x4_t mfma_f16_16x16x32(const f16x8_t& a, const f16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 MLA_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 MLA_DEV void st16(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
