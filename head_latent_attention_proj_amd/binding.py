@@ -25,6 +25,8 @@ EXPORTED = (
     "mla_block_prefill_workspace_bytes", "mla_block_decode_workspace_bytes", "mla_block_prefill", "mla_block_decode",
     "mla_cache_pool_plan", "mla_cache_pool_layer",
     "mla_test_gemm_workspace_bytes", "mla_test_gemm", "mla_decode_static", "mla_test_probe_stage",
+    "mla_page_pool_create", "mla_page_pool_alloc", "mla_page_pool_free", "mla_page_pool_available",
+    "mla_page_pool_destroy",
 )
 STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6, "decode_attn": 7,
          "prefill_attn": 8}
@@ -47,7 +49,9 @@ class MlaWeights(ctypes.Structure):
 class MlaCacheDesc(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("offset_h", ctypes.c_void_p), ("offset_d", ctypes.c_void_p),
                 ("len_h", ctypes.c_void_p), ("len_d", ctypes.c_void_p), ("cap_h", ctypes.c_void_p),
-                ("n_seqs", ctypes.c_int32), ("total_slots", ctypes.c_int64)]
+                ("n_seqs", ctypes.c_int32), ("total_slots", ctypes.c_int64),
+                ("block_table_h", ctypes.c_void_p), ("block_table_d", ctypes.c_void_p),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
 
 
 class MlaError(RuntimeError):
@@ -112,6 +116,16 @@ def lib() -> ctypes.CDLL:
     L.mla_test_gemm.restype = ctypes.c_int
     L.mla_test_probe_stage.argtypes = [i32, vp, vp]
     L.mla_test_probe_stage.restype = ctypes.c_int
+    L.mla_page_pool_create.argtypes = [i32, ctypes.POINTER(vp)]
+    L.mla_page_pool_create.restype = ctypes.c_int
+    L.mla_page_pool_alloc.argtypes = [vp, i32, vp]
+    L.mla_page_pool_alloc.restype = ctypes.c_int
+    L.mla_page_pool_free.argtypes = [vp, vp, i32]
+    L.mla_page_pool_free.restype = ctypes.c_int
+    L.mla_page_pool_available.argtypes = [vp]
+    L.mla_page_pool_available.restype = i32
+    L.mla_page_pool_destroy.argtypes = [vp]
+    L.mla_page_pool_destroy.restype = None
     _lib = L
     return L
 
@@ -169,7 +183,7 @@ class Cache:
         self.len_d = torch.zeros(len(caps), dtype=torch.int32, device=device)
         self._desc = MlaCacheDesc(self.data.data_ptr(), self.offset_h.ctypes.data, self.offset_d.data_ptr(),
                                   self.len_h.ctypes.data, self.len_d.data_ptr(), self.cap_h.ctypes.data,
-                                  len(caps), self.total_slots)
+                                  len(caps), self.total_slots, None, None, 0, 0)
 
     @property
     def desc(self) -> MlaCacheDesc:
@@ -183,6 +197,108 @@ class Cache:
         """View of sequence `seq`'s used slots as [len, entry_bytes] uint8."""
         o, n = int(self.offset_h[seq]), int(self.len_h[seq])
         return self.data.view(-1, self.entry_bytes)[o:o + n]
+
+
+class PagePool:
+    """The library's host page allocator (mla_page_pool_*): page ids 0 .. n_pages-1, handed out and
+    taken back; released pages are reused oldest first."""
+
+    def __init__(self, n_pages: int):
+        h = ctypes.c_void_p()
+        check(lib().mla_page_pool_create(n_pages, ctypes.byref(h)))
+        self._h = h
+        self.n_pages = n_pages
+
+    def alloc(self, n: int) -> np.ndarray:
+        ids = np.empty(max(n, 1), dtype=np.int32)
+        check(lib().mla_page_pool_alloc(self._h, n, ids.ctypes.data))
+        return ids[:n]
+
+    def free(self, ids) -> None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        check(lib().mla_page_pool_free(self._h, ids.ctypes.data, len(ids)))
+
+    @property
+    def available(self) -> int:
+        return lib().mla_page_pool_available(self._h)
+
+    def __del__(self):
+        try:
+            if self._h:
+                lib().mla_page_pool_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+
+class PagedCache(Cache):
+    """Paged latent cache: n_pages pages of page_size slots in one device buffer, a block table per
+    sequence (host + device copy) and pages taken from a PagePool as sequences grow (`reserve`) and
+    given back when a sequence ends (`release`). Same interface as Cache for the layer calls."""
+
+    def __init__(self, layer: "Layer", n_seqs: int, n_pages: int, page_size: int = 64, max_pages: int | None = None,
+                 pool: PagePool | None = None, device="cuda", fill_byte: int | None = None):
+        import torch
+
+        self.page_size, self.n_pages = page_size, n_pages
+        self.max_pages = max_pages or n_pages
+        self.pool = pool or PagePool(n_pages)
+        self.entry_bytes = layer.entry_bytes
+        self.total_slots = n_pages * page_size
+        self.data = torch.empty(self.total_slots * self.entry_bytes, dtype=torch.uint8, device=device)
+        if fill_byte is not None:
+            self.data.fill_(fill_byte)
+        self.table_h = np.full((n_seqs, self.max_pages), -1, dtype=np.int32)
+        self.table_d = torch.from_numpy(self.table_h).to(device)
+        self.n_held = np.zeros(n_seqs, dtype=np.int32)  # pages held per sequence
+        self.cap_h = np.zeros(n_seqs, dtype=np.int32)
+        self.len_h = np.zeros(n_seqs, dtype=np.int32)
+        self.len_d = torch.zeros(n_seqs, dtype=torch.int32, device=device)
+        self.offset_h = None
+        self._desc = MlaCacheDesc(self.data.data_ptr(), None, None, self.len_h.ctypes.data, self.len_d.data_ptr(),
+                                  self.cap_h.ctypes.data, n_seqs, self.total_slots, self.table_h.ctypes.data,
+                                  self.table_d.data_ptr(), page_size, self.max_pages)
+
+    def reserve(self, seq: int, positions: int) -> None:
+        """Give sequence `seq` pages for `positions` positions in all (its capacity)."""
+        need = -(-positions // self.page_size)
+        if need > self.n_held[seq]:
+            ids = self.pool.alloc(int(need - self.n_held[seq]))
+            self.table_h[seq, self.n_held[seq]:need] = ids
+            self.n_held[seq] = need
+            self.table_d[seq].copy_(torch_from(self.table_h[seq]))
+        self.cap_h[seq] = max(int(self.cap_h[seq]), positions)
+
+    def release(self, seq: int) -> None:
+        """Give the sequence's pages back to the pool and empty it."""
+        import torch
+
+        if self.n_held[seq]:
+            self.pool.free(self.table_h[seq, :self.n_held[seq]])
+        self.table_h[seq, :] = -1
+        self.table_d[seq].copy_(torch_from(self.table_h[seq]))
+        self.n_held[seq] = 0
+        self.cap_h[seq] = 0
+        self.len_h[seq] = 0
+        self.len_d[seq] = 0
+        torch.cuda.synchronize()
+
+    def slot_index(self, seq: int, positions) -> np.ndarray:
+        p = np.asarray(positions, dtype=np.int64)
+        return self.table_h[seq, p // self.page_size].astype(np.int64) * self.page_size + p % self.page_size
+
+    def slots(self, seq: int):
+        """Sequence `seq`'s used slots in position order as [len, entry_bytes] uint8 (a gathered copy)."""
+        import torch
+
+        idx = torch.from_numpy(self.slot_index(seq, np.arange(int(self.len_h[seq])))).to(self.data.device)
+        return self.data.view(-1, self.entry_bytes)[idx]
+
+
+def torch_from(a: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a))
 
 
 class CachePool:
@@ -223,7 +339,8 @@ class _PoolLayerCache(Cache):
         self.len_d = torch.zeros(len(pool.cap_h), dtype=torch.int32, device=device)
         self.total_slots, self.entry_bytes = pool.total_slots, pool.entry_bytes
         self._desc = MlaCacheDesc(None, self.offset_h.ctypes.data, self.offset_d.data_ptr(), self.len_h.ctypes.data,
-                                  self.len_d.data_ptr(), self.cap_h.ctypes.data, len(pool.cap_h), pool.total_slots)
+                                  self.len_d.data_ptr(), self.cap_h.ctypes.data, len(pool.cap_h), pool.total_slots,
+                                  None, None, 0, 0)
         check(lib().mla_cache_pool_layer(_ptr(pool.pool), pool.pool_bytes, pool.layer_bytes, l, ctypes.byref(self._desc)))
         self.data = pool.pool[l * pool.layer_bytes:(l + 1) * pool.layer_bytes]
 

@@ -39,11 +39,21 @@ namespace mla_k {
 namespace {
 
 constexpr int DKB = 32;    // positions per block
-constexpr int LDC = 584;   // sC row: 576 features + pad (1168 B: 16 rows -> distinct bank groups)
+constexpr int LDC = 576;   // sC row: 576 fp16 features in 16-byte chunks, swizzled per row (swz)
 constexpr int HALF = 288;  // score features per wave: [0, 288) or [288, 576)
 constexpr float LOG2E = 1.4426950408889634f;
 
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
+// Chunk swizzle of a staged FP8 block: 16-byte chunk c of row r sits at chunk c ^ swz(r) (only the low
+// three bits of c change, so a chunk stays in its aligned 128-byte group). swz is linear over the bits
+// of r mod 16 and chosen so that each LDS access phase meets distinct banks with 32 or with 64 four-byte
+// banks: the score reads (8 or 16 consecutive rows at one chunk), the transposed value reads (4 or 8
+// consecutive rows x 32 bytes) and the staging writes (8 even or 8 odd rows at one chunk).
+MLA_DEV int swz(int r) { return ((r & 1) << 1) ^ ((r & 2) << 1) ^ ((r & 4) ? 3 : 0) ^ ((r >> 3) & 1); }
+
+// element index of feature f of row r in the swizzled block
+MLA_DEV int sidx(int r, int f) { return r * LDC + (((f >> 3) ^ swz(r)) << 3) + (f & 7); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -70,6 +80,9 @@ MLA_DEV u32x2_t e4m3x4_to_f16(uint32_t w) {
 // group scales of RMSNorm outputs far below 1); the partial outputs are scaled back on the way out.
 constexpr float P_PRESCALE = 64.0f;
 
+// FP8 cache blocks whose loads are in flight while a block is used (at most 3)
+constexpr int FP8_AHEAD = 2;
+
 // FP8 cache entries. 8 waves: wave = hg + 4*lh, head group hg (heads hg*16 .. +15), half lh. A
 // wave forms the partial scores of its 16 heads over features [lh*288, lh*288+288) and, after the
 // two halves are added through LDS, mixes latent features [lh*256, lh*256+256). Two waves per SIMD
@@ -82,7 +95,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
   const int c0 = split * a.chunk;
   if (c0 >= L) return;
   const int c1 = min(L, c0 + a.chunk);
-  const int64_t slot0 = a.offset[seq];
   const int nblk = cdiv(c1 - c0, DKB);
   const int eb = a.entry_bytes;
   constexpr int kpe_off = KV_LORA + 16;
@@ -93,49 +105,59 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
   const int l16 = lane & 15, g = lane >> 4;
   const int head = hg * 16 + l16;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];      // fp16 [position][576 + pad]
+  __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];      // fp16 [position][576], swizzled
   __shared__ __attribute__((aligned(16))) float xS[8][64][12];         // partial scores [wave][lane][8 + pad]
   __shared__ __attribute__((aligned(16))) float sScale[4][DKB];        // group scales [group][position]
 
-  // ---- staging through registers, one block ahead: codes as position pairs (pair kp = tid & 15,
-  // 16-code chunk cc = tid >> 4), the rotary key (every thread one chunk of 4 float32 features),
-  // group scales (threads 256..287 one position each)
-  u32x4_t rl[2], rp, rs;
-  auto gload = [&](int blk) {
+  // ---- staging through registers, FP8_AHEAD blocks ahead (one register set per block in flight):
+  // codes as position pairs (pair kp = tid & 15, 16-code chunk cc = tid >> 4), the rotary key (every
+  // thread one chunk of 4 float32 features), group scales (threads 256..287 one position each)
+  u32x4_t rl[FP8_AHEAD][2], rp[FP8_AHEAD], rs[FP8_AHEAD];
+  // A 32-position block lies in one run of consecutive slots (a page holds whole blocks): its first
+  // slot is looked up once per block, rows are offsets from it.
+  auto gload = [&](int blk, auto setc) {
+    constexpr int S = decltype(setc)::value;
     const int kb = c0 + blk * DKB;
+    const uint8_t* bb = a.cache + slot_of(a.map, seq, kb) * eb;
     const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int key = min(kb + 2 * kp + u, c1 - 1);  // past the split's end: re-read (masked)
-      rl[u] = ld16(a.cache + (slot0 + key) * eb + cc * 16);
+      rl[S][u] = ld16(bb + (key - kb) * eb + cc * 16);
     }
-    if (tid >= 256 && tid < 256 + DKB) {
-      const int key = min(kb + (tid - 256), c1 - 1);
-      rs = ld16(a.cache + (slot0 + key) * eb + KV_LORA);
+    {  // every thread loads (threads 256..287 keep theirs): the same number of loads in every wave
+      const int key = min(kb + (tid & (DKB - 1)), c1 - 1);
+      rs[S] = ld16(bb + (key - kb) * eb + KV_LORA);
     }
     const int key = min(kb + (tid >> 4), c1 - 1);
-    rp = ld16(a.cache + (slot0 + key) * eb + kpe_off + (tid & 15) * 16);
+    rp[S] = ld16(bb + (key - kb) * eb + kpe_off + (tid & 15) * 16);
   };
-  auto sstore = [&]() {
+  auto sstore = [&](auto setc) {
+    constexpr int S = decltype(setc)::value;
     const int kp = tid & 15, cc = tid >> 4;
 #pragma unroll
     for (int hlf = 0; hlf < 2; ++hlf) {  // codes 8*hlf .. 8*hlf+7 of the chunk, positions 2kp and 2kp+1
-      const u32x2_t x01 = e4m3x4_to_f16(rl[0][2 * hlf]), x23 = e4m3x4_to_f16(rl[0][2 * hlf + 1]);
-      const u32x2_t y01 = e4m3x4_to_f16(rl[1][2 * hlf]), y23 = e4m3x4_to_f16(rl[1][2 * hlf + 1]);
-      st16(sC + (2 * kp) * LDC + cc * 16 + hlf * 8, u32x4_t{x01[0], x01[1], x23[0], x23[1]});
-      st16(sC + (2 * kp + 1) * LDC + cc * 16 + hlf * 8, u32x4_t{y01[0], y01[1], y23[0], y23[1]});
+      const u32x2_t x01 = e4m3x4_to_f16(rl[S][0][2 * hlf]), x23 = e4m3x4_to_f16(rl[S][0][2 * hlf + 1]);
+      const u32x2_t y01 = e4m3x4_to_f16(rl[S][1][2 * hlf]), y23 = e4m3x4_to_f16(rl[S][1][2 * hlf + 1]);
+      st16(sC + sidx(2 * kp, cc * 16 + hlf * 8), u32x4_t{x01[0], x01[1], x23[0], x23[1]});
+      st16(sC + sidx(2 * kp + 1, cc * 16 + hlf * 8), u32x4_t{y01[0], y01[1], y23[0], y23[1]});
     }
     if (tid >= 256 && tid < 256 + DKB) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[q]);
+      for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[S][q]);
     }
     // rotary key: 4 float32 features -> fp16
     const int pos = tid >> 4, f4 = (tid & 15) * 4;
-    *reinterpret_cast<u32x2_t*>(sC + pos * LDC + KV_LORA + f4) =
-        u32x2_t{pack_f16x2(__uint_as_float(rp[0]), __uint_as_float(rp[1])),
-                pack_f16x2(__uint_as_float(rp[2]), __uint_as_float(rp[3]))};
+    *reinterpret_cast<u32x2_t*>(sC + sidx(pos, KV_LORA + f4)) =
+        u32x2_t{pack_f16x2(__uint_as_float(rp[S][0]), __uint_as_float(rp[S][1])),
+                pack_f16x2(__uint_as_float(rp[S][2]), __uint_as_float(rp[S][3]))};
   };
-  gload(0);  // in flight during the query set-up
+  // the first blocks are in flight during the query set-up. Block indices past the split's last
+  // block re-read the last block (never staged): every loop trip then issues the same loads, so the
+  // compiler's wait before a set is used covers that set only, not the sets issued after it.
+  gload(0, std::integral_constant<int, 0>{});
+  if constexpr (FP8_AHEAD > 1) gload(min(1, nblk - 1), std::integral_constant<int, 1>{});
+  if constexpr (FP8_AHEAD > 2) gload(min(2, nblk - 1), std::integral_constant<int, 2>{});
 
   // ---- query fragments (B operand), fp16: column = head, features lh*288 + ks*32 + g*8 .. +7;
   // the latent part is the sum of the two float32 absorbed products, features >= 512 are the rotary
@@ -181,11 +203,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
 #pragma unroll
   for (int c = 0; c < 16; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int blk = 0; blk < nblk; ++blk) {
+  auto step = [&](const int blk, auto setc) {
     __syncthreads();  // the previous block's LDS reads are done
-    sstore();
+    sstore(setc);
     __syncthreads();
-    if (blk + 1 < nblk) gload(blk + 1);
+    gload(min(blk + FP8_AHEAD, nblk - 1), setc);
     const int kb = c0 + blk * DKB;
 
     // partial S^T[key][head] over this wave's 288 features, two key tiles; each 128-wide feature
@@ -193,8 +215,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
     f32x4_t sacc[2];
     sacc[0] = sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
-      const uint16_t* r0 = sC + l16 * LDC + lh * HALF + g * 8;
-      const uint16_t* r1 = r0 + 16 * LDC;
+      // feature f = lh*288 + 32ks + 8g is chunk lh*36 + 4ks + g; its low three bits are 4*((lh+ks)&1) + g,
+      // so two per-lane bases (even / odd lh+ks) plus a compile-time offset address every step
+      const int sw = swz(l16);
+      const uint16_t* rb[2] = {sC + l16 * LDC + ((g ^ sw) << 3), sC + l16 * LDC + (((4 + g) ^ sw) << 3)};
       // The half (lh) is wave-uniform; each half gets its own fully unrolled loop so that the
       // 128-feature group boundaries are compile-time; the group scales of the positions are read
       // once per block as 16-byte vectors, and the next step's fragments before this step's products.
@@ -209,15 +233,17 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
           sc1[gi] = *reinterpret_cast<const f32x4_t*>(&sScale[grp][16 + g * 4]);
         }
         f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
-        f16x8_t k0 = as_f16x8(ld16(r0)), k1 = as_f16x8(ld16(r1));
+        // chunk group (8 chunks) of step ks, as an element offset, and the base of its parity
+        auto kaddr = [&](int ks) { return rb[(LH + ks) & 1] + (((LH * 36 + 4 * ks) >> 3) << 6); };
+        f16x8_t k0 = as_f16x8(ld16(kaddr(0))), k1 = as_f16x8(ld16(kaddr(0) + 16 * LDC));
 #pragma unroll
         for (int ks = 0; ks < 9; ++ks) {
           const int f = LH * HALF + ks * 32;
           const int grp = f < KV_LORA ? (f >> 7) : 4;
           f16x8_t n0 = k0, n1 = k1;
           if (ks + 1 < 9) {
-            n0 = as_f16x8(ld16(r0 + ks * 32 + 32));
-            n1 = as_f16x8(ld16(r1 + ks * 32 + 32));
+            n0 = as_f16x8(ld16(kaddr(ks + 1)));
+            n1 = as_f16x8(ld16(kaddr(ks + 1) + 16 * LDC));
           }
           t0 = mfma_f16_16x16x32(k0, qf[ks], t0);
           t1 = mfma_f16_16x16x32(k1, qf[ks], t1);
@@ -318,14 +344,21 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
       // lane (l16, g): feature lh*256 + 16c + l16 at keys 4g..4g+3 (lo) and 16+4g.. (hi), read
       // as columns of the row-major block: lane r of the 16-lane group g points at key 4g + r/4,
       // features 4(r%4) .. +3 of the 16-feature tile
-      const uint16_t* tp = sC + (4 * g + (l16 >> 2)) * LDC + lh * 256 + 4 * (l16 & 3);
+      // (swizzled: feature lh*256 + 16cc + 4(l16&3) is chunk lh*32 + 2cc + ((l16>>1)&1), whose low three
+      // bits are 2(cc&3) + ((l16>>1)&1): four per-lane bases, one per cc mod 4, plus compile-time offsets)
+      const int row = 4 * g + (l16 >> 2), swr = swz(row);
+      const uint16_t* tp[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        tp[m] = sC + row * LDC + lh * 256 + (((2 * m + ((l16 >> 1) & 1)) ^ swr) << 3) + 4 * (l16 & 1);
 #pragma unroll
       for (int c0_ = 0; c0_ < 16; c0_ += 8) {
         u32x2_t lo[8], hi[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          lo[c] = ds_read_tr16(tp + (c0_ + c) * 16);
-          hi[c] = ds_read_tr16(tp + 16 * LDC + (c0_ + c) * 16);
+          const int cc = c0_ + c;
+          lo[c] = ds_read_tr16(tp[cc & 3] + (cc >> 2) * 64);
+          hi[c] = ds_read_tr16(tp[cc & 3] + 16 * LDC + (cc >> 2) * 64);
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -335,7 +368,17 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
         }
       }
     }
+  };
+  // one step per register set in every loop trip (each set named by a compile-time index), then the
+  // last nblk % FP8_AHEAD blocks
+  int blk = 0;
+  for (; blk + FP8_AHEAD <= nblk; blk += FP8_AHEAD) {
+    step(blk, std::integral_constant<int, 0>{});
+    if constexpr (FP8_AHEAD > 1) step(blk + 1, std::integral_constant<int, 1 % FP8_AHEAD>{});
+    if constexpr (FP8_AHEAD > 2) step(blk + 2, std::integral_constant<int, 2 % FP8_AHEAD>{});
   }
+  if (FP8_AHEAD > 1 && blk < nblk) step(blk, std::integral_constant<int, 0>{});
+  if (FP8_AHEAD > 2 && blk + 1 < nblk) step(blk + 1, std::integral_constant<int, 1 % FP8_AHEAD>{});
 
   // ---- split outputs: unnormalised o (relative to mrun, prescale taken out), running max and sum
   lrun += __shfl_xor(lrun, 16);
@@ -384,7 +427,6 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   const int c0 = split * a.chunk;
   if (c0 >= L) return;
   const int c1 = min(L, c0 + a.chunk);
-  const int64_t slot0 = a.offset[seq];
   const int nblk = cdiv(c1 - c0, DKB);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -412,9 +454,9 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   // Every load is issued unconditionally (an index past the block re-reads its last chunk and is
   // not stored): with no branch among them, the compiler's wait counts stay exact and the two
   // register sets really are in flight together.
-  // Row and byte column of each of the thread's chunks are fixed; a load adds the block's row to
-  // a 32-bit offset from the sequence's first slot (the uniform base stays in scalar registers).
-  const uint8_t* seq_base = a.cache + slot0 * BF16_ENTRY_BYTES;
+  // Row and byte column of each of the thread's chunks are fixed; a load adds its row to a 32-bit
+  // offset from the block's first slot (a uniform base in scalar registers: a 32-position block lies
+  // in one run of consecutive slots, as a page holds whole blocks).
   int crow[5], ccol[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
@@ -424,10 +466,11 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   }
   auto gload = [&](int blk, u32x4_t (&rs)[5]) {
     const int kb = c0 + blk * DKB;
+    const uint8_t* bb = a.cache + slot_of(a.map, seq, kb) * BF16_ENTRY_BYTES;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int key = min(kb + crow[i], c1 - 1);  // rows past the split's end: re-read, masked later
-      rs[i] = ld16(seq_base + (uint32_t)(key * BF16_ENTRY_BYTES + ccol[i]));
+      rs[i] = ld16(bb + (uint32_t)((key - kb) * BF16_ENTRY_BYTES + ccol[i]));
     }
   };
   auto sstore = [&](uint16_t* sCb, const u32x4_t (&rs)[5]) {

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
   // Bases common to the workgroup (scalar registers) plus 32-bit per-lane byte offsets: a load
   // costs one address register and a 32-bit add instead of a 64-bit multiply-add per block.
   const uint8_t* kn_base = (const uint8_t*)(a.knope + ((int64_t)m.kbase * 64 + h) * 128);
-  const uint8_t* pe_base = a.cache + m.slot0 * a.entry_bytes + a.kpe_off;
+  const uint8_t* pe_base = a.cache + m.krow0 * a.entry_bytes + a.kpe_off;
   const uint8_t* vt_base = (const uint8_t*)(a.vt + (int64_t)(h * 128) * a.vt_ld + m.kbase);
   auto gload = [&](int blk) {
     if constexpr (SPLIT) return;  // split staging loads and stores in one step (stage_split)
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
     }
     {
       const int key = min(kb + (tid >> 2), n_keys - 1);
-      const float* kp = (const float*)(a.cache + (m.slot0 + key) * a.entry_bytes + a.kpe_off) + (tid & 3) * 16;
+      const float* kp = (const float*)(a.cache + (m.krow0 + key) * a.entry_bytes + a.kpe_off) + (tid & 3) * 16;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(kp + 4 * c);

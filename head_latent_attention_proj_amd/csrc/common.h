@@ -88,6 +88,23 @@ MLA_DEV T wave_sum(T v) {
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Where position `pos` of sequence `seq` lives in the cache: slot offset[seq] + pos (contiguous
+// layout), or, with a block table, slot table[seq][pos >> page_shift] * page_size + the position's
+// offset in its page (pages of 2^page_shift slots, page_shift >= 6).
+struct SlotMap {
+  const int64_t* offset = nullptr;
+  const int32_t* table = nullptr;  // device [n_seqs][max_pages] page ids, or null
+  int32_t page_shift = 0;
+  int32_t max_pages = 0;
+};
+MLA_DEV int64_t slot_of(const SlotMap& m, int seq, int pos) {
+  if (m.table) {
+    const int pg = pos >> m.page_shift;
+    return ((int64_t)m.table[(int64_t)seq * m.max_pages + pg] << m.page_shift) + (pos - (pg << m.page_shift));
+  }
+  return m.offset[seq] + pos;
+}
+
 // 2^x with the hardware's v_exp_f32 alone: exp2f adds a range fix-up (compare, select, scale)
 // so that results below 2^-126 come out as denormals; softmax weights that small add nothing
 // to a float32 sum, so the attention kernels take the flushed value. exp2(-inf) = 0.

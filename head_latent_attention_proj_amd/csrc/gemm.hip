@@ -855,6 +855,12 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
   int splits = 1;
   const int wgs = pl.tiles * batch;
   if (wgs < TARGET_WGS / 2) splits = cdiv(TARGET_WGS, wgs);
+  // split-K partials are written and read back in float32: at decode-sized M (a few hundred
+  // rows) they can outweigh the operands themselves, so a split may add at most the operand
+  // bytes in partial traffic
+  const int64_t operand_bytes = 2 * (int64_t)batch * ((int64_t)M * K + (int64_t)N * K);
+  const int64_t part_bytes_per_split = 8 * (int64_t)batch * M * N;
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, operand_bytes / part_bytes_per_split));
   splits = std::max(1, std::min(splits, nsteps));
   const int steps_per = cdiv(nsteps, splits);
   pl.ksplit = steps_per * 64;

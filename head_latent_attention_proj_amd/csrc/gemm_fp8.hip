@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void splitk_reduce8_kernel(GemmArgs p, int spl
 }
 
 struct Plan8 {
-  int kind;  // 0 wsplit, 1 tile128, 2 tile256
+  int kind;  // 0 wsplit, 1 tile 128 x 128, 2 tile 128 x 256, 3 tile 128 x 64
   int mt, kw, ysplit;
   int splits, ksplit;
   int tiles;
@@ -516,12 +516,21 @@ Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
     pl.kw = kw;
     return pl;
   }
+  // Decode-sized M (up to 256 rows: one or two row tiles) takes 64-column tiles, twice the
+  // workgroups of 128-column ones before any split of K.
   const bool big = !prec && M >= 1024 && N >= 1024;
-  pl.kind = big ? 2 : 1;
-  pl.tiles = cdiv(M, 128) * cdiv(N, big ? 256 : 128);
+  const bool narrow = M <= 256;
+  pl.kind = big ? 2 : (narrow ? 3 : 1);
+  pl.tiles = cdiv(M, 128) * cdiv(N, big ? 256 : (narrow ? 64 : 128));
   int splits = 1;
   const int wgs = pl.tiles * batch;
   if (wgs < 256) splits = cdiv(512, wgs);
+  // float32 split-K partials are written and read back: the splits may add at most twice the
+  // operand bytes (codes) in partial traffic. Measured at 128 rows (decode of 128 sequences):
+  // q_a|kv_a 7 splits, o_proj 5, q_b 3 (q_b unsplit, 12 serial K stages per workgroup, took 42 us).
+  const int64_t operand_bytes = (int64_t)batch * ((int64_t)M * K + (int64_t)N * K);
+  const int64_t part_bytes_per_split = 8 * (int64_t)batch * M * N;
+  splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, 2 * operand_bytes / part_bytes_per_split));
   splits = std::max(1, std::min(splits, ngroups));
   const int per = cdiv(ngroups, splits);
   pl.ksplit = per * 128;
@@ -555,6 +564,9 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
   dim3 grid(pl.tiles, pl.splits, a.batch);
   if (pl.kind == 1)
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 128, 2, 2, TAG, PREC>), grid, dim3(256), 0, s, a, pl.splits,
+                       pl.ksplit);
+  else if (pl.kind == 3)
+    hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 64, 2, 2, TAG, PREC>), grid, dim3(256), 0, s, a, pl.splits,
                        pl.ksplit);
   else if constexpr (!PREC)
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 256, 2, 4, TAG, PREC>), grid, dim3(512), 0, s, a, pl.splits,

@@ -69,7 +69,9 @@ int64_t gemm_part_floats(int M, int N, int K, int batch);
 // Per-call sequence metadata (device, filled by plan_kernel at the start of a prefill)
 // ---------------------------------------------------------------------------------------------
 struct SeqMeta {
-  int64_t slot0;   // first cache slot of the sequence
+  int64_t slot0;   // first cache slot of the sequence (contiguous layout)
+  int64_t krow0;   // first row of the sequence's entries in the buffer the attention reads k_pe
+                   // from: the cache's slot0, or (block table) the gathered copy's kbase
   int32_t l0;      // positions held before this call
   int32_t t;       // new tokens in this call
   int32_t q0;      // first row of this call's tokens in x / y
@@ -78,8 +80,13 @@ struct SeqMeta {
   int32_t pad;
 };
 
-hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const int64_t* offset_d,
+hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const SlotMap& map,
                         const int32_t* len_d, int B, SeqMeta* meta, hipStream_t s);
+// Block-table layout: the entries of each prefill sequence (positions 0 .. l0 + t - 1) copied into
+// rows kbase .. of `dst` (row stride entry_bytes), so that kv_b and the attention read them
+// contiguously. max_rows >= the largest l0 + t of the batch.
+hipError_t gather_entries(const uint8_t* cache, const SlotMap& map, const SeqMeta* meta, int B, int max_rows,
+                          int entry_bytes, uint8_t* dst, hipStream_t s);
 hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, int32_t* len_d, int B,
                           hipStream_t s);
 
@@ -108,8 +115,8 @@ struct NormArgs {
   int B;
   // decode
   const int32_t* seq_ids;
-  const int64_t* offset;
   int32_t* len;
+  SlotMap map;           // where each position's entry lives
 };
 hipError_t norm_rope_append(const NormArgs& a, hipStream_t s);
 
@@ -119,9 +126,10 @@ hipError_t norm_rope_append(const NormArgs& a, hipStream_t s);
 bool gemm_bf16_fuses_qnorm(const GemmArgs& a);
 hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s);
 
-// Byte copy of n ready-made entries to dst (the slot of position len[seq]); len[seq] += n.
-hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_bytes, int n, int seq, int32_t* len_d,
-                                hipStream_t s);
+// Byte copy of n ready-made entries to positions pos0 .. pos0 + n - 1 of sequence seq (slots from
+// `map`); len[seq] += n.
+hipError_t cache_copy_append(uint8_t* cache, const SlotMap& map, const uint8_t* src, int entry_bytes, int n, int seq,
+                             int pos0, int32_t* len_d, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Prefill attention (rebuilt keys/values, causal): o[row][h*128+d] bf16
@@ -163,7 +171,7 @@ struct DecodeAttnArgs {
   const float* rope_cs;
   int max_pos;
   const int32_t* seq_ids;
-  const int64_t* offset;
+  SlotMap map;             // where each position's entry lives (pages hold whole 32-position blocks)
   const int32_t* len;      // positions held INCLUDING this step's entry
   int B;
   int chunk;               // positions per split

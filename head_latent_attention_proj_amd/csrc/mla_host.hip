@@ -199,11 +199,12 @@ struct DecodePlan {
 };
 
 // Split size for decode attention: about total / D positions (at least 64), D = 384 for the bf16
-// kernel and 512 for the FP8 kernel. Chosen by measurement on MI355X: bf16, 64 sequences of
+// kernel and 256 for the FP8 kernel. Chosen by measurement on MI355X: bf16, 64 sequences of
 // 1024..8192 positions: D = 256 took 194 us, 384 took 137 us, 512 took 160 us, a cost-model
-// choice (640) 150 us; FP8, 128 sequences of 16385: D = 512 beat 384 and the cost model by
-// 10-20 %; one sequence of 1000 positions: 64-position splits beat 32 (fewer float32 partials)
-// and 128 or more (longer serial chains per workgroup).
+// choice (640) 150 us; FP8, 128 sequences of about 16400 positions: D = 256 (two splits per
+// sequence, one workgroup per CU) took 629 us, 512 (four) 644 us, 384 (three: one and a half
+// workgroups per CU) 824 us; one sequence of 1000 positions: 64-position splits beat 32 (fewer
+// float32 partials) and 128 or more (longer serial chains per workgroup).
 DecodePlan plan_decode(int B, const int* lens_after, int n, bool fp8) {
   int64_t total = 0;
   int max_len = 1;
@@ -211,7 +212,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n, bool fp8) {
     total += lens_after[i];
     max_len = std::max(max_len, lens_after[i]);
   }
-  const int64_t D = fp8 ? 512 : 384;
+  const int64_t D = fp8 ? 256 : 384;
   DecodePlan p;
   p.chunk = (int)std::max<int64_t>(64, round_up((total + D - 1) / D, 32));
   p.max_splits = (max_len + p.chunk - 1) / p.chunk;
@@ -226,7 +227,7 @@ struct WsLayout {
   size_t cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
   size_t knope_lo, vt_lo, qs;  // FP8 only: residual planes, split q_nope
   size_t o_lat;                // decode: merged latent attention output (bf16; FP8: 2 planes)
-  size_t x8, x8s, qh8s, o32, o8, o8s, total;
+  size_t x8, x8s, qh8s, o32, o8, o8s, gath, total;
   int64_t gpart_floats;
   int64_t vt_ld;
 };
@@ -284,6 +285,8 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   L.o8s = take(fp8 ? (size_t)ntok * (O_IN / 128) * 4 : 0);
   L.gpart_floats = gpart_floats;
   L.gpart = take((size_t)gpart_floats * 4);
+  // paged prefill: each sequence's entries gathered into rows kbase .. (same padding as the keys)
+  L.gath = take(decode_splits > 0 ? 0 : (size_t)L.vt_ld * (fp8 ? FP8_ENTRY_BYTES : BF16_ENTRY_BYTES));
   L.total = off;
   return L;
 }
@@ -303,27 +306,68 @@ int proj_ysplit(const mla_ctx* ctx, const mla_k::GemmArgs& g) {
   return ctx->fp8 ? mla_k::gemm_fp8_ysplit(g) : mla_k::gemm_ysplit(g);
 }
 
+bool paged(const mla_cache* c) { return c->page_size != 0; }
+
+int page_shift(int32_t page_size) {
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  return sh;
+}
+
 mla_status check_cache(const mla_ctx* ctx, const mla_cache* c) {
   if (!c) return fail(MLA_E_ARG, "cache is NULL");
-  if (!c->data || !c->offset_h || !c->offset_d || !c->len_h || !c->len_d || !c->cap_h)
-    return fail(MLA_E_ARG, "cache has a NULL pointer");
+  if (!c->data || !c->len_h || !c->len_d || !c->cap_h) return fail(MLA_E_ARG, "cache has a NULL pointer");
   if (c->n_seqs <= 0 || c->total_slots <= 0) return fail(MLA_E_ARG, "cache has no sequences or slots");
   if (!aligned16(c->data)) return fail(MLA_E_ALIGN, "cache data is not 16-byte aligned");
+  if (paged(c)) {
+    if (c->page_size < 64 || (c->page_size & (c->page_size - 1)) || c->total_slots % c->page_size)
+      return fail(MLA_E_ARG, "page_size %d must be a power of two >= 64 dividing total_slots", c->page_size);
+    if (!c->block_table_h || !c->block_table_d || c->max_pages <= 0)
+      return fail(MLA_E_ARG, "a paged cache needs both block tables and max_pages > 0");
+  } else if (!c->offset_h || !c->offset_d) {
+    return fail(MLA_E_ARG, "cache has a NULL offset array");
+  }
   (void)ctx;
   return MLA_OK;
+}
+
+SlotMap slot_map(const mla_cache* c) {
+  SlotMap m;
+  if (paged(c)) {
+    m.table = c->block_table_d;
+    m.page_shift = page_shift(c->page_size);
+    m.max_pages = c->max_pages;
+  } else {
+    m.offset = c->offset_d;
+  }
+  return m;
 }
 
 mla_status check_seq(const mla_ctx* ctx, const mla_cache* c, int s, int64_t add) {
   if (s < 0 || s >= c->n_seqs) return fail(MLA_E_ARG, "sequence id %d outside [0, %d)", s, c->n_seqs);
   const int64_t len = c->len_h[s];
-  if (len < 0 || c->cap_h[s] < 0 || c->offset_h[s] < 0 || c->offset_h[s] + c->cap_h[s] > c->total_slots)
+  if (len < 0 || c->cap_h[s] < 0)
+    return fail(MLA_E_ARG, "sequence %d has an inconsistent cap/len", s);
+  if (paged(c)) {
+    if ((int64_t)c->cap_h[s] > (int64_t)c->max_pages * c->page_size)
+      return fail(MLA_E_ARG, "sequence %d: capacity %d exceeds its %d table pages", s, c->cap_h[s], c->max_pages);
+  } else if (c->offset_h[s] < 0 || c->offset_h[s] + c->cap_h[s] > c->total_slots) {
     return fail(MLA_E_ARG, "sequence %d has an inconsistent offset/cap/len", s);
+  }
   if (len + add > c->cap_h[s])
     return fail(MLA_E_CAPACITY, "sequence %d: %lld positions + %lld new exceed its %d slots", s, (long long)len,
                 (long long)add, c->cap_h[s]);
   if (len + add > ctx->cfg.max_positions)
     return fail(MLA_E_CAPACITY, "sequence %d: %lld positions exceed max_positions %d", s, (long long)(len + add),
                 ctx->cfg.max_positions);
+  if (paged(c) && len + add > 0) {  // every page the call reads or writes names a page of the cache
+    const int64_t n_pages = c->total_slots / c->page_size;
+    const int32_t* row = c->block_table_h + (int64_t)s * c->max_pages;
+    for (int64_t pg = 0; pg <= (len + add - 1) / c->page_size; ++pg)
+      if (row[pg] < 0 || row[pg] >= n_pages)
+        return fail(MLA_E_ARG, "sequence %d: page %lld of its table is %d, outside [0, %lld)", s, (long long)pg,
+                    row[pg], (long long)n_pages);
+  }
   return MLA_OK;
 }
 
@@ -515,9 +559,8 @@ mla_status mla_cache_append(mla_ctx* ctx, mla_cache* cache, int32_t seq_id, cons
   st = check_seq(ctx, cache, seq_id, n);
   if (st != MLA_OK) return st;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
-  uint8_t* dst = (uint8_t*)cache->data + (cache->offset_h[seq_id] + cache->len_h[seq_id]) * (int64_t)eb;
-  HIP_TRY(mla_k::cache_copy_append_at(dst, (const uint8_t*)entries, eb, n, seq_id, cache->len_d,
-                                      (hipStream_t)stream));
+  HIP_TRY(mla_k::cache_copy_append((uint8_t*)cache->data, slot_map(cache), (const uint8_t*)entries, eb, n, seq_id,
+                                   cache->len_h[seq_id], cache->len_d, (hipStream_t)stream));
   cache->len_h[seq_id] += n;
   return MLA_OK;
 }
@@ -588,7 +631,8 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   const bool fp8 = ctx->fp8;
   const int eb = (int)mla_cache_entry_bytes(&ctx->cfg);
   auto* meta = (mla_k::SeqMeta*)(w + L.meta);
-  HIP_TRY(mla_k::prefill_plan(seq_ids_d, q_start_d, cache->offset_d, cache->len_d, B, meta, s));
+  const SlotMap map = slot_map(cache);
+  HIP_TRY(mla_k::prefill_plan(seq_ids_d, q_start_d, map, cache->len_d, B, meta, s));
 
   // 1. fused q_a | kv_a projection (fp32 out); FP8: x quantised per token and 128-group first
   if (fp8)
@@ -607,6 +651,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = ntok; na.meta = meta; na.B = B;
+  na.map = map;
   na.q_hat_codes = w + L.q_hat; na.q_hat_scales = (float*)(w + L.qh8s);
   HIP_TRY(mla_k::norm_rope_append(na, s));
   // 3. q_b
@@ -616,11 +661,21 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   g.C = w + L.q; g.ldc = QB_N; g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.tag = mla_k::TAG_QB;
   g.epi = fp8 ? mla_k::EPI_F32 : mla_k::EPI_BF16;
   HIP_TRY(run_proj(ctx, g, s));
-  // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values
+  // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values.
+  //    Paged cache: the sequences' entries are gathered into contiguous rows first (kv_b's rows and
+  //    the attention's rotary keys are then read from the copy).
+  const uint8_t* kv_rows = (const uint8_t*)cache->data;
+  if (paged(cache)) {
+    int max_rows = 0;
+    for (int b = 0; b < B; ++b)
+      max_rows = std::max(max_rows, cache->len_h[seq_ids_h[b]] + q_start_h[b + 1] - q_start_h[b]);
+    HIP_TRY(mla_k::gather_entries((const uint8_t*)cache->data, map, meta, B, max_rows, eb, w + L.gath, s));
+    kv_rows = w + L.gath;
+  }
   for (int b = 0; b < B; ++b) {
     const int sid = seq_ids_h[b];
     const int n = cache->len_h[sid] + q_start_h[b + 1] - q_start_h[b];
-    const uint8_t* rows = (const uint8_t*)cache->data + cache->offset_h[sid] * (int64_t)eb;
+    const uint8_t* rows = kv_rows + (paged(cache) ? kbase[b] : cache->offset_h[sid]) * (int64_t)eb;
     g = gemm_common(w, L);
     if (fp8) {  // entry = [512 codes | 4 group scales | k_pe]
       g.A = rows; g.lda = eb; g.a_scale = (const float*)(rows + KV_LORA); g.as_ld = eb / 4;
@@ -640,7 +695,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   mla_k::PrefillAttnArgs pa{};
   pa.q = w + L.q; pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
   pa.split = fp8; pa.knope_lo = (const uint16_t*)(w + L.knope_lo); pa.vt_lo = (const uint16_t*)(w + L.vt_lo);
-  pa.vt_ld = L.vt_ld; pa.cache = (const uint8_t*)cache->data; pa.entry_bytes = eb;
+  pa.vt_ld = L.vt_ld; pa.cache = kv_rows; pa.entry_bytes = eb;
   pa.kpe_off = fp8 ? KV_LORA + 16 : KV_LORA * 2;
   pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
   pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o); pa.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr;
@@ -714,7 +769,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   na.g_q = ctx->g_q; na.g_kv = ctx->g_kv; na.eps = ctx->cfg.rms_eps;
   na.q_hat = (uint16_t*)(w + L.q_hat); na.rope_cs = ctx->rope_cs; na.max_pos = ctx->cfg.max_positions;
   na.cache = (uint8_t*)cache->data; na.entry_bytes = eb; na.fp8 = fp8; na.n_tokens = B; na.meta = nullptr;
-  na.seq_ids = seq_ids_d; na.offset = cache->offset_d; na.len = cache->len_d;
+  na.seq_ids = seq_ids_d; na.map = slot_map(cache); na.len = cache->len_d;
   na.q_hat_codes = w + L.q_hat; na.q_hat_scales = (float*)(w + L.qh8s);
   // 3. q_b. bf16 weights at one or two tokens: the norms of step 2 run inside the q_b kernel
   //    (one launch less on a latency-bound path); otherwise a norm kernel first.
@@ -754,7 +809,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   da.q_lat = w + L.q_lat; da.q_lat_lo = (int64_t)B * HEADS * KV_LORA; da.q = w + L.q;
   da.cache = (const uint8_t*)cache->data;
   da.entry_bytes = eb; da.fp8 = fp8; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
-  da.seq_ids = seq_ids_d; da.offset = cache->offset_d; da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
+  da.seq_ids = seq_ids_d; da.map = slot_map(cache); da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
   da.max_splits = dp.max_splits; da.scale = ctx->scale; da.part_o = (float*)(w + L.part_o);
   da.part_ml = (float*)(w + L.part_ml); da.w_uv_s = ctx->s_kvb; da.o_lat = (uint16_t*)(w + L.o_lat);
   const bool fuse_uv = !fp8 && B <= mla_k::MERGE_UV_MAX_B;  // merge and W_UV in one kernel
@@ -857,6 +912,67 @@ mla_status mla_cache_pool_layer(void* pool, size_t pool_bytes, size_t layer_byte
   cache->data = (uint8_t*)pool + (size_t)layer * layer_bytes;
   return MLA_OK;
 }
+
+}  // extern "C"
+
+// Host page allocator: free ids in a FIFO ring (released pages are reused oldest first), plus an
+// allocation bit per page so that a double free or a foreign id is refused.
+struct mla_page_pool {
+  std::vector<int32_t> ring;  // free ids, head .. head + count - 1 (mod n)
+  std::vector<uint8_t> used;
+  int32_t head = 0, count = 0;
+};
+
+extern "C" {
+
+mla_status mla_page_pool_create(int32_t n_pages, mla_page_pool** out) {
+  if (!out) return fail(MLA_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_pages <= 0) return fail(MLA_E_ARG, "n_pages must be positive");
+  mla_page_pool* p = new mla_page_pool;
+  p->ring.resize(n_pages);
+  p->used.assign(n_pages, 0);
+  for (int32_t i = 0; i < n_pages; ++i) p->ring[i] = i;
+  p->count = n_pages;
+  *out = p;
+  return MLA_OK;
+}
+
+mla_status mla_page_pool_alloc(mla_page_pool* pool, int32_t n, int32_t* ids) {
+  if (!pool || (n > 0 && !ids)) return fail(MLA_E_ARG, "pool or ids is NULL");
+  if (n < 0) return fail(MLA_E_ARG, "n must not be negative");
+  if (n > pool->count) return fail(MLA_E_CAPACITY, "%d pages asked for, %d free", n, pool->count);
+  const int32_t size = (int32_t)pool->ring.size();
+  for (int32_t i = 0; i < n; ++i) {
+    ids[i] = pool->ring[pool->head];
+    pool->used[ids[i]] = 1;
+    pool->head = (pool->head + 1) % size;
+  }
+  pool->count -= n;
+  return MLA_OK;
+}
+
+mla_status mla_page_pool_free(mla_page_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || (n > 0 && !ids)) return fail(MLA_E_ARG, "pool or ids is NULL");
+  if (n < 0) return fail(MLA_E_ARG, "n must not be negative");
+  const int32_t size = (int32_t)pool->ring.size();
+  for (int32_t i = 0; i < n; ++i) {  // validate everything before changing anything
+    if (ids[i] < 0 || ids[i] >= size || !pool->used[ids[i]])
+      return fail(MLA_E_ARG, "page %d is not an allocated page of this pool", ids[i]);
+    for (int32_t j = 0; j < i; ++j)
+      if (ids[j] == ids[i]) return fail(MLA_E_ARG, "page %d is freed twice", ids[i]);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->used[ids[i]] = 0;
+    pool->ring[(pool->head + pool->count) % size] = ids[i];
+    ++pool->count;
+  }
+  return MLA_OK;
+}
+
+int32_t mla_page_pool_available(const mla_page_pool* pool) { return pool ? pool->count : -1; }
+
+void mla_page_pool_destroy(mla_page_pool* pool) { delete pool; }
 
 size_t mla_block_prefill_workspace_bytes(const mla_ctx* ctx, int32_t max_tokens, int32_t max_batch, int64_t max_keys) {
   const size_t n = mla_prefill_workspace_bytes(ctx, max_tokens, max_batch, max_keys);

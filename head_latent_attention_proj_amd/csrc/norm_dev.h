@@ -60,7 +60,7 @@ MLA_DEV void kv_norm_rope_append_bf16(const NormArgs& a, int tok, float* red, fl
   const int tid = threadIdx.x;
   const int seq = a.seq_ids[tok];
   const int pos = a.len[seq];
-  const int64_t slot = a.offset[seq] + pos;
+  const int64_t slot = slot_of(a.map, seq, pos);
   const float* row = a.cqkv + (int64_t)tok * QKVA_N;
   constexpr int MAX_PARTS = 4;
   float pv[MAX_PARTS][3];

@@ -10,6 +10,8 @@
 // The cache entry of a position is [c_hat (512) | rotated k_pe (64)] ("Key-value latent" page,
 // mla-kv excerpt: the 512 + 64 split of kv_a_proj_with_mqa; the latent RMSNorm output is the
 // input of kv_b, so it is what the keys and values are rebuilt from).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "norm_dev.h"
@@ -33,14 +35,15 @@ MLA_DEV uint32_t e4m3_rne_sat(float q) {
   return sign | (e << 3) | (r & 7u);
 }
 
-__global__ void plan_kernel(const int32_t* seq_ids, const int32_t* q_start, const int64_t* offset,
-                            const int32_t* len, int B, SeqMeta* meta) {
+__global__ void plan_kernel(const int32_t* seq_ids, const int32_t* q_start, SlotMap map, const int32_t* len, int B,
+                            SeqMeta* meta) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int kbase = 0;
   for (int b = 0; b < B; ++b) {
     const int s = seq_ids[b];
     SeqMeta m;
-    m.slot0 = offset[s];
+    m.slot0 = map.table ? 0 : map.offset[s];
+    m.krow0 = map.table ? kbase : m.slot0;  // block table: k_pe is read from the gathered copy
     m.l0 = len[s];
     m.q0 = q_start[b];
     m.t = q_start[b + 1] - q_start[b];
@@ -76,11 +79,11 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
     }
     const SeqMeta m = a.meta[lo];
     pos = m.l0 + (tok - m.q0);
-    slot = m.slot0 + pos;
+    slot = slot_of(a.map, m.seq, pos);
   } else {
     seq = a.seq_ids[tok];
     pos = a.len[seq];
-    slot = a.offset[seq] + pos;
+    slot = slot_of(a.map, seq, pos);
   }
 
   const float* row = a.cqkv + (int64_t)tok * QKVA_N;
@@ -196,10 +199,28 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   }
 }
 
-__global__ void copy_append_kernel(uint8_t* dst, const uint8_t* src, int64_t nvec, int32_t* len, int seq, int n) {
+// 16 bytes per thread; entry e of the n goes to the slot of position pos0 + e.
+__global__ void copy_append_kernel(uint8_t* cache, SlotMap map, const uint8_t* src, int eb, int64_t nvec, int32_t* len,
+                                   int seq, int pos0, int n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nvec) st16(dst + i * 16, ld16(src + i * 16));
+  if (i < nvec) {
+    const int vpe = eb >> 4;  // 16-byte pieces per entry
+    const int e = (int)(i / vpe), v = (int)(i - (int64_t)e * vpe);
+    st16(cache + slot_of(map, seq, pos0 + e) * eb + v * 16, ld16(src + i * 16));
+  }
   if (i == 0) len[seq] += n;
+}
+
+// Block-table prefill: sequence b's positions 0 .. l0 + t - 1 into rows kbase .. of dst.
+// blockIdx.y = sequence of the batch; 16 bytes per thread.
+__global__ void gather_kernel(const uint8_t* cache, SlotMap map, const SeqMeta* meta, int eb, uint8_t* dst) {
+  const SeqMeta m = meta[blockIdx.y];
+  const int vpe = eb >> 4;
+  const int64_t nvec = (int64_t)(m.l0 + m.t) * vpe;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(i / vpe), v = (int)(i - (int64_t)p * vpe);
+    st16(dst + ((int64_t)m.kbase + p) * eb + v * 16, ld16(cache + slot_of(map, m.seq, p) * eb + v * 16));
+  }
 }
 
 // One wave per 128-feature group of one row.
@@ -322,9 +343,17 @@ __global__ void fill_zero_kernel(int* p, int64_t n) {
 
 }  // namespace
 
-hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const int64_t* offset_d,
+hipError_t prefill_plan(const int32_t* seq_ids_d, const int32_t* q_start_d, const SlotMap& map,
                         const int32_t* len_d, int B, SeqMeta* meta, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, seq_ids_d, q_start_d, offset_d, len_d, B, meta);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, seq_ids_d, q_start_d, map, len_d, B, meta);
+  return hipGetLastError();
+}
+
+hipError_t gather_entries(const uint8_t* cache, const SlotMap& map, const SeqMeta* meta, int B, int max_rows,
+                          int entry_bytes, uint8_t* dst, hipStream_t s) {
+  const int64_t nvec = (int64_t)max_rows * (entry_bytes / 16);
+  const unsigned gx = (unsigned)std::min<int64_t>((nvec + 255) / 256, 1024);
+  hipLaunchKernelGGL(gather_kernel, dim3(gx, B), dim3(256), 0, s, cache, map, meta, entry_bytes, dst);
   return hipGetLastError();
 }
 
@@ -340,11 +369,11 @@ hipError_t norm_rope_append(const NormArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t cache_copy_append_at(uint8_t* dst, const uint8_t* src, int entry_bytes, int n, int seq, int32_t* len_d,
-                                hipStream_t s) {
+hipError_t cache_copy_append(uint8_t* cache, const SlotMap& map, const uint8_t* src, int entry_bytes, int n, int seq,
+                             int pos0, int32_t* len_d, hipStream_t s) {
   const int64_t nvec = (int64_t)n * entry_bytes / 16;
-  hipLaunchKernelGGL(copy_append_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s, dst, src, nvec,
-                     len_d, seq, n);
+  hipLaunchKernelGGL(copy_append_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, s, cache, map, src,
+                     entry_bytes, nvec, len_d, seq, pos0, n);
   return hipGetLastError();
 }
 

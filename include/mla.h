@@ -129,18 +129,34 @@ typedef struct {
  * per position against 576) are derived from these entries inside the kernels; the cache
  * keeps the 576-feature form ("In numbers" on the dense-block attention page: 70,272 vs
  * 2,498,560 bytes per token over 61 layers).
- * Sequence s owns slots [offset[s], offset[s] + cap[s]); position p of s is slot offset[s]+p.
- * len[s] = positions held. The library advances len_h at enqueue time and len_d on the stream;
- * the caller must keep them equal between calls (initialise both, e.g. to 0). */
+ * Two slot layouts:
+ *   contiguous (page_size = 0): sequence s owns slots [offset[s], offset[s] + cap[s]); position p
+ *     of s is slot offset[s] + p;
+ *   paged (page_size > 0, a power of two >= 64): the slots form pages of page_size consecutive
+ *     slots, page k = slots [k * page_size, (k + 1) * page_size); position p of s lives in page
+ *     block_table[s * max_pages + p / page_size] at offset p % page_size. The table rows name the
+ *     pages of each sequence in position order; pages may be anywhere and in any order (a cache
+ *     manager hands them out and takes them back, e.g. with mla_page_pool_*). offset_h/_d are
+ *     ignored. A call touching positions 0 .. n-1 of s needs valid page ids (in [0, total_slots /
+ *     page_size)) for pages 0 .. (n-1) / page_size of s's row, checked on the host before any
+ *     enqueue (MLA_E_ARG); pages must not be shared by sequences that a call writes.
+ * len[s] = positions held, cap[s] = positions the sequence may hold. The library advances len_h at
+ * enqueue time and len_d on the stream; the caller must keep them equal between calls (initialise
+ * both, e.g. to 0), and keep block_table_d equal to block_table_h. */
 typedef struct {
   void* data;              /* device, total_slots * entry_bytes, 16-byte aligned */
-  const int64_t* offset_h; /* host  [n_seqs] first slot of each sequence */
+  const int64_t* offset_h; /* host  [n_seqs] first slot of each sequence (contiguous layout) */
   const int64_t* offset_d; /* device[n_seqs] same values */
   int32_t* len_h;          /* host  [n_seqs] positions held */
   int32_t* len_d;          /* device[n_seqs] same values */
-  const int32_t* cap_h;    /* host  [n_seqs] slots reserved per sequence */
+  const int32_t* cap_h;    /* host  [n_seqs] positions reserved per sequence */
   int32_t n_seqs;
   int64_t total_slots;
+  /* paged layout (all zero / NULL: contiguous) */
+  const int32_t* block_table_h; /* host  [n_seqs][max_pages] page ids */
+  const int32_t* block_table_d; /* device, same values */
+  int32_t page_size;            /* slots per page: 0, or a power of two >= 64 */
+  int32_t max_pages;            /* row length of the block table (>= ceil(cap / page_size)) */
 } mla_cache;
 
 /* Bytes of the packed-weight buffer mla_init_weights fills (fused q_a|kv_a weight, transposed
@@ -256,6 +272,20 @@ mla_status mla_cache_pool_plan(const mla_config* cfg, int32_t n_layers, int32_t 
  * total_slots from the plan (shared by all layers) and the layer's own len_h / len_d. Host-only;
  * on an error *cache is unchanged. */
 mla_status mla_cache_pool_layer(void* pool, size_t pool_bytes, size_t layer_bytes, int32_t layer, mla_cache* cache);
+
+/* ---- Page allocator for paged caches (host only; the cache manager of a serving loop): a pool
+ * of n_pages page ids 0 .. n_pages-1. alloc hands out n free ids in ascending order of release
+ * (freed pages are reused first-in, first-out) or fails with MLA_E_CAPACITY, leaving the pool
+ * unchanged, when fewer are free; free takes ids back (MLA_E_ARG for an id out of range or not
+ * allocated, nothing freed then). A pool is not thread-safe: one thread at a time. With
+ * mla_cache_pool_plan-style stacks of layers, one page id addresses the same pages in every
+ * layer's region, so one pool and one block table serve the whole stack. */
+typedef struct mla_page_pool mla_page_pool;
+mla_status mla_page_pool_create(int32_t n_pages, mla_page_pool** out);
+mla_status mla_page_pool_alloc(mla_page_pool* pool, int32_t n, int32_t* ids);
+mla_status mla_page_pool_free(mla_page_pool* pool, const int32_t* ids, int32_t n);
+int32_t mla_page_pool_available(const mla_page_pool* pool); /* free pages; -1 for NULL */
+void mla_page_pool_destroy(mla_page_pool* pool);
 
 /* Append n ready-made entries (device, n * mla_cache_entry_bytes bytes, the slot format above)
  * to sequence seq_id at positions len .. len+n-1: a byte copy into the slots, then len += n.

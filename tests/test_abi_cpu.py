@@ -153,3 +153,31 @@ def test_cache_pool_rejects_bad_arguments(L):
     assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1152, 2, None) == 1
     assert L.mla_cache_pool_layer(ctypes.c_void_p(base), 4096, 1152, 1, ctypes.byref(desc)) == 0
     assert desc.data == base + 1152
+
+
+def test_page_pool_hands_out_and_takes_back_pages(L):
+    """The host page allocator of paged caches: ids in order, FIFO reuse of released pages, and
+    refusals (too few free, double free, foreign id) that change nothing."""
+    import numpy as np
+
+    pool = binding.PagePool(5)
+    assert pool.available == 5
+    assert pool.alloc(3).tolist() == [0, 1, 2] and pool.available == 2
+    with pytest.raises(binding.MlaError) as ei:
+        pool.alloc(3)
+    assert ei.value.status == 3 and pool.available == 2  # MLA_E_CAPACITY, nothing taken
+    pool.free([1])
+    assert pool.available == 3
+    assert pool.alloc(3).tolist() == [3, 4, 1]  # never-used pages first, then the released one
+    with pytest.raises(binding.MlaError) as ei:
+        pool.free([2, 2])
+    assert ei.value.status == 1 and pool.available == 0  # a double free is refused as a whole
+    with pytest.raises(binding.MlaError):
+        pool.free([7])
+    pool.free([2, 0])
+    assert pool.available == 2 and pool.alloc(2).tolist() == [2, 0]
+    h = ctypes.c_void_p()
+    assert L.mla_page_pool_create(0, ctypes.byref(h)) == 1
+    assert L.mla_page_pool_available(None) == -1
+    ids = np.zeros(1, dtype=np.int32)
+    assert L.mla_page_pool_alloc(None, 1, ids.ctypes.data) == 1
