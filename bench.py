@@ -392,8 +392,9 @@ def main():
         extra["C4_prefill_B4_T4096_fp8"] = {
             "ms": round(t * 1e3, 3), "tokens_per_s": round(4 * T8 / t, 1), "tflops": round(fl / t / 1e12, 2),
             "mfma_frac": round((proj_fp8 / FP8_PEAK + att / BF16_PEAK) / t, 4),
-            "roofline": roofline("prefill_attn_kernel<true> (causal, split precision)", "mfma-bf16", att, t_at,
-                                 "flops: 640 per head per causal pair (counted once, though computed in split precision)"),
+            "roofline": roofline("prefill_attn_kernel<true> (causal, fp16 operands, value residuals)", "mfma-bf16", att,
+                                 t_at, "flops: 640 per head per causal pair (counted once, though the value products "
+                                       "run twice: values and their fp16 residuals)"),
             "roofline_oproj": roofline("gemm_fp8_tile_kernel (o_proj, M=16384, N=7168, K=8192, FP8)", "mfma-fp8",
                                        2 * 4 * T8 * 8192 * 7168, t_op, "flops: 2 M N K"),
             "note": "mfma_frac = (fp8 projection flops / 5 PF + attention flops / 2.5 PF) / time"}

@@ -14,6 +14,8 @@
 // register prefetch. Workgroups are numbered head-fastest so every query tile of one head
 // lands on the same XCD (its L2 keeps that head's keys and values); query tiles run
 // longest-first.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,12 +32,28 @@ constexpr float LOG2E = 1.4426950408889634f;
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 MLA_DEV void st8(void* p, const u32x2_t& v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
-// SPLIT (FP8 weights): q arrives in float32 and K_nope, V^T, k_pe and the probabilities carry a
-// bf16 residual next to their bf16 value; each product takes hi*hi + hi*lo + lo*hi, which is
-// accurate to about 16 significant bits (the FP8 path's o_proj quantiser amplifies any rounding
-// of its input, so bf16 alone is not enough there).
+// SPLIT (FP8 weights): q and k_pe arrive in float32, K_nope and V^T in fp16 with an fp16 residual
+// plane of V^T. Queries and keys are rounded to fp16 (11 significant bits) and the probabilities
+// too; each score is one fp16 product, each value product two (value and its residual), so the
+// values enter at about 22 bits. Chosen from a CPU emulation of these roundings against the W8A8
+// float64 layer (the FP8 path's o_proj quantiser amplifies any rounding of its input): bf16
+// hi + lo parts on every operand (three products each way) gave 8.0e-3 max-abs on the layer
+// output, this form 9.8e-3, a single fp16 product for the values too 1.6e-2.
 template <bool SPLIT>
-__global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(PrefillAttnArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
+  using frag_t = std::conditional_t<SPLIT, f16x8_t, bf16x8_t>;
+  auto as_frag = [](const u32x4_t& v) {
+    if constexpr (SPLIT) return as_f16x8(v);
+    else return as_bf16x8(v);
+  };
+  auto mm = [](const frag_t& x, const frag_t& y, const f32x4_t& c) {
+    if constexpr (SPLIT) return mfma_f16_16x16x32(x, y, c);
+    else return mfma_bf16_16x16x32(x, y, c);
+  };
+  auto pack2 = [](float lo, float hi) {
+    if constexpr (SPLIT) return pack_f16x2(lo, hi);
+    else return pack_bf16x2(lo, hi);
+  };
   const int h = blockIdx.x;
   const int b = blockIdx.z;
   const SeqMeta m = a.meta[b];
@@ -53,11 +71,10 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[PKB * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[128 * LDV];
-  __shared__ __attribute__((aligned(16))) uint16_t sKl[SPLIT ? PKB * LDK : 8];  // residual planes
-  __shared__ __attribute__((aligned(16))) uint16_t sVl[SPLIT ? 128 * LDV : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sVl[SPLIT ? 128 * LDV : 8];  // value residuals
 
   // ---- Q fragments: B operand of S^T, column = query, 8 features of group g per k-step
-  bf16x8_t qf[2][6], ql[SPLIT ? 2 : 1][6];
+  frag_t qf[2][6];
   int qpos[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -80,7 +97,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
       } else {
         const u32x4_t raw = ld16((const uint16_t*)a.q + qoff + ks * 32 + g * 8);
         if (ks < 4) {
-          qf[qt][ks] = as_bf16x8(raw);
+          qf[qt][ks] = as_frag(raw);
           continue;
         }
 #pragma unroll
@@ -100,121 +117,93 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
           x[2 * j + 1] = x0 * sn + x1 * c;
         }
       }
-      u32x4_t hi, lo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-        lo[j] = pack_bf16x2(x[2 * j] - bf_lo(hi[j]), x[2 * j + 1] - bf_hi(hi[j]));
-      }
-      qf[qt][ks] = as_bf16x8(hi);
-      if constexpr (SPLIT) ql[qt][ks] = as_bf16x8(lo);
+      qf[qt][ks] = as_frag(u32x4_t{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])});
     }
   }
 
-  // ---- block staging (global -> registers -> LDS)
-  u32x4_t pk[4], pp[2], pv[4];
+  // ---- block staging (global -> registers -> LDS), one block ahead; the value residuals (FP8) are
+  // loaded at staging time instead (held across the block's math they would spill registers)
+  constexpr int NPP = SPLIT ? 4 : 2;  // k_pe pieces per thread (float32 in FP8 entries)
+  u32x4_t pk[4], pp[NPP], pv[4];
   const int kr = tid >> 4, kc = (tid & 15) * 8;   // K_nope: 16 threads per key row (256 B)
-  const int pr = tid >> 3, pc = (tid & 7) * 8;    // k_pe / V^T: 8 threads per 128-byte row
+  const int pr = tid >> 3, pc = (tid & 7) * 8;    // V^T: 8 threads per 128-byte row; bf16 k_pe likewise
+  const int fr = tid >> 2, fc = (tid & 3) * 16;   // float32 k_pe: 4 threads per 256-byte row
   // Bases common to the workgroup (scalar registers) plus 32-bit per-lane byte offsets: a load
   // costs one address register and a 32-bit add instead of a 64-bit multiply-add per block.
   const uint8_t* kn_base = (const uint8_t*)(a.knope + ((int64_t)m.kbase * 64 + h) * 128);
   const uint8_t* pe_base = a.cache + m.krow0 * a.entry_bytes + a.kpe_off;
   const uint8_t* vt_base = (const uint8_t*)(a.vt + (int64_t)(h * 128) * a.vt_ld + m.kbase);
+  const uint8_t* vl_base = SPLIT ? (const uint8_t*)(a.vt_lo + (int64_t)(h * 128) * a.vt_ld + m.kbase) : nullptr;
+  // value row piece (i, this thread) of block kb: byte offset from vt_base / vl_base
+  auto voff = [&](int i, int kb) { return ((uint32_t)(i * 32 + pr) * (uint32_t)a.vt_ld + (uint32_t)(kb + pc)) * 2u; };
+  // keys past the last one are not written by kv_b: their value pieces are zeroed
+  auto vmask = [&](int kb, int j) {
+    const int key = kb + pc + 2 * j;
+    uint32_t mask = 0xffffffffu;
+    if (key >= n_keys) mask &= 0xffff0000u;
+    if (key + 1 >= n_keys) mask &= 0x0000ffffu;
+    return mask;
+  };
   auto gload = [&](int blk) {
-    if constexpr (SPLIT) return;  // split staging loads and stores in one step (stage_split)
     const int kb = blk * PKB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t key = (uint32_t)min(kb + i * 16 + kr, n_keys - 1);
       pk[i] = ld16(kn_base + (key * (64u * 128u * 2u) + (uint32_t)kc * 2u));
     }
+    if constexpr (SPLIT) {
+      const uint32_t key = (uint32_t)min(kb + fr, n_keys - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t key = (uint32_t)min(kb + i * 32 + pr, n_keys - 1);
-      pp[i] = ld16(pe_base + (key * (uint32_t)a.entry_bytes + (uint32_t)pc * 2u));
+      for (int i = 0; i < 4; ++i) pp[i] = ld16(pe_base + (key * (uint32_t)a.entry_bytes + (uint32_t)(fc + 4 * i) * 4u));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t key = (uint32_t)min(kb + i * 32 + pr, n_keys - 1);
+        pp[i] = ld16(pe_base + (key * (uint32_t)a.entry_bytes + (uint32_t)pc * 2u));
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t row = (uint32_t)(i * 32 + pr);
-      pv[i] = ld16(vt_base + (row * (uint32_t)a.vt_ld + (uint32_t)(kb + pc)) * 2u);
-    }
-    if (kb + PKB > n_keys) {  // value rows past the last key are not written: zero them
+    for (int i = 0; i < 4; ++i) pv[i] = ld16(vt_base + voff(i, kb));
+    if (kb + PKB > n_keys) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kb + pc + 2 * j;
-          uint32_t w = pv[i][j];
-          if (key >= n_keys) w &= 0xffff0000u;
-          if (key + 1 >= n_keys) w &= 0x0000ffffu;
-          pv[i][j] = w;
-        }
-    }
-  };
-  // Split staging: hi and lo planes of K_nope and V^T, float32 k_pe split on the way to LDS.
-  // Loads are not held across the block's math (the registers hold the split queries instead).
-  auto stage_split = [&](int blk) {
-    const int kb = blk * PKB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(kb + i * 16 + kr, n_keys - 1);
-      const int64_t off = ((int64_t)(m.kbase + key) * 64 + h) * 128 + kc;
-      const u32x4_t x = ld16(a.knope + off), y = ld16(a.knope_lo + off);
-      st16(sK + (i * 16 + kr) * LDK + kc, x);
-      st16(sKl + (i * 16 + kr) * LDK + kc, y);
-    }
-    {
-      const int key = min(kb + (tid >> 2), n_keys - 1);
-      const float* kp = (const float*)(a.cache + (m.krow0 + key) * a.entry_bytes + a.kpe_off) + (tid & 3) * 16;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(kp + 4 * c);
-        const uint32_t h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
-        const uint32_t r0 = pack_bf16x2(v[0] - bf_lo(h0), v[1] - bf_hi(h0));
-        const uint32_t r1 = pack_bf16x2(v[2] - bf_lo(h1), v[3] - bf_hi(h1));
-        const int col = 128 + (tid & 3) * 16 + 4 * c;
-        st8(sK + (tid >> 2) * LDK + col, u32x2_t{h0, h1});
-        st8(sKl + (tid >> 2) * LDK + col, u32x2_t{r0, r1});
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i * 32 + pr;
-      const int64_t off = (int64_t)(h * 128 + row) * a.vt_ld + m.kbase + kb + pc;
-      u32x4_t x = ld16(a.vt + off), y = ld16(a.vt_lo + off);
-      if (kb + PKB > n_keys) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kb + pc + 2 * j;
-          uint32_t mask = 0xffffffffu;
-          if (key >= n_keys) mask &= 0xffff0000u;
-          if (key + 1 >= n_keys) mask &= 0x0000ffffu;
-          x[j] &= mask;
-          y[j] &= mask;
-        }
-      }
-      uint16_t* d = sV + row * LDV + pc;
-      st8(d, u32x2_t{x[0], x[1]});
-      st8(d + 4, u32x2_t{x[2], x[3]});
-      uint16_t* dl = sVl + row * LDV + pc;
-      st8(dl, u32x2_t{y[0], y[1]});
-      st8(dl + 4, u32x2_t{y[2], y[3]});
+        for (int j = 0; j < 4; ++j) pv[i][j] &= vmask(kb, j);
     }
   };
   auto sstore = [&](int blk) {
+    const int kb = blk * PKB;
+    u32x4_t pvl[SPLIT ? 4 : 1];
     if constexpr (SPLIT) {
-      stage_split(blk);
-      return;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pvl[i] = ld16(vl_base + voff(i, kb));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) st16(sK + (i * 16 + kr) * LDK + kc, pk[i]);
+    if constexpr (SPLIT) {  // float32 rotary key -> fp16
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st16(sK + (i * 32 + pr) * LDK + 128 + pc, pp[i]);
+      for (int i = 0; i < 4; ++i)
+        st8(sK + fr * LDK + 128 + fc + 4 * i,
+            u32x2_t{pack_f16x2(__uint_as_float(pp[i][0]), __uint_as_float(pp[i][1])),
+                    pack_f16x2(__uint_as_float(pp[i][2]), __uint_as_float(pp[i][3]))});
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) st16(sK + (i * 32 + pr) * LDK + 128 + pc, pp[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint16_t* d = sV + (i * 32 + pr) * LDV + pc;
       st8(d, u32x2_t{pv[i][0], pv[i][1]});
       st8(d + 4, u32x2_t{pv[i][2], pv[i][3]});
+      if constexpr (SPLIT) {
+        if (kb + PKB > n_keys) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pvl[i][j] &= vmask(kb, j);
+        }
+        uint16_t* dl = sVl + (i * 32 + pr) * LDV + pc;
+        st8(dl, u32x2_t{pvl[i][0], pvl[i][1]});
+        st8(dl + 4, u32x2_t{pvl[i][2], pvl[i][3]});
+      }
     }
   };
 
@@ -242,30 +231,18 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
     for (int kt = 0; kt < 4; ++kt) sacc[kt][0] = sacc[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
-      bf16x8_t kf[4];
+      frag_t kf[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_bf16x8(ld16(sK + (kt * 16 + l16) * LDK + ks * 32 + g * 8));
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_frag(ld16(sK + (kt * 16 + l16) * LDK + ks * 32 + g * 8));
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt][0] = mfma_bf16_16x16x32(kf[kt], qf[0][ks], sacc[kt][0]);
-        sacc[kt][1] = mfma_bf16_16x16x32(kf[kt], qf[1][ks], sacc[kt][1]);
-        if constexpr (SPLIT) {
-          sacc[kt][0] = mfma_bf16_16x16x32(kf[kt], ql[0][ks], sacc[kt][0]);
-          sacc[kt][1] = mfma_bf16_16x16x32(kf[kt], ql[1][ks], sacc[kt][1]);
-        }
-      }
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8_t kl = as_bf16x8(ld16(sKl + (kt * 16 + l16) * LDK + ks * 32 + g * 8));
-          sacc[kt][0] = mfma_bf16_16x16x32(kl, qf[0][ks], sacc[kt][0]);
-          sacc[kt][1] = mfma_bf16_16x16x32(kl, qf[1][ks], sacc[kt][1]);
-        }
+        sacc[kt][0] = mm(kf[kt], qf[0][ks], sacc[kt][0]);
+        sacc[kt][1] = mm(kf[kt], qf[1][ks], sacc[kt][1]);
       }
     }
 
     const bool need_mask = kb + PKB - 1 > wq_lo;
-    bf16x8_t pf[2][2], pl[SPLIT ? 2 : 1][2];
+    frag_t pf[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       // scores stay unscaled here: the scale (softmax scale times log2 e, positive) commutes with
@@ -308,22 +285,11 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
         }
       lrun[qt] += psum;
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        u32x4_t w;
-        w[0] = pack_bf16x2(sacc[2 * ps][qt][0], sacc[2 * ps][qt][1]);
-        w[1] = pack_bf16x2(sacc[2 * ps][qt][2], sacc[2 * ps][qt][3]);
-        w[2] = pack_bf16x2(sacc[2 * ps + 1][qt][0], sacc[2 * ps + 1][qt][1]);
-        w[3] = pack_bf16x2(sacc[2 * ps + 1][qt][2], sacc[2 * ps + 1][qt][3]);
-        pf[ps][qt] = as_bf16x8(w);
-        if constexpr (SPLIT) {
-          u32x4_t r;
-          r[0] = pack_bf16x2(sacc[2 * ps][qt][0] - bf_lo(w[0]), sacc[2 * ps][qt][1] - bf_hi(w[0]));
-          r[1] = pack_bf16x2(sacc[2 * ps][qt][2] - bf_lo(w[1]), sacc[2 * ps][qt][3] - bf_hi(w[1]));
-          r[2] = pack_bf16x2(sacc[2 * ps + 1][qt][0] - bf_lo(w[2]), sacc[2 * ps + 1][qt][1] - bf_hi(w[2]));
-          r[3] = pack_bf16x2(sacc[2 * ps + 1][qt][2] - bf_lo(w[3]), sacc[2 * ps + 1][qt][3] - bf_hi(w[3]));
-          pl[ps][qt] = as_bf16x8(r);
-        }
-      }
+      for (int ps = 0; ps < 2; ++ps)
+        pf[ps][qt] = as_frag(u32x4_t{pack2(sacc[2 * ps][qt][0], sacc[2 * ps][qt][1]),
+                                     pack2(sacc[2 * ps][qt][2], sacc[2 * ps][qt][3]),
+                                     pack2(sacc[2 * ps + 1][qt][0], sacc[2 * ps + 1][qt][1]),
+                                     pack2(sacc[2 * ps + 1][qt][2], sacc[2 * ps + 1][qt][3])});
     }
     // O^T[d][q] += V^T[d][keys] P^T[keys][q]; lane group g holds keys {g*4..+3, 16+g*4..+3}
 #pragma unroll
@@ -332,17 +298,15 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void prefill_attn_kernel(Prefil
       for (int d = 0; d < 8; ++d) {
         const uint16_t* vp = sV + (d * 16 + l16) * LDV + ps * 32 + g * 4;
         const u32x2_t lo = ld8(vp), hi = ld8(vp + 16);
-        const bf16x8_t vf = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-        oacc[d][0] = mfma_bf16_16x16x32(vf, pf[ps][0], oacc[d][0]);
-        oacc[d][1] = mfma_bf16_16x16x32(vf, pf[ps][1], oacc[d][1]);
+        const frag_t vf = as_frag(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+        oacc[d][0] = mm(vf, pf[ps][0], oacc[d][0]);
+        oacc[d][1] = mm(vf, pf[ps][1], oacc[d][1]);
         if constexpr (SPLIT) {
           const uint16_t* vl = sVl + (d * 16 + l16) * LDV + ps * 32 + g * 4;
           const u32x2_t lo2 = ld8(vl), hi2 = ld8(vl + 16);
-          const bf16x8_t vfl = as_bf16x8(u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]});
-          oacc[d][0] = mfma_bf16_16x16x32(vf, pl[ps][0], oacc[d][0]);
-          oacc[d][1] = mfma_bf16_16x16x32(vf, pl[ps][1], oacc[d][1]);
-          oacc[d][0] = mfma_bf16_16x16x32(vfl, pf[ps][0], oacc[d][0]);
-          oacc[d][1] = mfma_bf16_16x16x32(vfl, pf[ps][1], oacc[d][1]);
+          const frag_t vfl = as_frag(u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]});
+          oacc[d][0] = mm(vfl, pf[ps][0], oacc[d][0]);
+          oacc[d][1] = mm(vfl, pf[ps][1], oacc[d][1]);
         }
       }
   }

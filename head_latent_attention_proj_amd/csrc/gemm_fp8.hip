@@ -58,19 +58,16 @@ MLA_DEV void epi_store8(const GemmArgs& p, int b, int m, int n, float v) {
   } else if (p.epi == EPI_BF16) {
     if (p.resid) v += bf2f(p.resid[(int64_t)m * p.ldr + n]);
     ((uint16_t*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = f2bf(v);
-  } else {  // EPI_KVB; with knope_lo / vt_lo set, the bf16 residual goes to a second plane
+  } else {  // EPI_KVB in fp16; with vt_lo set, the values' fp16 residuals go to a second plane
     const int h = n >> 8, r = n & 255;
     const int64_t key = p.key_base + m;
-    const uint16_t hi = f2bf(v);
-    const uint16_t lo = f2bf(v - bf2f(hi));
+    const uint32_t hv = pack_f16x2(v, 0.f);
     if (r < 128) {
-      const int64_t i = key * 8192 + h * 128 + r;
-      p.knope[i] = hi;
-      if (p.knope_lo) p.knope_lo[i] = lo;
+      p.knope[key * 8192 + h * 128 + r] = (uint16_t)hv;
     } else {
       const int64_t i = (int64_t)(h * 128 + r - 128) * p.vt_ld + key;
-      p.vt[i] = hi;
-      if (p.vt_lo) p.vt_lo[i] = lo;
+      p.vt[i] = (uint16_t)hv;
+      if (p.vt_lo) p.vt_lo[i] = (uint16_t)pack_f16x2(v - f16_lo(hv), 0.f);
     }
   }
 }
@@ -355,13 +352,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     }
     if constexpr (WTN == 64 && WM * WN * WTM * (WTN + 8) * 4 <= 2 * (BM + BN) * LDK) {
       if (p.epi == EPI_KVB && (p.key_base & 3) == 0 && (p.N & 7) == 0) {
-        // kv_b: a wave's 64 columns lie in one half of a head's 256 (wave-uniform). Content keys
-        // and their bf16 residuals go through LDS (two planes per wave) and leave as 16-byte
-        // pieces of K_nope rows; values go straight to V^T as 8-byte pieces (four consecutive
-        // keys of one feature per lane). Every wave reaches the barrier.
+        // kv_b (fp16): a wave's 64 columns lie in one half of a head's 256 (wave-uniform). Content
+        // keys go through LDS and leave as 16-byte pieces of K_nope rows; values and their fp16
+        // residuals go straight to V^T as 8-byte pieces (four consecutive keys of one feature per
+        // lane). Every wave reaches the barrier.
         constexpr int LDW = WTN + 8;
-        uint16_t* shi = reinterpret_cast<uint16_t*>(smem) + wave * (2 * WTM * LDW);
-        uint16_t* slo = shi + WTM * LDW;
+        uint16_t* shi = reinterpret_cast<uint16_t*>(smem) + wave * (WTM * LDW);
         const int nw0 = n0 + wn * WTN;
         const bool khalf = (nw0 & 255) < 128;
         if (khalf) {
@@ -370,13 +366,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float v = acc[i][j][e];
-                const uint16_t h = f2bf(v);
-                const int at = (i * 16 + g * 4 + e) * LDW + j * 16 + l16;
-                shi[at] = h;
-                slo[at] = f2bf(v - bf2f(h));
-              }
+              for (int e = 0; e < 4; ++e)
+                shi[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = (uint16_t)pack_f16x2(acc[i][j][e], 0.f);
         } else {
 #pragma unroll
           for (int i = 0; i < TM; ++i)
@@ -387,12 +378,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
               if (n >= p.N) continue;
               if (mb + 3 < p.M) {
                 const f32x4_t v = acc[i][j];
-                const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+                const uint32_t h01 = pack_f16x2(v[0], v[1]), h23 = pack_f16x2(v[2], v[3]);
                 const int64_t at = (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb;
                 *reinterpret_cast<u32x2_t*>(p.vt + at) = u32x2_t{h01, h23};
                 if (p.vt_lo)
                   *reinterpret_cast<u32x2_t*>(p.vt_lo + at) =
-                      u32x2_t{pack_bf16x2(v[0] - bf_lo(h01), v[1] - bf_hi(h01)), pack_bf16x2(v[2] - bf_lo(h23), v[3] - bf_hi(h23))};
+                      u32x2_t{pack_f16x2(v[0] - f16_lo(h01), v[1] - f16_hi(h01)), pack_f16x2(v[2] - f16_lo(h23), v[3] - f16_hi(h23))};
               } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -413,7 +404,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
               if (m < p.M) {
                 const int64_t at = (p.key_base + m) * 8192 + col;
                 st16(p.knope + at, ld16(shi + r * LDW + lc8));
-                if (p.knope_lo) st16(p.knope_lo + at, ld16(slo + r * LDW + lc8));
               }
             }
           }
@@ -434,12 +424,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
           if (n >= p.N) continue;
           if ((n & 255) >= 128 && mb + 3 < p.M) {
             const f32x4_t v = acc[i][j];
-            const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+            const uint32_t h01 = pack_f16x2(v[0], v[1]), h23 = pack_f16x2(v[2], v[3]);
             const int64_t at = (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb;
             *reinterpret_cast<u32x2_t*>(p.vt + at) = u32x2_t{h01, h23};
             if (p.vt_lo)
               *reinterpret_cast<u32x2_t*>(p.vt_lo + at) =
-                  u32x2_t{pack_bf16x2(v[0] - bf_lo(h01), v[1] - bf_hi(h01)), pack_bf16x2(v[2] - bf_lo(h23), v[3] - bf_hi(h23))};
+                  u32x2_t{pack_f16x2(v[0] - f16_lo(h01), v[1] - f16_hi(h01)), pack_f16x2(v[2] - f16_lo(h23), v[3] - f16_hi(h23))};
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)

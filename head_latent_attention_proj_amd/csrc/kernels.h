@@ -14,7 +14,8 @@ enum Epilogue : int {
   EPI_F32 = 0,   // C float32
   EPI_BF16 = 1,  // C bf16
   EPI_KVB = 2,   // kv_b output split per head: content keys -> knope[key][h*128+d] (bf16),
-                 // values -> vt[(h*128+d) * vt_ld + key] (bf16, key-contiguous for P.V)
+                 // values -> vt[(h*128+d) * vt_ld + key] (bf16, key-contiguous for P.V);
+                 // FP8 kernels write fp16 there instead (see vt_lo)
 };
 
 // Stage tags: one kernel symbol per projection so traces attribute time per stage.
@@ -33,8 +34,8 @@ struct GemmArgs {
   // EPI_KVB destinations
   uint16_t* knope = nullptr;
   uint16_t* vt = nullptr;
-  uint16_t* knope_lo = nullptr;  // FP8 kernels only: optional planes of the bf16 residuals
-  uint16_t* vt_lo = nullptr;     // (value - bf16(value)), same layout as knope / vt
+  uint16_t* vt_lo = nullptr;     // FP8 kernels only: optional plane of the fp16 value residuals
+                                 // (value - fp16(value)), same layout as vt
   int64_t vt_ld = 0;
   int64_t key_base = 0;
   // FP8 (E4M3FN codes) operands: A scales per (row, 128-group) with row stride as_ld floats;
@@ -136,13 +137,12 @@ hipError_t cache_copy_append(uint8_t* cache, const SlotMap& map, const uint8_t* 
 // ---------------------------------------------------------------------------------------------
 struct PrefillAttnArgs {
   const void* q;           // [n_tok][64][192] bf16 (split: float32), rotary part not yet rotated
-  const uint16_t* knope;   // [keys][64][128] bf16
-  const uint16_t* vt;      // [64*128][vt_ld] bf16
+  const uint16_t* knope;   // [keys][64][128] bf16 (split: fp16)
+  const uint16_t* vt;      // [64*128][vt_ld] bf16 (split: fp16)
   int64_t vt_ld;
-  // split precision (FP8 weights): q is float32 and every product is carried as bf16 hi + lo
-  // parts; knope_lo / vt_lo hold the residuals of knope / vt, k_pe is float32 in the entry
+  // split precision (FP8 weights): q is float32, k_pe float32 in the entry; queries and keys are
+  // rounded to fp16 and the values carry an fp16 residual plane vt_lo next to vt
   int split;
-  const uint16_t* knope_lo;
   const uint16_t* vt_lo;
   const uint8_t* cache;    // for the rotated shared key k_pe of each position
   int entry_bytes;

@@ -225,7 +225,7 @@ DecodePlan plan_decode(int B, const int* lens_after, int n, bool fp8) {
 
 struct WsLayout {
   size_t cqkv, q_hat, q, o, meta, knope, vt, q_lat, part_o, part_ml, gpart;
-  size_t knope_lo, vt_lo, qs;  // FP8 only: residual planes, split q_nope
+  size_t vt_lo, qs;  // FP8 only: fp16 residual plane of the values, split q_nope
   size_t o_lat;                // decode: merged latent attention output (bf16; FP8: 2 planes)
   size_t x8, x8s, qh8s, o32, o8, o8s, gath, total;
   int64_t gpart_floats;
@@ -269,7 +269,6 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   L.vt_ld = round_up(nkeys, 64);
   L.knope = take((size_t)L.vt_ld * HEADS * NOPE * 2);
   L.vt = take((size_t)L.vt_ld * HEADS * VD * 2);
-  L.knope_lo = take(fp8 ? (size_t)L.vt_ld * HEADS * NOPE * 2 : 0);
   L.vt_lo = take(fp8 ? (size_t)L.vt_ld * HEADS * VD * 2 : 0);
   // q_lat: bf16 [B][64][512], or FP8: two float32 products (high and residual part of q_nope)
   L.q_lat = take(decode_splits > 0 ? (size_t)nbatch * HEADS * KV_LORA * (fp8 ? 8 : 2) : 0);
@@ -686,15 +685,15 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
     g.M = n; g.N = KVB_N; g.K = KV_LORA; g.epi = mla_k::EPI_KVB; g.tag = mla_k::TAG_KVB;
     g.knope = (uint16_t*)(w + L.knope); g.vt = (uint16_t*)(w + L.vt); g.vt_ld = L.vt_ld; g.key_base = kbase[b];
     if (fp8) {
-      g.knope_lo = (uint16_t*)(w + L.knope_lo);
       g.vt_lo = (uint16_t*)(w + L.vt_lo);
     }
     HIP_TRY(run_proj(ctx, g, s));
   }
-  // 5. causal attention (FP8: split precision, float32 output -- the o_proj quantiser's input)
+  // 5. causal attention (FP8: fp16 operands with value residuals, float32 output -- the o_proj
+  //    quantiser's input)
   mla_k::PrefillAttnArgs pa{};
   pa.q = w + L.q; pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
-  pa.split = fp8; pa.knope_lo = (const uint16_t*)(w + L.knope_lo); pa.vt_lo = (const uint16_t*)(w + L.vt_lo);
+  pa.split = fp8; pa.vt_lo = (const uint16_t*)(w + L.vt_lo);
   pa.vt_ld = L.vt_ld; pa.cache = kv_rows; pa.entry_bytes = eb;
   pa.kpe_off = fp8 ? KV_LORA + 16 : KV_LORA * 2;
   pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
