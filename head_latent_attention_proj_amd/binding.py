@@ -26,7 +26,7 @@ EXPORTED = (
     "mla_cache_pool_plan", "mla_cache_pool_layer",
     "mla_test_gemm_workspace_bytes", "mla_test_gemm", "mla_decode_static", "mla_test_probe_stage",
     "mla_page_pool_create", "mla_page_pool_alloc", "mla_page_pool_free", "mla_page_pool_available",
-    "mla_page_pool_destroy",
+    "mla_page_pool_destroy", "mla_test_gemm_fp8_workspace_bytes", "mla_test_gemm_fp8",
 )
 STAGE = {"none": 0, "qkva": 1, "qb": 2, "kvb": 3, "oproj": 4, "absorb": 5, "uv": 6, "decode_attn": 7,
          "prefill_attn": 8}
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
     L.mla_test_gemm_workspace_bytes.restype = sz
     L.mla_test_gemm.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32, vp, sz, vp]
     L.mla_test_gemm.restype = ctypes.c_int
+    L.mla_test_gemm_fp8_workspace_bytes.argtypes = [i32, i32, i32]
+    L.mla_test_gemm_fp8_workspace_bytes.restype = sz
+    L.mla_test_gemm_fp8.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.mla_test_gemm_fp8.restype = ctypes.c_int
     L.mla_test_probe_stage.argtypes = [i32, vp, vp]
     L.mla_test_probe_stage.restype = ctypes.c_int
     L.mla_page_pool_create.argtypes = [i32, ctypes.POINTER(vp)]
@@ -543,4 +547,18 @@ class Gemm:
         check(lib().mla_test_gemm(M, N, K, batch, _ptr(A), lda or K, sA, _ptr(B), ldb or K, sB, _ptr(C),
                                   ldc or N, sC, out_bf16, STAGE[stage], _ptr(self._ws), self._ws.numel(),
                                   _stream(stream)))
+        return C
+
+    def fp8(self, A, a_scale, B, b_scale, C, M, N, K, precise: bool, stream=None):
+        """mla_test_gemm_fp8: C [M, N] float32 = dequant(A) dequant(B)^T from E4M3FN codes (uint8
+        tensors [M, K], [N, K]) and float32 scales [M, K/128], [ceil(N/128), K/128]."""
+        import torch
+
+        need = lib().mla_test_gemm_fp8_workspace_bytes(M, N, K)
+        if need == 0:
+            raise MlaError(1, "invalid GEMM shape")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=A.device)
+        check(lib().mla_test_gemm_fp8(M, N, K, _ptr(A), _ptr(a_scale), _ptr(B), _ptr(b_scale), _ptr(C),
+                                      1 if precise else 0, _ptr(self._ws), self._ws.numel(), _stream(stream)))
         return C

@@ -1041,4 +1041,30 @@ mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const v
   return MLA_OK;
 }
 
+size_t mla_test_gemm_fp8_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+  return std::max<size_t>(256, (size_t)mla_k::gemm_fp8_part_floats(M, N, K, 1) * 4);
+}
+
+mla_status mla_test_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const float* a_scale, const void* B,
+                             const float* b_scale, float* C, int32_t precise, void* ws, size_t ws_bytes,
+                             mla_stream stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(MLA_E_ARG, "non-positive GEMM size");
+  if (K % 128 || N % 8) return fail(MLA_E_UNSUPPORTED, "K must be a multiple of 128 and N of 8");
+  if (!A || !a_scale || !B || !b_scale || !C || !ws) return fail(MLA_E_ARG, "a pointer argument is NULL");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(ws))
+    return fail(MLA_E_ALIGN, "operands must start on 16-byte boundaries");
+  const size_t need = mla_test_gemm_fp8_workspace_bytes(M, N, K);
+  if (ws_bytes < need) return fail(MLA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  mla_k::GemmArgs g;
+  g.tag = precise ? mla_k::TAG_QKVA : mla_k::TAG_OPROJ;  // the tag selects the form
+  g.A = A; g.lda = K; g.B = B; g.ldb = K; g.C = C; g.ldc = N;
+  g.a_scale = a_scale; g.as_ld = K / 128; g.b_scale = b_scale; g.bs_ld = K / 128;
+  g.M = M; g.N = N; g.K = K; g.batch = 1; g.epi = mla_k::EPI_F32;
+  g.part = (float*)ws;
+  g.part_cap = mla_k::gemm_fp8_part_floats(M, N, K, 1);
+  HIP_TRY(mla_k::gemm_fp8(g, (hipStream_t)stream));
+  return MLA_OK;
+}
+
 }  // extern "C"

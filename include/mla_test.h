@@ -42,6 +42,22 @@ mla_status mla_test_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const v
                          const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC, int32_t out_bf16,
                          int32_t stage, void* ws, size_t ws_bytes, mla_stream stream);
 
+/* Workspace bytes mla_test_gemm_fp8 needs for this shape (split-K partials). */
+size_t mla_test_gemm_fp8_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/* The FP8 projection kernel on its own ("Key-value latent" page, linear excerpt: E4M3 weights with
+ * one scale per 128 x 128 block, activations quantised per token and 128 features):
+ * C[m][n] = sum_k (a[m][k] * a_scale[m][k/128]) * (b[n][k] * b_scale[n/128][k/128]).
+ * A [M, K] and B [N, K] are device E4M3FN codes, rows K bytes apart; a_scale [M][K/128] and
+ * b_scale [ceil(N/128)][K/128] device float32, rows K/128 apart; C [M, N] device float32, rows N
+ * apart. precise = 1: the form of q_a|kv_a and kv_b (codes widened exactly to bf16, each 128-wide
+ * group summed by bf16 MFMAs into float32); precise = 0: the form of q_b and o_proj (one FP8 MFMA
+ * per group with unit hardware scales). K must be a multiple of 128, N of 8. ws: device workspace of
+ * ws_bytes >= mla_test_gemm_fp8_workspace_bytes() (scratch only). */
+mla_status mla_test_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const float* a_scale, const void* B,
+                             const float* b_scale, float* C, int32_t precise, void* ws, size_t ws_bytes,
+                             mla_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
