@@ -199,6 +199,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
   constexpr int AP = BM / RPP, BP = BN / RPP;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of rows per pass");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * LDK];
+  __shared__ __attribute__((aligned(16))) float sSa[2][BM];  // A scales of the stage's K group, per row
+  static_assert((BM & (BM - 1)) == 0 && NT >= BM, "one A scale per thread");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,9 +231,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 #pragma unroll
   for (int i = 0; i < BP; ++i) gb[i] = B + (int64_t)min(n0 + i * RPP + lr, p.N - 1) * p.ldb + lc;
 
-  // scale rows of this lane's results: m = mrow0 + i*16 + e (clamped), column block of tile j
-  const int mrow0 = m0 + wm * WTM + g * 4;
-  const int ncol0 = n0 + wn * WTN;
+  // A scales staged with the tiles (row tid % BM of the tile, every thread loads one: the same loads
+  // in every wave); a wave's columns lie in one 128-column weight block (WTN divides 128), whose
+  // scale is read once per K group
+  static_assert(128 % WTN == 0, "a wave's columns span one weight scale block");
+  const float* gsa = p.a_scale + (int64_t)min(m0 + (tid & (BM - 1)), p.M - 1) * p.as_ld;
+  const float* gsb = p.b_scale + (int64_t)(min(n0 + wn * WTN, p.N - 1) >> 7) * p.bs_ld;
+  float rsa;
 
   u32x4_t ra[AP], rb[BP];
   f32x4_t acc[TM][TN];
@@ -249,6 +255,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     for (int i = 0; i < AP; ++i) ra[i] = ld16(ga[i] + k0);
 #pragma unroll
     for (int i = 0; i < BP; ++i) rb[i] = ld16(gb[i] + k0);
+    rsa = gsa[k0 >> 7];
   };
   auto sstore = [&](int buf) {
     uint8_t* sa = smem + buf * (BM + BN) * LDK;
@@ -257,6 +264,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lc, ra[i]);
 #pragma unroll
     for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lc, rb[i]);
+    if (tid < BM) sSa[buf][tid] = rsa;
   };
 
   if (nk > 0) {
@@ -268,13 +276,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     const int cur = kt & 1;
     const int kg = (kb >> 7) + kt;
     if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
-    float sa[TM][4], sbv[TN];
+    // combined scale of this lane's result rows m = m0 + wm*WTM + i*16 + g*4 + e for this K group
+    f32x4_t sab[TM];
+    {
+      const float sbk = gsb[kg];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sa[i][e] = p.a_scale[(int64_t)min(mrow0 + i * 16 + e, p.M - 1) * p.as_ld + kg];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sbv[j] = p.b_scale[(int64_t)(min(ncol0 + j * 16, p.N - 1) >> 7) * p.bs_ld + kg];
+      for (int i = 0; i < TM; ++i) sab[i] = *reinterpret_cast<const f32x4_t*>(&sSa[cur][wm * WTM + i * 16 + g * 4]) * sbk;
+    }
     const uint8_t* sA = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK + g * 32;
     const uint8_t* sB = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK + g * 32;
     if constexpr (PREC) {
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * (sa[i][e] * sbv[j]);
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sab[i][e];
     } else {
       i32x8_t bfr[TN];
 #pragma unroll
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
         for (int j = 0; j < TN; ++j) {
           const f32x4_t d = mfma_fp8_16x16x128(af, bfr[j]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[e] * (sa[i][e] * sbv[j]);
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[e] * sab[i][e];
         }
       }
     }
