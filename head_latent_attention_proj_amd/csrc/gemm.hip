@@ -561,11 +561,12 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, Norm
 }
 
 // ------------------------------------------------------------------------------------------
-// Per-head products at M <= 64 with short K (decode W_UK absorb and W_UV)
+// Per-head products at M <= 256 with short K (decode W_UK absorb and W_UV)
 // ------------------------------------------------------------------------------------------
-// Workgroup = (head, 16 NWV output columns); x_h (M x K, K = 32 KS) is staged in LDS once and
-// every wave streams 16 weight rows over the whole K with all of its loads issued up front;
-// 16x16x32 MFMA, A fragments from LDS (rows >= M are copies of row M - 1 and never stored).
+// Workgroup = (head, 16 NWV output columns, 64-row chunk of x); the chunk x_h[m0 .. m0+63] (K =
+// 32 KS) is staged in LDS once and every wave streams 16 weight rows over the whole K with all of
+// its loads issued up front; 16x16x32 MFMA, A fragments from LDS (rows >= M are copies of row
+// M - 1 and never stored).
 template <int KS, int NWV, int TAG>
 __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
   constexpr int LDX = KS * 32 + 8;  // padded LDS row: consecutive rows in distinct 16-byte bank groups
@@ -575,7 +576,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.y * (16 * NWV) + wave * 16;
-  const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
+  const int m0 = blockIdx.z * 64;
+  const uint16_t* A = (const uint16_t*)p.A + batch * p.sA + (int64_t)m0 * p.lda;
+  const int mrows = min(64, p.M - m0);
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
   u32x4_t wb[KS];
   const uint16_t* wr = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + 8 * g;
@@ -589,7 +592,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + NT * i, row = c / CH, ch = c % CH;
-      xv[i] = ld16(A + (int64_t)min(row, p.M - 1) * p.lda + ch * 8);
+      xv[i] = ld16(A + (int64_t)min(row, mrows - 1) * p.lda + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = 16 * i + 4 * g + e, n = n0 + l16;
-      if (m < p.M && n < p.N) epi_store(p, batch, m, n, acc[i][e]);
+      if (m < mrows && n < p.N) epi_store(p, batch, m0 + m, n, acc[i][e]);
     }
 }
 
@@ -793,11 +796,11 @@ Plan plan_gemm(int M, int N, int K, int batch, int ysplit_max = 1, bool rows_ok 
     pl.ksplit = K;
     pl.ysplit = 1;
   }
-  // Per-head products, M <= 64, K of 128 or 512: x staged once per (head, 128 columns).
+  // Per-head products, M <= 256, K of 128 or 512: x staged once per (head, 128 columns, 64 rows).
   // Measured on MI355X at M = 64: W_UK absorb and W_UV run in a fraction of the streaming
   // kernel's time, whose 16-column tiles re-read x for every tile; at M = 1 (decode of one
   // sequence) the absorb's 256 workgroups of 8 waves beat 2048 single-wave ones by ~1 us.
-  if (M <= 64 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
+  if (M <= 256 && batch > 1 && (K == 128 || K == 512) && N % 128 == 0) {
     pl.kind = 4;
     pl.nw = K == 512 ? 4 : 8;  // W_UV (one 128-column tile per head): two workgroups per head, ~1 us faster at M = 64
     pl.tiles = N / (16 * pl.nw);
@@ -910,7 +913,7 @@ void launch_rows(const GemmArgs& a, const Plan& pl, dim3 grid, size_t lds, hipSt
 template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   if (pl.kind == 4) {
-    dim3 grid(a.batch, pl.tiles);
+    dim3 grid(a.batch, pl.tiles, cdiv(a.M, 64));
     if (pl.nw == 8) {
       if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 8, TAG>), grid, dim3(512), 0, s, a);
       else hipLaunchKernelGGL((gemm_head_kernel<16, 8, TAG>), grid, dim3(512), 0, s, a);

@@ -69,9 +69,10 @@ def test_gemm_bf16_output_matches_float64(M, N, K):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(K))
 
 
-@pytest.mark.parametrize("Bt", [1, 2, 5, 33, 64])
+@pytest.mark.parametrize("Bt", [1, 2, 5, 33, 64, 100, 256])
 def test_gemm_bf16_output_and_batched_strides(Bt):
-    """Per-head batched product with row/batch strides (the decode absorption layout)."""
+    """Per-head batched product with row/batch strides (the decode absorption layout); above 64
+    rows the per-head kernel runs in 64-row chunks (100: a ragged last chunk)."""
     import torch
 
     log(f"batched gemm Bt={Bt}")
@@ -90,7 +91,7 @@ def test_gemm_bf16_output_and_batched_strides(Bt):
     assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-6
 
 
-@pytest.mark.parametrize("Bt", [1, 2, 20, 64])
+@pytest.mark.parametrize("Bt", [1, 2, 20, 64, 200, 256])
 def test_gemm_value_mix_layout(Bt):
     """Per-head W_UV product: o[b][h*128 + d] = sum_c o_lat[b][h][c] W_UV,h[d][c] (K = 512)."""
     import torch
