@@ -524,15 +524,17 @@ Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
   const bool narrow = M <= 256;
   pl.kind = big ? 2 : (narrow ? 3 : 1);
   pl.tiles = cdiv(M, 128) * cdiv(N, big ? 256 : (narrow ? 64 : 128));
+  // K splits: as many as still fit one round of workgroups (two 128 x 64 or 128 x 128 tile
+  // workgroups per CU: 512), and float32 partials (written and read back) adding at most the
+  // operand bytes (codes) in traffic. Measured at 128 rows (decode of 128 sequences), forced split
+  // counts 1 .. 16: o_proj best at 4 (38 us; 5 splits = 560 workgroups, a second round: 54 us),
+  // q_b unsplit (19 us; 3 splits 27), q_a|kv_a 6-7 (19-20 us).
   int splits = 1;
   const int wgs = pl.tiles * batch;
-  if (wgs < 256) splits = cdiv(512, wgs);
-  // float32 split-K partials are written and read back: the splits may add at most twice the
-  // operand bytes (codes) in partial traffic. Measured at 128 rows (decode of 128 sequences):
-  // q_a|kv_a 7 splits, o_proj 5, q_b 3 (q_b unsplit, 12 serial K stages per workgroup, took 42 us).
+  if (wgs < 256) splits = std::max(1, 512 / wgs);
   const int64_t operand_bytes = (int64_t)batch * ((int64_t)M * K + (int64_t)N * K);
   const int64_t part_bytes_per_split = 8 * (int64_t)batch * M * N;
-  splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, 2 * operand_bytes / part_bytes_per_split));
+  splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, operand_bytes / part_bytes_per_split));
   splits = std::max(1, std::min(splits, ngroups));
   const int per = cdiv(ngroups, splits);
   pl.ksplit = per * 128;
