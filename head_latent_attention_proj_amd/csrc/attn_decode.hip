@@ -107,7 +107,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
 
   __shared__ __attribute__((aligned(16))) uint16_t sC[DKB * LDC];      // fp16 [position][576], swizzled
   __shared__ __attribute__((aligned(16))) float xS[8][64][12];         // partial scores [wave][lane][8 + pad]
-  __shared__ __attribute__((aligned(16))) float sScale[4][DKB];        // group scales [group][position]
+  __shared__ __attribute__((aligned(16))) float sScale[4][DKB];        // group scales x P_PRESCALE [group][position]
 
   // ---- staging through registers, FP8_AHEAD blocks ahead (one register set per block in flight):
   // codes as position pairs (pair kp = tid & 15, 16-code chunk cc = tid >> 4), the rotary key (every
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
     }
     if (tid >= 256 && tid < 256 + DKB) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[S][q]);
+      for (int q = 0; q < 4; ++q) sScale[q][tid - 256] = __uint_as_float(rs[S][q]) * P_PRESCALE;
     }
     // rotary key: 4 float32 features -> fp16
     const int pos = tid >> 4, f4 = (tid & 15) * 4;
@@ -197,7 +197,9 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
     }
   }
 
-  const float sl2 = a.scale * LOG2E;
+  // scores are formed with the group scales times P_PRESCALE (the rotary part times it too): the
+  // power of two comes out exactly in the exponent's scale
+  const float sl2 = a.scale * LOG2E * (1.0f / P_PRESCALE);
   float mrun = -INFINITY, lrun = 0.f;
   f32x4_t oacc[16];
 #pragma unroll
@@ -254,8 +256,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
               sacc[0] += t0 * sc0[grp - G0];
               sacc[1] += t1 * sc1[grp - G0];
             } else {
-              sacc[0] += t0;
-              sacc[1] += t1;
+              sacc[0] += t0 * P_PRESCALE;
+              sacc[1] += t1 * P_PRESCALE;
             }
             t0 = t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
@@ -279,16 +281,19 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[kt][e] = lh == 0 ? sacc[kt][e] + theirs[e] : theirs[e] + sacc[kt][e];
     }
-    float bmax = -INFINITY;
+    // positions past the split's end occur in its last block only (wave-uniform test)
+    if (kb + DKB > c1) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kb + kt * 16 + g * 4 + e >= c1) sv[kt][e] = -INFINITY;
+    }
+    float bmax = -INFINITY;  // unscaled scores: the scale is applied in the exponent's fma
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float sc = sv[kt][e];  // unscaled: the scale is applied in the exponent's fma
-        if (kb + kt * 16 + g * 4 + e >= c1) sc = -INFINITY;
-        sv[kt][e] = sc;
-        bmax = fmaxf(bmax, sc);
-      }
+      for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sv[kt][e]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     bmax *= sl2;  // the scale (positive) commutes with the maximum
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
       for (int kt = 0; kt < 2; ++kt) {
         const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sScale[2 * lh + q][kt * 16 + g * 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_[kt][e] = sv[kt][e] * (sc[e] * P_PRESCALE);
+        for (int e = 0; e < 4; ++e) s_[kt][e] = sv[kt][e] * sc[e];
       }
       u32x4_t w, r;
       w[0] = pack_f16x2(s_[0][0], s_[0][1]);
