@@ -318,20 +318,41 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     l += __shfl_xor(l, 32);
     const float inv = 1.0f / l;
     const int qrel = q0 + wave * 32 + qt * 16 + l16;
+    if (SPLIT && a.o_codes) {
+      // the o_proj input quantiser ("Key-value latent" page, linear excerpt: dynamic activations,
+      // one scale per token and 128 features = this head's 128 values of the token): s = amax/448
+      // (1 for an all-zero group), code = RNE-saturating E4M3 of v/s, in float32. The token's 128
+      // values sit in the four lanes l16 + 16g; all lanes take part in the exchange.
+      float v[8][4], amax = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[d][e] = oacc[d][qt][e] * inv;
+          amax = fmaxf(amax, fabsf(v[d][e]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if (qrel >= m.t) continue;
+      const int64_t row = m.q0 + qrel;
+      const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= e4m3_rne_sat(v[d][e] / sc) << (8 * e);
+        *reinterpret_cast<uint32_t*>(a.o_codes + row * 8192 + h * 128 + d * 16 + g * 4) = w;
+      }
+      if (g == 0) a.o_scales[row * 64 + h] = sc;
+      continue;
+    }
     if (qrel >= m.t) continue;
     const int64_t row = m.q0 + qrel;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int col = h * 128 + d * 16 + g * 4;
-      if (a.o_f32) {
-        float* dst = a.o_f32 + row * 8192 + col;
-        *reinterpret_cast<f32x4_t*>(dst) = oacc[d][qt] * inv;
-      } else {
-        st8(a.o + row * 8192 + col,
-            u32x2_t{pack_bf16x2(oacc[d][qt][0] * inv, oacc[d][qt][1] * inv),
-                    pack_bf16x2(oacc[d][qt][2] * inv, oacc[d][qt][3] * inv)});
-      }
-    }
+    for (int d = 0; d < 8; ++d)
+      st8(a.o + row * 8192 + h * 128 + d * 16 + g * 4,
+          u32x2_t{pack_bf16x2(oacc[d][qt][0] * inv, oacc[d][qt][1] * inv),
+                  pack_bf16x2(oacc[d][qt][2] * inv, oacc[d][qt][3] * inv)});
   }
 }
 

@@ -72,6 +72,21 @@ MLA_DEV f32x4_t mfma_f16_16x16x32(const f16x8_t& a, const f16x8_t& b, const f32x
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// OCP E4M3FN encode of a float32, round to nearest even, saturating at +-448.
+MLA_DEV uint32_t e4m3_rne_sat(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  if (!(a < 448.f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (m = 8 is the smallest normal)
+    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.f);
+    return sign | m;
+  }
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+  const uint32_t e = (r >> 3) - 127u + 7u;
+  return sign | (e << 3) | (r & 7u);
+}
+
 MLA_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 MLA_DEV void st16(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 

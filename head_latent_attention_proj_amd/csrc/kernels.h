@@ -153,8 +153,11 @@ struct PrefillAttnArgs {
   int B;
   int max_t;               // largest T_b (grid sizing)
   float scale;             // softmax scale
-  uint16_t* o;             // [n_tok][8192] bf16 (when o_f32 is null)
-  float* o_f32;            // optional fp32 output [n_tok][8192]
+  uint16_t* o;             // [n_tok][8192] bf16 (when o_codes is null)
+  // optional FP8 output, the o_proj input quantised in the epilogue (one 1 x 128 group = one
+  // head of one token): E4M3FN codes [n_tok][8192] and float32 scales [n_tok][64]
+  uint8_t* o_codes;
+  float* o_scales;
 };
 hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 

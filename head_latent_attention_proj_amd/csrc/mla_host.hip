@@ -278,7 +278,7 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   L.x8 = take(fp8 ? (size_t)ntok * HIDDEN : 0);
   L.x8s = take(fp8 ? (size_t)ntok * (HIDDEN / 128) * 4 : 0);
   L.qh8s = take(fp8 ? (size_t)ntok * (Q_LORA / 128) * 4 : 0);
-  L.o32 = take(fp8 ? (size_t)ntok * O_IN * 4 * (decode_splits > 0 ? 2 : 1) : 0);  // decode: 2 planes
+  L.o32 = take(fp8 && decode_splits > 0 ? (size_t)ntok * O_IN * 4 * 2 : 0);  // decode: W_UV's two planes
   L.o_lat = take(decode_splits > 0 ? (size_t)nbatch * HEADS * KV_LORA * 2 * (fp8 ? 2 : 1) : 0);
   L.o8 = take(fp8 ? (size_t)ntok * O_IN : 0);
   L.o8s = take(fp8 ? (size_t)ntok * (O_IN / 128) * 4 : 0);
@@ -689,20 +689,21 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
     }
     HIP_TRY(run_proj(ctx, g, s));
   }
-  // 5. causal attention (FP8: fp16 operands with value residuals, float32 output -- the o_proj
-  //    quantiser's input)
+  // 5. causal attention (FP8: fp16 operands with value residuals; the epilogue applies the o_proj
+  //    input quantiser and writes codes and scales)
   mla_k::PrefillAttnArgs pa{};
   pa.q = w + L.q; pa.knope = (const uint16_t*)(w + L.knope); pa.vt = (const uint16_t*)(w + L.vt);
   pa.split = fp8; pa.vt_lo = (const uint16_t*)(w + L.vt_lo);
   pa.vt_ld = L.vt_ld; pa.cache = kv_rows; pa.entry_bytes = eb;
   pa.kpe_off = fp8 ? KV_LORA + 16 : KV_LORA * 2;
   pa.rope_cs = ctx->rope_cs; pa.max_pos = ctx->cfg.max_positions; pa.meta = meta; pa.B = B; pa.max_t = max_t;
-  pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o); pa.o_f32 = fp8 ? (float*)(w + L.o32) : nullptr;
+  pa.scale = ctx->scale; pa.o = (uint16_t*)(w + L.o);
+  if (fp8) {  // the attention epilogue writes o_proj's quantised input
+    pa.o_codes = w + L.o8;
+    pa.o_scales = (float*)(w + L.o8s);
+  }
   PROBED(MLA_STAGE_PREFILL_ATTN, mla_k::prefill_attention(pa, s));
   // 6. o_proj
-  if (fp8)
-    HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), nullptr, O_IN, ntok, O_IN, w + L.o8,
-                                     (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
   set_a(ctx, g, w + L.o, O_IN, w + L.o8, (const float*)(w + L.o8s), O_IN / 128);
   g.B = ctx->w_o; g.ldb = O_IN; g.b_scale = ctx->s_o; g.bs_ld = O_IN / 128;

@@ -20,21 +20,6 @@ namespace mla_k {
 
 namespace {
 
-// OCP E4M3FN encode of a float32, round to nearest even, saturating at +-448.
-MLA_DEV uint32_t e4m3_rne_sat(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fabsf(q);
-  if (!(a < 448.f)) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (m = 8 is the smallest normal)
-    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.f);
-    return sign | m;
-  }
-  const uint32_t ua = __float_as_uint(a);
-  const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
-  const uint32_t e = (r >> 3) - 127u + 7u;
-  return sign | (e << 3) | (r & 7u);
-}
-
 __global__ void plan_kernel(const int32_t* seq_ids, const int32_t* q_start, SlotMap map, const int32_t* len, int B,
                             SeqMeta* meta) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
