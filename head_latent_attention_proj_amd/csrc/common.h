@@ -87,6 +87,29 @@ MLA_DEV uint32_t e4m3_rne_sat(float q) {
   return sign | (e << 3) | (r & 7u);
 }
 
+// Direct-to-LDS loads: every lane of the wave reads `size` bytes at its own global address and
+// they land at l + size * lane (l wave-uniform).
+MLA_DEV void gl2lds16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+MLA_DEV void gl2lds4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt and lgkmcnt at their maxima).
+template <int N>
+MLA_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS byte address of a __shared__ pointer.
+MLA_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+
 MLA_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 MLA_DEV void st16(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 

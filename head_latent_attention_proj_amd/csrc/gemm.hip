@@ -628,22 +628,6 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 // row l16, features 8g .. 8g+7: the block in LDS is already the MFMA operand image, and every
 // lane reads its operand back at 16*l (contiguous, conflict-free). The loads hold no registers,
 // so S-1 stages are in flight while one is multiplied, and one barrier per stage suffices.
-MLA_DEV void gl2lds16(const void* g, uint16_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt and lgkmcnt at their maxima).
-template <int N>
-MLA_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// LDS byte address of a __shared__ pointer.
-MLA_DEV uint32_t lds_addr(const uint16_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-}
 
 // One stage's operands of a wave: A blocks 0 .. 2*MT-1 at a + 1024*b, the wave's two weight blocks
 // at w and w + 1024 (byte addresses, this lane's 16 bytes). Written as one asm block that waits

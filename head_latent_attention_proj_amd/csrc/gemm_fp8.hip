@@ -475,6 +475,226 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
       }
 }
 
+// ------------------------------------------------------------------------------------------
+// Prefill-sized M, native form: K groups streamed through a ring of LDS stages
+// ------------------------------------------------------------------------------------------
+// 128 x 256 output tile, 8 waves of 64 x 64 (2 x 4). A stage is one K group: the A tile as 8 and
+// the B tile as 16 blocks of 16 rows x 128 codes, and the tile's 128 A scales. Every piece is
+// fetched by direct-to-LDS loads, which hold no registers: two stages are in flight while the
+// third is multiplied (the register-staged tile kernel has one stage of compute to cover each
+// load). One wave instruction fetches 8 whole rows of a block (lane l: row l / 8, one 16-byte
+// chunk), so it touches 8 cache lines; a block lands row-major, chunk c of row r at position
+// c ^ ((r / 2) % 8): a lane's operand halves (row l16, chunks 2g and 2g + 1) are then read with
+// the 16 lanes of one g on distinct banks. The row scales are fetched by one wave per 64 rows.
+// Three stages of 48.5 KB: one workgroup per CU.
+namespace ring8 {
+constexpr int BM = 128, BN = 256, S = 3;
+constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+constexpr int SC_BYTES = BM * 4;
+constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;  // 49,664 bytes
+constexpr int LDW = 64 + 4;                          // float32 epilogue staging row (a wave's 64 columns)
+}  // namespace ring8
+
+// One stage's operands of a wave (byte addresses of this lane's 16 bytes): A blocks at a0 / a1
+// (chunk halves 0 / 1) + 2048 i, B blocks at b0 / b1 + 2048 j, the row scales (4 floats) at
+// c + 64 i, and the stage's weight-block scale (a scalar load from sb). One asm block that waits
+// for its own reads: the compiler cannot tell that they never touch the slots the direct-to-LDS
+// loads are still filling and would wait for every load in flight (it also turns a plain load of
+// the weight scale into a vector load, counted with the ring's). Early-clobber outputs, so no
+// read's destination is an address of a later read.
+MLA_DEV void ring8_operands(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uint32_t c, const float* sb,
+                            u32x4_t (&ra)[8], u32x4_t (&rb)[8], f32x4_t (&sc)[4], float& sbk) {
+  asm volatile(
+      "s_load_dword %20, %26, 0x0\n\t"
+      "ds_read_b128 %0, %21\n\tds_read_b128 %1, %22\n\t"
+      "ds_read_b128 %2, %21 offset:2048\n\tds_read_b128 %3, %22 offset:2048\n\t"
+      "ds_read_b128 %4, %21 offset:4096\n\tds_read_b128 %5, %22 offset:4096\n\t"
+      "ds_read_b128 %6, %21 offset:6144\n\tds_read_b128 %7, %22 offset:6144\n\t"
+      "ds_read_b128 %8, %23\n\tds_read_b128 %9, %24\n\t"
+      "ds_read_b128 %10, %23 offset:2048\n\tds_read_b128 %11, %24 offset:2048\n\t"
+      "ds_read_b128 %12, %23 offset:4096\n\tds_read_b128 %13, %24 offset:4096\n\t"
+      "ds_read_b128 %14, %23 offset:6144\n\tds_read_b128 %15, %24 offset:6144\n\t"
+      "ds_read_b128 %16, %25\n\tds_read_b128 %17, %25 offset:64\n\t"
+      "ds_read_b128 %18, %25 offset:128\n\tds_read_b128 %19, %25 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(ra[4]), "=&v"(ra[5]), "=&v"(ra[6]), "=&v"(ra[7]),
+        "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3]), "=&v"(rb[4]), "=&v"(rb[5]), "=&v"(rb[6]), "=&v"(rb[7]),
+        "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3]), "=&s"(sbk)
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(c), "s"(sb)
+      : "memory");
+}
+
+// Requirements (checked by ring8_ok): K a multiple of 128, 16-byte aligned operand rows, epilogue
+// EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), and for
+// a residual 16-byte alignment and ldr a multiple of 8.
+template <int TAG>
+__global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
+  using namespace ring8;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // tile order of the tile kernel: XCD-aware, then groups of 8 row tiles
+  const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
+  const int ntile = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((ntile & 7) == 0) bid = (bid & 7) * (ntile >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int fm = (bid / per_group) * GM;
+  const int gs = min(tiles_m - fm, GM);
+  const int m0 = (fm + (bid % per_group) % gs) * BM;
+  const int n0 = ((bid % per_group) / gs) * BN;
+  const int batch = blockIdx.z;
+  const uint8_t* A = (const uint8_t*)p.A + batch * p.sA;
+  const uint8_t* B = (const uint8_t*)p.B + batch * p.sB;
+  const int nk = p.K >> 7;
+
+  // this wave's loads: A block `wave`, B blocks 2 wave and 2 wave + 1, two instructions of 8 rows
+  // each (rows past M and N re-read the last one); lane l reads row 8 q + l / 8 of instruction q,
+  // the chunk that belongs at position l % 8 of that row
+  const int lr = lane >> 3;
+  auto src = [&](const uint8_t* base, int64_t ld, int r0, int lim, int q) {
+    const int r = q * 8 + lr;
+    return base + (int64_t)min(r0 + r, lim - 1) * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  };
+  const uint8_t* ga0 = src(A, p.lda, m0 + wave * 16, p.M, 0);
+  const uint8_t* ga1 = src(A, p.lda, m0 + wave * 16, p.M, 1);
+  const uint8_t* gb0 = src(B, p.ldb, n0 + wave * 32, p.N, 0);
+  const uint8_t* gb1 = src(B, p.ldb, n0 + wave * 32, p.N, 1);
+  const uint8_t* gb2 = src(B, p.ldb, n0 + wave * 32 + 16, p.N, 0);
+  const uint8_t* gb3 = src(B, p.ldb, n0 + wave * 32 + 16, p.N, 1);
+  // the row scales: waves 0 and 4 fetch rows wm * 64 + lane
+  const bool scw = wn == 0;
+  const float* gsa = p.a_scale + (int64_t)min(m0 + wm * 64 + lane, p.M - 1) * p.as_ld;
+  auto issue = [&](int kt, int slot) {
+    uint8_t* st = ring + slot * STAGE;
+    const int64_t k0 = (int64_t)kt * 128;
+    gl2lds16(ga0 + k0, st + wave * 2048);
+    gl2lds16(ga1 + k0, st + wave * 2048 + 1024);
+    gl2lds16(gb0 + k0, st + A_BYTES + wave * 4096);
+    gl2lds16(gb1 + k0, st + A_BYTES + wave * 4096 + 1024);
+    gl2lds16(gb2 + k0, st + A_BYTES + wave * 4096 + 2048);
+    gl2lds16(gb3 + k0, st + A_BYTES + wave * 4096 + 3072);
+    if (scw) gl2lds4(gsa + kt, st + A_BYTES + B_BYTES + wm * 256);
+  };
+
+  // the wave's weight scales: its 64 columns lie in one 128-column block
+  const float* gsb = p.b_scale + (int64_t)(min(n0 + wn * 64, p.N - 1) >> 7) * p.bs_ld;
+  // operand addresses within a stage: row l16 of a block, chunk halves 2g and 2g + 1
+  const int swz = (l16 >> 1) & 7;
+  const uint32_t oa0 = wm * 8192 + l16 * 128 + (((2 * g) ^ swz) << 4);
+  const uint32_t oa1 = wm * 8192 + l16 * 128 + (((2 * g + 1) ^ swz) << 4);
+  const uint32_t ob0 = A_BYTES + wn * 8192 + l16 * 128 + (((2 * g) ^ swz) << 4);
+  const uint32_t ob1 = A_BYTES + wn * 8192 + l16 * 128 + (((2 * g + 1) ^ swz) << 4);
+  const uint32_t osc = A_BYTES + B_BYTES + wm * 256 + g * 16;
+
+  // acc: the scaled sum of the groups before the previous one; d, sp: the previous group's sums
+  // and combined scales, added while this group's products run (a wave's scaling work then
+  // overlaps its own MFMAs instead of following them; the order of the additions is unchanged)
+  f32x4_t acc[4][4], d[4][4], sp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sp[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = d[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(min(t, nk - 1), t);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's part of stage t has landed (one stage, 6 or 7 loads, may stay in flight) ...
+    if (scw)
+      wait_vmcnt<(S - 2) * 7>();
+    else
+      wait_vmcnt<(S - 2) * 6>();
+    // ... and every wave's; all are done with stage t - 1, whose slot is refilled next. A plain
+    // barrier: __syncthreads' release fence would wait for every load in flight.
+    asm volatile("s_barrier" ::: "memory");
+    // past the last stage the same loads re-fetch it into a consumed slot, so every trip issues
+    // the same loads and the wait counts stay exact
+    issue(min(t + S - 1, nk - 1), (t + S - 1) % S);
+    const uint32_t st = lds_addr(ring + (t % S) * STAGE);
+    u32x4_t ra[8], rb[8];
+    f32x4_t sc[4];
+    float sbk;
+    ring8_operands(st + oa0, st + oa1, st + ob0, st + ob1, st + osc, gsb + t, ra, rb, sc, sbk);
+    i32x8_t bfr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = cat8(rb[2 * j], rb[2 * j + 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8_t af = cat8(ra[2 * i], ra[2 * i + 1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sp[i][e];
+        d[i][j] = mfma_fp8_16x16x128(af, bfr[j]);
+      }
+      sp[i] = sc[i] * sbk;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sp[i][e];
+  wait_vmcnt<0>();  // the tail's re-fetches have landed
+  __syncthreads();  // every wave is done with the ring: it becomes the output staging
+  static_assert(8 * 64 * LDW * 4 <= S * STAGE, "epilogue staging fits the ring");
+
+  // float32 results through LDS (a private region per wave), then whole 16-byte pieces of output
+  // rows: bf16 rounds acc (+ residual) once, as the per-element epilogue does
+  float* sw = reinterpret_cast<float*>(ring) + wave * (64 * LDW);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = acc[i][j][e];
+  __syncthreads();
+  const int mw = m0 + wm * 64, nw = n0 + wn * 64;
+  if (p.epi == EPI_BF16) {
+    const int lr = lane >> 3, lc = (lane & 7) * 8;
+    const int n = nw + lc;
+    if (n < p.N) {
+      uint16_t* cb = (uint16_t*)p.C + batch * p.sC + n;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = k * 8 + lr, m = mw + r;
+        if (m >= p.M) continue;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc + 4);
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if (p.resid) {
+          const u32x4_t rr = ld16(p.resid + (int64_t)m * p.ldr + n);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] += bf_lo(rr[q]);
+            v[2 * q + 1] += bf_hi(rr[q]);
+          }
+        }
+        st16(cb + (int64_t)m * p.ldc, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
+      }
+    }
+  } else {
+    const int lr = lane >> 4, lc = (lane & 15) * 4;
+    const int n = nw + lc;
+    if (n < p.N) {
+      float* cf = (float*)p.C + batch * p.sC + n;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int r = k * 4 + lr, m = mw + r;
+        if (m < p.M) *reinterpret_cast<f32x4_t*>(cf + (int64_t)m * p.ldc) = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc);
+      }
+    }
+  }
+}
+
 template <int TAG>
 __global__ __launch_bounds__(256) void splitk_reduce8_kernel(GemmArgs p, int splits) {
   const int64_t mn = (int64_t)p.M * p.N;
@@ -557,6 +777,17 @@ void launch_fp8_wsplit(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
   }
 }
 
+// The ring kernel's layout and epilogue requirements
+bool ring8_ok(const GemmArgs& a) {
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (a.K < 128 || (a.lda & 15) || (a.ldb & 15) || (a.sA & 15) || (a.sB & 15) || !al16(a.A) ||
+      !al16(a.B) || !al16(a.C))
+    return false;
+  if (a.epi == EPI_BF16)
+    return (a.N & 7) == 0 && (a.ldc & 7) == 0 && (a.sC & 7) == 0 && (!a.resid || (al16(a.resid) && (a.ldr & 7) == 0));
+  return a.epi == EPI_F32 && (a.N & 3) == 0 && (a.ldc & 3) == 0 && (a.sC & 3) == 0;
+}
+
 template <int TAG, bool PREC>
 void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
   if (pl.kind == 0) {
@@ -566,6 +797,12 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
     return;
   }
   dim3 grid(pl.tiles, pl.splits, a.batch);
+  if constexpr (!PREC) {
+    if (pl.kind == 2 && pl.splits == 1 && ring8_ok(a)) {
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG>), grid, dim3(512), 0, s, a);
+      return;
+    }
+  }
   if (pl.kind == 1)
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 128, 2, 2, TAG, PREC>), grid, dim3(256), 0, s, a, pl.splits,
                        pl.ksplit);

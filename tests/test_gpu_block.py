@@ -109,6 +109,34 @@ def test_block_fp8_prefill_then_decode():
     L.close()
 
 
+def test_block_fp8_prefill_1100_tokens_sampled_rows():
+    """A prefill long enough for the prefill-sized FP8 o_proj, whose epilogue adds the residual
+    before the bf16 rounding (in place: h overwrites x)."""
+    import torch
+
+    T = 1100
+    log(f"block fp8: prefill {T} tokens in place, sampled rows")
+    wq = synth.make_weights_fp8(seed=0)
+    w64 = {}
+    for name in ("q_a", "q_b", "kv_a", "kv_b", "o"):
+        w64[name] = ofp8.dequant_weight(wq[name], wq[name + "_s"])
+    for name in ("q_a_norm", "kv_a_norm"):
+        w64[name] = synth.bf16_bits_to_f64(wq[name])
+    L = binding.Layer(binding.weights_to_device(wq), max_positions=4096, wdtype=binding.WDTYPE_FP8)
+    gbits, g64 = norm_gain()
+    g = binding.bf16_tensor(gbits)
+    xbits = synth.make_hidden(T, seed=6250)
+    x = binding.bf16_tensor(xbits)
+    cache = binding.Cache(L, [T])
+    h = y_of(L.block_prefill(cache, [0], [0, T], g, x, h=x))
+    torch.cuda.synchronize()
+    x64 = synth.bf16_bits_to_f64(xbits)
+    rows = np.array([0, 1, 517, 1023, 1024, 1099])
+    ref = omla.block_attention(x64, w64, g64, rows=rows, w8a8=True)
+    check_block(h[rows], x64[rows], ref, f"fp8 prefill T={T} rows {rows.tolist()}")
+    L.close()
+
+
 def test_block_rejects_partial_overlap_and_missing_gain():
     import ctypes
 
