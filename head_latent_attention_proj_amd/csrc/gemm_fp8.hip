@@ -524,10 +524,11 @@ MLA_DEV void ring8_operands(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, 
       : "memory");
 }
 
-// Requirements (checked by ring8_ok): K a multiple of 128, 16-byte aligned operand rows, epilogue
-// EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), and for
-// a residual 16-byte alignment and ldr a multiple of 8.
-template <int TAG>
+// Requirements (checked by ring8_ok): K a multiple of 128, 16-byte aligned operand rows, and
+// EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), for a
+// residual 16-byte alignment and ldr a multiple of 8; or EPI_KVB (batch 1) with key_base and vt_ld
+// multiples of 4, N of 8, K_nope 16-byte and V^T planes 8-byte aligned.
+template <int TAG, bool PREC>
 __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
   using namespace ring8;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
@@ -624,16 +625,42 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
     i32x8_t bfr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bfr[j] = cat8(rb[2 * j], rb[2 * j + 1]);
+    if constexpr (PREC) {
+      // the same 32 codes per lane, widened to bf16 and summed in four steps of eight (the
+      // group's sum is complete before it is scaled, as in the tile kernel)
+      bf16x8_t bw[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8_t af = cat8(ra[2 * i], ra[2 * i + 1]);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int s = 0; s < 4; ++s) bw[j][s] = widen8(bfr[j][2 * s], bfr[j][2 * s + 1]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sp[i][e];
-        d[i][j] = mfma_fp8_16x16x128(af, bfr[j]);
+      for (int i = 0; i < 4; ++i) {
+        const i32x8_t af = cat8(ra[2 * i], ra[2 * i + 1]);
+        bf16x8_t aw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) aw[s] = widen8(af[2 * s], af[2 * s + 1]);
+        const f32x4_t sab = sc[i] * sbk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) dd = mfma_bf16_16x16x32(aw[s], bw[j][s], dd);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += dd[e] * sab[e];
+        }
       }
-      sp[i] = sc[i] * sbk;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x8_t af = cat8(ra[2 * i], ra[2 * i + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sp[i][e];
+          d[i][j] = mfma_fp8_16x16x128(af, bfr[j]);
+        }
+        sp[i] = sc[i] * sbk;
+      }
     }
   }
 #pragma unroll
@@ -646,6 +673,60 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
   __syncthreads();  // every wave is done with the ring: it becomes the output staging
   static_assert(8 * 64 * LDW * 4 <= S * STAGE, "epilogue staging fits the ring");
 
+  const int mw = m0 + wm * 64, nw = n0 + wn * 64;
+  if (p.epi == EPI_KVB) {
+    // kv_b (fp16): a wave's 64 columns lie in one half of a head's 256. Content keys go through
+    // LDS and leave as 16-byte pieces of K_nope rows; values and their fp16 residuals go straight
+    // to V^T as 8-byte pieces (a lane's four accumulators are four consecutive keys of one feature)
+    constexpr int LDH = 64 + 8;
+    uint16_t* shi = reinterpret_cast<uint16_t*>(ring) + wave * (64 * LDH);
+    const bool khalf = (nw & 255) < 128;
+    if (khalf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) shi[(i * 16 + g * 4 + e) * LDH + j * 16 + l16] = (uint16_t)pack_f16x2(acc[i][j][e], 0.f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int mb = mw + i * 16 + g * 4;
+          const int n = nw + j * 16 + l16;
+          if (n >= p.N) continue;
+          if (mb + 3 < p.M) {
+            const f32x4_t v = acc[i][j];
+            const uint32_t h01 = pack_f16x2(v[0], v[1]), h23 = pack_f16x2(v[2], v[3]);
+            const int64_t at = (int64_t)((n >> 8) * 128 + (n & 255) - 128) * p.vt_ld + p.key_base + mb;
+            *reinterpret_cast<u32x2_t*>(p.vt + at) = u32x2_t{h01, h23};
+            if (p.vt_lo)
+              *reinterpret_cast<u32x2_t*>(p.vt_lo + at) =
+                  u32x2_t{pack_f16x2(v[0] - f16_lo(h01), v[1] - f16_hi(h01)), pack_f16x2(v[2] - f16_lo(h23), v[3] - f16_hi(h23))};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (mb + e < p.M) epi_store8(p, batch, mb + e, n, acc[i][j][e]);
+          }
+        }
+    }
+    __syncthreads();
+    if (khalf) {
+      const int lr8 = lane >> 3, lc8 = (lane & 7) * 8;
+      const int n = nw + lc8;
+      if (n < p.N) {
+        const int64_t col = (n >> 8) * 128 + (n & 255);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = k * 8 + lr8, m = mw + r;
+          if (m < p.M) st16(p.knope + (p.key_base + m) * 8192 + col, ld16(shi + r * LDH + lc8));
+        }
+      }
+    }
+    return;
+  }
+
   // float32 results through LDS (a private region per wave), then whole 16-byte pieces of output
   // rows: bf16 rounds acc (+ residual) once, as the per-element epilogue does
   float* sw = reinterpret_cast<float*>(ring) + wave * (64 * LDW);
@@ -656,7 +737,6 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = acc[i][j][e];
   __syncthreads();
-  const int mw = m0 + wm * 64, nw = n0 + wn * 64;
   if (p.epi == EPI_BF16) {
     const int lr = lane >> 3, lc = (lane & 7) * 8;
     const int n = nw + lc;
@@ -785,6 +865,11 @@ bool ring8_ok(const GemmArgs& a) {
     return false;
   if (a.epi == EPI_BF16)
     return (a.N & 7) == 0 && (a.ldc & 7) == 0 && (a.sC & 7) == 0 && (!a.resid || (al16(a.resid) && (a.ldr & 7) == 0));
+  if (a.epi == EPI_KVB) {
+    auto al8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; };
+    return a.batch == 1 && (a.key_base & 3) == 0 && (a.vt_ld & 3) == 0 && (a.N & 7) == 0 && al16(a.knope) &&
+           al8(a.vt) && (!a.vt_lo || al8(a.vt_lo));
+  }
   return a.epi == EPI_F32 && (a.N & 3) == 0 && (a.ldc & 3) == 0 && (a.sC & 3) == 0;
 }
 
@@ -797,9 +882,12 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
     return;
   }
   dim3 grid(pl.tiles, pl.splits, a.batch);
-  if constexpr (!PREC) {
-    if (pl.kind == 2 && pl.splits == 1 && ring8_ok(a)) {
-      hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG>), grid, dim3(512), 0, s, a);
+  // prefill sizes: the ring kernel (one 128 x 256 tile per CU), for the precise form when it has
+  // at least one round of workgroups
+  if (pl.splits == 1 && ring8_ok(a)) {
+    const int rt = cdiv(a.M, ring8::BM) * cdiv(a.N, ring8::BN);
+    if (PREC ? (pl.kind == 1 && a.M >= 1024 && a.N >= 1024 && rt * a.batch >= 256) : pl.kind == 2) {
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC>), dim3(rt, 1, a.batch), dim3(512), 0, s, a);
       return;
     }
   }

@@ -6,8 +6,9 @@ library forms each 128-wide K group's sum in one of two ways: "precise" widens t
 bf16 and sums them with bf16 MFMAs into float32 (q_a|kv_a, kv_b), "native" uses one FP8 MFMA per
 group (q_b, o_proj). The error is measured relative to sum_k |a_k b_k| of each output element (the
 natural scale of a summation error), on the layer's own weights and activations quantised by the
-oracle's quantiser, with ragged M (decode-sized, and prefill-sized for the native form's
-128 x 256 tiles fed through a ring of LDS stages). Bars: precise within float32 summation (1e-5), native within
+oracle's quantiser, with ragged M: decode-sized, and prefill-sized for the 128 x 256 tiles fed
+through a ring of LDS stages (the native form from 1024 rows, the precise one from a full round of
+such tiles). Bars: precise within float32 summation (1e-5), native within
 1e-3; both levels are logged, since they decide which projections may take the native form.
 """
 import numpy as np
@@ -29,7 +30,8 @@ def deq_rows(codes, scales):
     return ofp8.dequant_1x128(codes, scales)
 
 
-@pytest.mark.parametrize("name,M", [("q_a", 200), ("q_b", 129), ("kv_b", 300), ("o", 96), ("q_b", 1100), ("o", 1030)])
+@pytest.mark.parametrize("name,M", [("q_a", 200), ("q_b", 129), ("kv_b", 300), ("o", 96), ("q_b", 1100), ("o", 1030),
+                                    ("kv_b", 1100), ("q_a", 5600)])
 def test_fp8_gemm_forms_against_float64(name, M):
     import torch
 
