@@ -383,7 +383,7 @@ def main():
             cp8.len_d.zero_()
             lf.prefill(cp8, sids, qs8, xp8, y=yp8, seq_ids_d=sids_dev, q_start_d=qs8_dev)
 
-        t = R.timed(pre8, 3, 1)
+        t = R.timed(pre8, 6, 2)
         t_at = R.probed(pre8, 3, 0, "prefill_attn")
         t_op = R.probed(pre8, 3, 0, "oproj")
         fl = 4 * prefill_flops(T8)
@@ -395,7 +395,7 @@ def main():
             "roofline": roofline("prefill_attn_kernel<true> (causal, fp16 operands, value residuals)", "mfma-bf16", att,
                                  t_at, "flops: 640 per head per causal pair (counted once, though the value products "
                                        "run twice: values and their fp16 residuals)"),
-            "roofline_oproj": roofline("gemm_fp8_tile_kernel (o_proj, M=16384, N=7168, K=8192, FP8)", "mfma-fp8",
+            "roofline_oproj": roofline("gemm_fp8_ring_kernel (o_proj, M=16384, N=7168, K=8192, FP8 native)", "mfma-fp8",
                                        2 * 4 * T8 * 8192 * 7168, t_op, "flops: 2 M N K"),
             "note": "mfma_frac = (fp8 projection flops / 5 PF + attention flops / 2.5 PF) / time"}
         del cp8, xp8, yp8

@@ -222,7 +222,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     __syncthreads();
     sstore(blk);
     __syncthreads();
-    if (blk + 1 < nblk) gload(blk + 1);
+    // the next block's loads, issued unconditionally (the last trip re-loads its own block, unused)
+    // so that they sit in the same straight-line code as the score products
+    gload(min(blk + 1, nblk - 1));
     const int kb = blk * PKB;
     if (kb > wq_hi) continue;  // every key of this block is in the future of this wave's queries
 
@@ -241,39 +243,49 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       }
     }
 
-    const bool need_mask = kb + PKB - 1 > wq_lo;
-    frag_t pf[2][2];
+    if (kb + PKB - 1 > wq_lo) {  // wave-uniform: only blocks that reach past the wave's first query
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      // scores stay unscaled here: the scale (softmax scale times log2 e, positive) commutes with
-      // the maximum and is applied inside each exponent's fused multiply-add
-      float bmax = -INFINITY;
-      if (need_mask) {  // wave-uniform: only blocks that reach past the wave's first query
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (kb + kt * 16 + g * 4 + e > qpos[qt]) sacc[kt][qt][e] = -INFINITY;
-      }
+    }
+    // scores stay unscaled here: the scale (softmax scale times log2 e, positive) commutes with
+    // the maximum and is applied inside each exponent's fused multiply-add
+    float bmax[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, sacc[kt][qt][e]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      bmax *= sl2;
-      // The running maximum is raised only when some query's block maximum exceeds it by more
-      // than 8 (log2 units; wave-uniform decision): probabilities stay <= 256 and the output
-      // accumulators are rescaled rarely. The first block holds key 0, visible to every query,
-      // so mrun is finite after it.
-      if (__any(bmax > mrun[qt] + 8.0f)) {
-        const float mnew = fmaxf(mrun[qt], bmax);
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kt][qt][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      bmax[qt] = mx * sl2;
+    }
+    // The running maximum is raised only when some query's block maximum exceeds it by more than
+    // 8 (log2 units; one wave-uniform decision for both query tiles): probabilities stay <= 256
+    // and the output accumulators are rescaled rarely. The first block holds key 0, visible to
+    // every query, so mrun is finite after it.
+    if (__any(bmax[0] > mrun[0] + 8.0f || bmax[1] > mrun[1] + 8.0f)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mnew = fmaxf(mrun[qt], bmax[qt]);
         const float alpha = exp2_flush(mrun[qt] - mnew);
         mrun[qt] = mnew;
         lrun[qt] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) oacc[d][qt] *= alpha;
       }
+    }
+    // probabilities, their sums and the value products of both query tiles in one stretch of
+    // straight-line code: one tile's exponentials can issue while the other's products run
+    frag_t pf[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
