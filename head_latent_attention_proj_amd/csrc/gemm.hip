@@ -56,14 +56,19 @@ template <int BM, int BN, int WM, int WN, int TAG>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int splits, int ksplit) {
   constexpr int NT = WM * WN * 64;
   constexpr int BK = 64;
-  constexpr int LDK = BK + 8;  // 144-byte rows: 8 consecutive rows hit 8 distinct 16-byte bank groups
+  // Stage rows of 64 features (128 bytes) without padding; 16-byte chunk c of row r is kept at
+  // position c ^ ((r / 2) % 8). The stores (8 lanes per row) and the operand reads (row l16, chunk
+  // 4s + g) then meet distinct banks for every 16 lanes of an instruction; padded 144-byte rows left
+  // the stores of two consecutive rows on four shared banks.
+  constexpr int LDK = BK;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr int CPR = BK / 8;
   constexpr int RPP = NT / CPR;
   constexpr int AP = BM / RPP, BP = BN / RPP;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of rows per pass");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+  constexpr int SMEM = std::max(2 * (BM + BN) * LDK, WM * WN * WTM * (WTN + 8));  // tiles / epilogue staging
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,6 +94,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
 
   const int lr = tid / CPR, lc = (tid % CPR) * 8;
+  static_assert(CPR == 8 && RPP % 16 == 0, "swizzle: 8 chunks per row, passes of whole 16-row groups");
+  const int lcs = (((tid % CPR) ^ ((lr >> 1) & 7)) << 3);  // this thread's chunk, swizzled
   const uint16_t* ga[AP];
   const uint16_t* gb[BP];
 #pragma unroll
@@ -117,9 +124,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
     uint16_t* sa = smem + buf * (BM + BN) * LDK;
     uint16_t* sb = sa + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lc, ra[i]);
+    for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lcs, ra[i]);
 #pragma unroll
-    for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lc, rb[i]);
+    for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lcs, rb[i]);
   };
 
   if (nk > 0) {
@@ -130,15 +137,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
-    const uint16_t* sa = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK + g * 8;
-    const uint16_t* sb = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK + g * 8;
+    const uint16_t* sa = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK;
+    const uint16_t* sb = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK;
+    const int swz = (l16 >> 1) & 7;  // the operand rows' swizzle (16-row tiles keep it)
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s) {
+      const int cs = ((4 * s + g) ^ swz) << 3;
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(ld16(sa + i * 16 * LDK + s * 32));
+      for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(ld16(sa + i * 16 * LDK + cs));
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = as_bf16x8(ld16(sb + j * 16 * LDK + s * 32));
+      for (int j = 0; j < TN; ++j) bfr[j] = as_bf16x8(ld16(sb + j * 16 * LDK + cs));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
       // tile buffers are free after the loop's last barrier), then stores whole 16-byte pieces of
       // output rows, eight lanes per 128-byte row segment, instead of one 2-byte store per value
       constexpr int LDW = WTN + 8;
-      static_assert(WM * WN * WTM * LDW <= 2 * (BM + BN) * LDK, "epilogue staging fits the tile buffers");
+      static_assert(WM * WN * WTM * LDW <= SMEM, "epilogue staging fits the tile buffers");
       uint16_t* sw = smem + wave * (WTM * LDW);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(GemmArgs p, int 
       // go through LDS as for bf16 outputs and leave as 16-byte pieces of K_nope rows; values go
       // straight to V^T, a lane's four accumulators (four consecutive keys of one feature) as one
       // 8-byte store. Every wave reaches the barrier.
-      static_assert(WTN == 64 && WM * WN * WTM * (WTN + 8) <= 2 * (BM + BN) * LDK, "kv_b epilogue layout");
+      static_assert(WTN == 64 && WM * WN * WTM * (WTN + 8) <= SMEM, "kv_b epilogue layout");
       constexpr int LDW = WTN + 8;
       uint16_t* sw = smem + wave * (WTM * LDW);
       const int nw0 = n0 + wn * WTN;
