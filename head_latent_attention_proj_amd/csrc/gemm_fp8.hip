@@ -190,15 +190,18 @@ __global__ __launch_bounds__(KW * 64) void gemm_fp8_wsplit_kernel(GemmArgs p) {
 template <int BM, int BN, int WM, int WN, int TAG, bool PREC>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, int splits, int ksplit) {
   constexpr int NT = WM * WN * 64;
-  constexpr int BK = 128;        // bytes (= codes) per row per stage: one K group
-  constexpr int LDK = BK + 16;
+  constexpr int BK = 128;  // bytes (= codes) per row per stage: one K group
+  // unpadded 128-byte stage rows, 16-byte chunk c of row r at position c ^ ((r / 2) % 8): the
+  // stores (8 lanes per row) and the operand reads meet distinct banks in every 16 lanes
+  constexpr int LDK = BK;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr int CPR = BK / 16;
   constexpr int RPP = NT / CPR;
   constexpr int AP = BM / RPP, BP = BN / RPP;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of rows per pass");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * LDK];
+  constexpr int SMEM = std::max(2 * (BM + BN) * LDK, WM * WN * (BM / WM) * (BN / WN + 8) * 4);  // tiles / epilogue
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ __attribute__((aligned(16))) float sSa[2][BM];  // A scales of the stage's K group, per row
   static_assert((BM & (BM - 1)) == 0 && NT >= BM, "one A scale per thread");
 
@@ -224,6 +227,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
   const uint8_t* B = (const uint8_t*)p.B + batch * p.sB;
 
   const int lr = tid / CPR, lc = (tid % CPR) * 16;
+  static_assert(CPR == 8 && RPP % 16 == 0, "swizzle: 8 chunks per row, passes of whole 16-row groups");
+  const int lcs = ((tid % CPR) ^ ((lr >> 1) & 7)) << 4;  // this thread's chunk, swizzled
   const uint8_t* ga[AP];
   const uint8_t* gb[BP];
 #pragma unroll
@@ -261,9 +266,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     uint8_t* sa = smem + buf * (BM + BN) * LDK;
     uint8_t* sb = sa + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lc, ra[i]);
+    for (int i = 0; i < AP; ++i) st16(sa + (i * RPP + lr) * LDK + lcs, ra[i]);
 #pragma unroll
-    for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lc, rb[i]);
+    for (int i = 0; i < BP; ++i) st16(sb + (i * RPP + lr) * LDK + lcs, rb[i]);
     if (tid < BM) sSa[buf][tid] = rsa;
   };
 
@@ -283,8 +288,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 #pragma unroll
       for (int i = 0; i < TM; ++i) sab[i] = *reinterpret_cast<const f32x4_t*>(&sSa[cur][wm * WTM + i * 16 + g * 4]) * sbk;
     }
-    const uint8_t* sA = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK + g * 32;
-    const uint8_t* sB = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK + g * 32;
+    // this lane's rows (row l16 of each 16-row tile keeps its swizzle) and the positions of its
+    // chunks 2g and 2g + 1
+    const uint8_t* sA = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK;
+    const uint8_t* sB = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK;
+    const int swz = (l16 >> 1) & 7;
+    const int c0 = ((2 * g) ^ swz) << 4, c1 = ((2 * g + 1) ^ swz) << 4;
     if constexpr (PREC) {
       // four steps of eight codes (k = g*32 + st*8 ..) widened to bf16 as they are read
       f32x4_t d[TM][TN];
@@ -297,12 +306,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
         bf16x8_t bw[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sB + j * 16 * LDK + st * 8);
+          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sB + j * 16 * LDK + (st < 2 ? c0 : c1) + (st & 1) * 8);
           bw[j] = widen8(r[0], r[1]);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sA + i * 16 * LDK + st * 8);
+          const u32x2_t r = *reinterpret_cast<const u32x2_t*>(sA + i * 16 * LDK + (st < 2 ? c0 : c1) + (st & 1) * 8);
           const bf16x8_t aw = widen8(r[0], r[1]);
 #pragma unroll
           for (int j = 0; j < TN; ++j) d[i][j] = mfma_bf16_16x16x32(aw, bw[j], d[i][j]);
@@ -317,10 +326,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     } else {
       i32x8_t bfr[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = cat8(ld16(sB + j * 16 * LDK), ld16(sB + j * 16 * LDK + 16));
+      for (int j = 0; j < TN; ++j) bfr[j] = cat8(ld16(sB + j * 16 * LDK + c0), ld16(sB + j * 16 * LDK + c1));
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const i32x8_t af = cat8(ld16(sA + i * 16 * LDK), ld16(sA + i * 16 * LDK + 16));
+        const i32x8_t af = cat8(ld16(sA + i * 16 * LDK + c0), ld16(sA + i * 16 * LDK + c1));
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const f32x4_t d = mfma_fp8_16x16x128(af, bfr[j]);
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
       // (then free) tile buffers and stores whole 16-byte pieces of output rows, eight lanes per
       // 128-byte row segment, instead of one 2-byte store per value
       constexpr int LDW = WTN + 8;
-      static_assert(WM * WN * WTM * LDW * 2 <= 2 * (BM + BN) * LDK, "epilogue staging fits the tile buffers");
+      static_assert(WM * WN * WTM * LDW * 2 <= SMEM, "epilogue staging fits the tile buffers");
       uint16_t* sw = reinterpret_cast<uint16_t*>(smem) + wave * (WTM * LDW);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
       }
       return;
     }
-    if constexpr (WTN == 64 && WM * WN * WTM * (WTN + 8) * 4 <= 2 * (BM + BN) * LDK) {
+    if constexpr (WTN == 64 && WM * WN * WTM * (WTN + 8) * 4 <= SMEM) {
       if (p.epi == EPI_KVB && (p.key_base & 3) == 0 && (p.N & 7) == 0) {
         // kv_b (fp16): a wave's 64 columns lie in one half of a head's 256 (wave-uniform). Content
         // keys go through LDS and leave as 16-byte pieces of K_nope rows; values and their fp16
