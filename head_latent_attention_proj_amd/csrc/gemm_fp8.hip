@@ -497,11 +497,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 // the 16 lanes of one g on distinct banks. The row scales are fetched by one wave per 64 rows.
 // Three stages of 48.5 KB: one workgroup per CU.
 namespace ring8 {
-constexpr int BM = 128, BN = 256, S = 3;
-constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+constexpr int BM = 128, S = 3;
+constexpr int A_BYTES = BM * 128;
 constexpr int SC_BYTES = BM * 4;
-constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;  // 49,664 bytes
-constexpr int LDW = 64 + 4;                          // float32 epilogue staging row (a wave's 64 columns)
+constexpr int LDW = 64 + 4;  // float32 epilogue staging row (a wave's 64 columns)
+// stage bytes for a BN-column tile: 49,664 at 256 columns, 25,088 at 64
+constexpr int stage_bytes(int bn) { return A_BYTES + bn * 128 + SC_BYTES; }
 }  // namespace ring8
 
 // One stage's operands of a wave (byte addresses of this lane's 16 bytes): A blocks at a0 / a1
@@ -537,13 +538,19 @@ MLA_DEV void ring8_operands(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, 
 // EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), for a
 // residual 16-byte alignment and ldr a multiple of 8; or EPI_KVB (batch 1) with key_base and vt_ld
 // multiples of 4, N of 8, K_nope 16-byte and V^T planes 8-byte aligned.
-template <int TAG, bool PREC>
-__global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
+// BN = 256 (prefill sizes: 8 waves, one workgroup per CU) or 64 (decode sizes: 2 waves, two
+// workgroups per CU, K split over blockIdx.y into float32 partials when `splits` > 1).
+template <int TAG, bool PREC, int BN>
+__global__ __launch_bounds__(BN / 32 * 64) void gemm_fp8_ring_kernel(GemmArgs p, int splits, int ksplit) {
   using namespace ring8;
+  constexpr int WN = BN / 64, NW = 2 * WN;  // waves: 2 x WN of 64 x 64
+  constexpr int APW = 8 / NW;               // A blocks (16 rows) fetched per wave; B blocks: 2
+  constexpr int B_BYTES = BN * 128;
+  constexpr int STAGE = stage_bytes(BN);
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, g = lane >> 4;
 
   // tile order of the tile kernel: XCD-aware, then groups of 8 row tiles
@@ -557,42 +564,48 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
   const int gs = min(tiles_m - fm, GM);
   const int m0 = (fm + (bid % per_group) % gs) * BM;
   const int n0 = ((bid % per_group) / gs) * BN;
-  const int batch = blockIdx.z;
+  const int batch = blockIdx.z, split = blockIdx.y;
   const uint8_t* A = (const uint8_t*)p.A + batch * p.sA;
   const uint8_t* B = (const uint8_t*)p.B + batch * p.sB;
-  const int nk = p.K >> 7;
+  const int kg0 = split * (ksplit >> 7);                   // this split's first K group
+  const int nk = min(p.K, (split + 1) * ksplit) / 128 - kg0;  // >= 1 (plan)
 
-  // this wave's loads: A block `wave`, B blocks 2 wave and 2 wave + 1, two instructions of 8 rows
-  // each (rows past M and N re-read the last one); lane l reads row 8 q + l / 8 of instruction q,
-  // the chunk that belongs at position l % 8 of that row
+  // this wave's loads: A blocks APW wave .. +APW-1, B blocks 2 wave and 2 wave + 1, two
+  // instructions of 8 rows each per block (rows past M and N re-read the last one); lane l reads
+  // row 8 q + l / 8 of instruction q, the chunk that belongs at position l % 8 of that row
   const int lr = lane >> 3;
   auto src = [&](const uint8_t* base, int64_t ld, int r0, int lim, int q) {
     const int r = q * 8 + lr;
-    return base + (int64_t)min(r0 + r, lim - 1) * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    return base + (int64_t)min(r0 + r, lim - 1) * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 4) + (int64_t)kg0 * 128;
   };
-  const uint8_t* ga0 = src(A, p.lda, m0 + wave * 16, p.M, 0);
-  const uint8_t* ga1 = src(A, p.lda, m0 + wave * 16, p.M, 1);
-  const uint8_t* gb0 = src(B, p.ldb, n0 + wave * 32, p.N, 0);
-  const uint8_t* gb1 = src(B, p.ldb, n0 + wave * 32, p.N, 1);
-  const uint8_t* gb2 = src(B, p.ldb, n0 + wave * 32 + 16, p.N, 0);
-  const uint8_t* gb3 = src(B, p.ldb, n0 + wave * 32 + 16, p.N, 1);
-  // the row scales: waves 0 and 4 fetch rows wm * 64 + lane
+  const uint8_t* ga[APW][2];
+#pragma unroll
+  for (int a = 0; a < APW; ++a) {
+    ga[a][0] = src(A, p.lda, m0 + (wave * APW + a) * 16, p.M, 0);
+    ga[a][1] = src(A, p.lda, m0 + (wave * APW + a) * 16, p.M, 1);
+  }
+  const uint8_t* gb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) gb[t] = src(B, p.ldb, n0 + wave * 32 + (t >> 1) * 16, p.N, t & 1);
+  // the row scales: the waves of column 0 fetch rows wm * 64 + lane
   const bool scw = wn == 0;
-  const float* gsa = p.a_scale + (int64_t)min(m0 + wm * 64 + lane, p.M - 1) * p.as_ld;
+  const float* gsa = p.a_scale + (int64_t)min(m0 + wm * 64 + lane, p.M - 1) * p.as_ld + kg0;
   auto issue = [&](int kt, int slot) {
     uint8_t* st = ring + slot * STAGE;
     const int64_t k0 = (int64_t)kt * 128;
-    gl2lds16(ga0 + k0, st + wave * 2048);
-    gl2lds16(ga1 + k0, st + wave * 2048 + 1024);
-    gl2lds16(gb0 + k0, st + A_BYTES + wave * 4096);
-    gl2lds16(gb1 + k0, st + A_BYTES + wave * 4096 + 1024);
-    gl2lds16(gb2 + k0, st + A_BYTES + wave * 4096 + 2048);
-    gl2lds16(gb3 + k0, st + A_BYTES + wave * 4096 + 3072);
+#pragma unroll
+    for (int a = 0; a < APW; ++a) {
+      gl2lds16(ga[a][0] + k0, st + (wave * APW + a) * 2048);
+      gl2lds16(ga[a][1] + k0, st + (wave * APW + a) * 2048 + 1024);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) gl2lds16(gb[t] + k0, st + A_BYTES + wave * 4096 + t * 1024);
     if (scw) gl2lds4(gsa + kt, st + A_BYTES + B_BYTES + wm * 256);
   };
+  constexpr int LPS = 2 * APW + 4;  // loads per wave per stage, plus one on the scale waves
 
   // the wave's weight scales: its 64 columns lie in one 128-column block
-  const float* gsb = p.b_scale + (int64_t)(min(n0 + wn * 64, p.N - 1) >> 7) * p.bs_ld;
+  const float* gsb = p.b_scale + (int64_t)(min(n0 + wn * 64, p.N - 1) >> 7) * p.bs_ld + kg0;
   // operand addresses within a stage: row l16 of a block, chunk halves 2g and 2g + 1
   const int swz = (l16 >> 1) & 7;
   const uint32_t oa0 = wm * 8192 + l16 * 128 + (((2 * g) ^ swz) << 4);
@@ -615,11 +628,11 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue(min(t, nk - 1), t);
   for (int t = 0; t < nk; ++t) {
-    // this wave's part of stage t has landed (one stage, 6 or 7 loads, may stay in flight) ...
+    // this wave's part of stage t has landed (one stage of LPS or LPS + 1 loads may stay in flight) ...
     if (scw)
-      wait_vmcnt<(S - 2) * 7>();
+      wait_vmcnt<(S - 2) * (LPS + 1)>();
     else
-      wait_vmcnt<(S - 2) * 6>();
+      wait_vmcnt<(S - 2) * LPS>();
     // ... and every wave's; all are done with stage t - 1, whose slot is refilled next. A plain
     // barrier: __syncthreads' release fence would wait for every load in flight.
     asm volatile("s_barrier" ::: "memory");
@@ -680,9 +693,31 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
       for (int e = 0; e < 4; ++e) acc[i][j][e] += d[i][j][e] * sp[i][e];
   wait_vmcnt<0>();  // the tail's re-fetches have landed
   __syncthreads();  // every wave is done with the ring: it becomes the output staging
-  static_assert(8 * 64 * LDW * 4 <= S * STAGE, "epilogue staging fits the ring");
+  static_assert(NW * 64 * LDW * 4 <= S * STAGE, "epilogue staging fits the ring");
 
   const int mw = m0 + wm * 64, nw = n0 + wn * 64;
+  float* sw = reinterpret_cast<float*>(ring) + wave * (64 * LDW);
+  if (splits > 1) {
+    // K split: float32 partials of this split, whole 16-byte pieces of rows (N a multiple of 4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = acc[i][j][e];
+    __syncthreads();
+    float* part = p.part + ((int64_t)batch * splits + split) * p.M * p.N;
+    const int lr4 = lane >> 4, lc4 = (lane & 15) * 4;
+    const int n = nw + lc4;
+    if (n < p.N) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int r = k * 4 + lr4, m = mw + r;
+        if (m < p.M) *reinterpret_cast<f32x4_t*>(part + (int64_t)m * p.N + n) = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc4);
+      }
+    }
+    return;
+  }
   if (p.epi == EPI_KVB) {
     // kv_b (fp16): a wave's 64 columns lie in one half of a head's 256. Content keys go through
     // LDS and leave as 16-byte pieces of K_nope rows; values and their fp16 residuals go straight
@@ -738,7 +773,6 @@ __global__ __launch_bounds__(512) void gemm_fp8_ring_kernel(GemmArgs p) {
 
   // float32 results through LDS (a private region per wave), then whole 16-byte pieces of output
   // rows: bf16 rounds acc (+ residual) once, as the per-element epilogue does
-  float* sw = reinterpret_cast<float*>(ring) + wave * (64 * LDW);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -891,16 +925,27 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
     return;
   }
   dim3 grid(pl.tiles, pl.splits, a.batch);
-  // prefill sizes: the ring kernel (one 128 x 256 tile per CU), for the precise form when it has
-  // at least one round of workgroups
-  if (pl.splits == 1 && ring8_ok(a)) {
-    const int rt = cdiv(a.M, ring8::BM) * cdiv(a.N, ring8::BN);
-    if (PREC ? (pl.kind == 1 && a.M >= 1024 && a.N >= 1024 && rt * a.batch >= 256) : pl.kind == 2) {
-      hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC>), dim3(rt, 1, a.batch), dim3(512), 0, s, a);
+  // The ring kernel: at prefill sizes one 128 x 256 tile per CU (the precise form when it has at
+  // least one round of workgroups), at decode sizes (up to 256 rows) 128 x 64 tiles with the
+  // plan's K split, native form only (measured at 128 rows: q_b 22.7 -> 16.3 us, o_proj 31.1 ->
+  // 28.7 us; the precise q_a|kv_a 14.0 -> 17.1 us, its one wave per SIMD left waiting on the
+  // chained bf16 products); otherwise the register-staged tile kernel.
+  bool ring = false;
+  if (ring8_ok(a)) {
+    const int rt = cdiv(a.M, ring8::BM) * cdiv(a.N, 256);
+    if (pl.splits == 1 && (PREC ? (pl.kind == 1 && a.M >= 1024 && a.N >= 1024 && rt * a.batch >= 256) : pl.kind == 2)) {
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC, 256>), dim3(rt, 1, a.batch), dim3(512), 0, s, a, 1, a.K);
       return;
     }
+    if constexpr (!PREC) {
+      if (pl.kind == 3) {
+        hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC, 64>), grid, dim3(128), 0, s, a, pl.splits, pl.ksplit);
+        ring = true;
+      }
+    }
   }
-  if (pl.kind == 1)
+  if (ring) {
+  } else if (pl.kind == 1)
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 128, 2, 2, TAG, PREC>), grid, dim3(256), 0, s, a, pl.splits,
                        pl.ksplit);
   else if (pl.kind == 3)
