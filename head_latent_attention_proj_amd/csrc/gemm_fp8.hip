@@ -538,8 +538,8 @@ MLA_DEV void ring8_operands(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, 
 // EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), for a
 // residual 16-byte alignment and ldr a multiple of 8; or EPI_KVB (batch 1) with key_base and vt_ld
 // multiples of 4, N of 8, K_nope 16-byte and V^T planes 8-byte aligned.
-// BN = 256 (prefill sizes: 8 waves, one workgroup per CU) or 64 (decode sizes: 2 waves, two
-// workgroups per CU, K split over blockIdx.y into float32 partials when `splits` > 1).
+// BN = 256 (prefill sizes: 8 waves, one workgroup per CU), 128 (4 waves, one per CU) or 64 (2 waves,
+// two per CU); at decode sizes K is split over blockIdx.y into float32 partials (`splits` > 1).
 template <int TAG, bool PREC, int BN>
 __global__ __launch_bounds__(BN / 32 * 64) void gemm_fp8_ring_kernel(GemmArgs p, int splits, int ksplit) {
   using namespace ring8;
@@ -938,7 +938,14 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
       return;
     }
     if constexpr (!PREC) {
-      if (pl.kind == 3) {
+      // 128 columns (one workgroup of 4 waves per CU, half the A re-reads per output) while that
+      // still gives 192 workgroups: o_proj at 128 rows 28.7 -> 23.9 us with the plan's 4 splits
+      const int t128 = cdiv(a.M, ring8::BM) * cdiv(a.N, 128);
+      if (pl.kind == 3 && t128 * pl.splits * a.batch >= 192) {
+        hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC, 128>), dim3(t128, pl.splits, a.batch), dim3(256), 0, s, a,
+                           pl.splits, pl.ksplit);
+        ring = true;
+      } else if (pl.kind == 3) {
         hipLaunchKernelGGL((gemm_fp8_ring_kernel<TAG, PREC, 64>), grid, dim3(128), 0, s, a, pl.splits, pl.ksplit);
         ring = true;
       }
