@@ -630,43 +630,44 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 // ------------------------------------------------------------------------------------------
 // 16 < M <= 64 with K >= 512: a ring of LDS stages filled by direct-to-LDS loads
 // ------------------------------------------------------------------------------------------
-// Workgroup = NW waves = 16*NW output columns over one K split. A stage covers 64 features: the
-// A tile (16*MT rows as 2*MT fragment blocks of 16 rows x 32 features, fetched by the waves in
-// turn) and each wave's own two weight blocks (its 16 rows). One wave instruction fetches one
-// 1 KB block straight into LDS (lane l's 16 bytes land at byte 16*l), with lane (l16, g) reading
-// row l16, features 8g .. 8g+7: the block in LDS is already the MFMA operand image, and every
-// lane reads its operand back at 16*l (contiguous, conflict-free). The loads hold no registers,
-// so S-1 stages are in flight while one is multiplied, and one barrier per stage suffices.
+// Workgroup = NW waves = 16*NW output columns over one K split. A stage covers 64 features
+// (128 bytes per row): the A tile (16*MT rows, MT groups of 16) and each wave's own 16 weight
+// rows. One wave instruction fetches 8 whole rows straight into LDS (lane l reads row l / 8, one
+// 16-byte chunk, landing at byte 16*l), so it touches 8 cache lines; a 16-row group lands
+// row-major with chunk c of row r at position c ^ ((r / 2) % 8), and a lane's operand (row l16,
+// chunk 4h + g for the stage's feature half h) is read with the 16 lanes of one g on distinct
+// banks. The loads hold no registers, so S-1 stages are in flight while one is multiplied, and
+// one barrier per stage suffices.
 
-// One stage's operands of a wave: A blocks 0 .. 2*MT-1 at a + 1024*b, the wave's two weight blocks
-// at w and w + 1024 (byte addresses, this lane's 16 bytes). Written as one asm block that waits
-// for its own reads: the compiler does not know that these LDS reads never touch the ring slots
-// the direct-to-LDS loads are still filling, and would otherwise wait for every load in flight.
-// The outputs are early-clobber: a read's destination must not be an address register of a later
-// read in the block.
+// One stage's operands of a wave (byte addresses of this lane's 16 bytes): A row group i, feature
+// half h at a_h + 2048 i; the wave's weight rows at w_h. Written as one asm block that waits for
+// its own reads: the compiler does not know that these LDS reads never touch the ring slots the
+// direct-to-LDS loads are still filling, and would otherwise wait for every load in flight. The
+// outputs are early-clobber: a read's destination must not be an address register of a later read.
 template <int MT>
-MLA_DEV void lds_stage_operands(uint32_t a, uint32_t w, u32x4_t (&ra)[2 * MT], u32x4_t (&rb)[2]) {
+MLA_DEV void lds_stage_operands(uint32_t a0, uint32_t a1, uint32_t w0, uint32_t w1, u32x4_t (&ra)[2 * MT],
+                                u32x4_t (&rb)[2]) {
   if constexpr (MT == 4) {
     asm volatile(
-        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %10 offset:1024\n\t"
-        "ds_read_b128 %2, %10 offset:2048\n\tds_read_b128 %3, %10 offset:3072\n\t"
-        "ds_read_b128 %4, %10 offset:4096\n\tds_read_b128 %5, %10 offset:5120\n\t"
-        "ds_read_b128 %6, %10 offset:6144\n\tds_read_b128 %7, %10 offset:7168\n\t"
-        "ds_read_b128 %8, %11\n\tds_read_b128 %9, %11 offset:1024\n\t"
+        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %11\n\t"
+        "ds_read_b128 %2, %10 offset:2048\n\tds_read_b128 %3, %11 offset:2048\n\t"
+        "ds_read_b128 %4, %10 offset:4096\n\tds_read_b128 %5, %11 offset:4096\n\t"
+        "ds_read_b128 %6, %10 offset:6144\n\tds_read_b128 %7, %11 offset:6144\n\t"
+        "ds_read_b128 %8, %12\n\tds_read_b128 %9, %13\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(ra[4]), "=&v"(ra[5]), "=&v"(ra[6]), "=&v"(ra[7]),
           "=&v"(rb[0]), "=&v"(rb[1])
-        : "v"(a), "v"(w)
+        : "v"(a0), "v"(a1), "v"(w0), "v"(w1)
         : "memory");
   } else {
     static_assert(MT == 2, "MT 2 or 4");
     asm volatile(
-        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:1024\n\t"
-        "ds_read_b128 %2, %6 offset:2048\n\tds_read_b128 %3, %6 offset:3072\n\t"
-        "ds_read_b128 %4, %7\n\tds_read_b128 %5, %7 offset:1024\n\t"
+        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %6 offset:2048\n\tds_read_b128 %3, %7 offset:2048\n\t"
+        "ds_read_b128 %4, %8\n\tds_read_b128 %5, %9\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1])
-        : "v"(a), "v"(w)
+        : "v"(a0), "v"(a1), "v"(w0), "v"(w1)
         : "memory");
   }
 }
@@ -675,9 +676,9 @@ MLA_DEV void lds_stage_operands(uint32_t a, uint32_t w, u32x4_t (&ra)[2 * MT], u
 // parts); 2: partials to p.part for splitk_reduce_kernel.
 template <int MT, int NW, int S, int TAG>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs p, int ksplit, int mode) {
-  constexpr int ABLK = 2 * MT;   // A fragment blocks per stage
-  constexpr int APW = ABLK / NW;  // of which each wave fetches APW
-  static_assert(ABLK % NW == 0 && S >= 2, "A blocks divide over the waves");
+  constexpr int ABLK = 2 * MT;   // A instructions per stage (8 rows each)
+  constexpr int APW = ABLK / NW;  // of which each wave issues APW
+  static_assert(ABLK % NW == 0 && S >= 2, "A loads divide over the waves");
   constexpr int LPS = APW + 2;                  // loads per stage per wave
   constexpr int STAGE = (ABLK + 2 * NW) * 512;  // bf16 elements per stage
   __shared__ __attribute__((aligned(1024))) uint16_t ring[S * STAGE];
@@ -691,13 +692,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs p, int ks
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA;
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
 
+  // lane l of load instruction q (rows 8q .. 8q+7 of a 16-row group) reads row 8q + l/8, the chunk
+  // that belongs at position l % 8 of that row
+  const int lr = lane >> 3;
+  auto chunk = [&](int q) { return (((lane & 7) ^ (((q * 8 + lr) >> 1) & 7)) << 3); };
   const uint16_t* ga[APW];
 #pragma unroll
   for (int j = 0; j < APW; ++j) {
-    const int blk = wave * APW + j;  // row group blk / 2, feature half blk % 2
-    ga[j] = A + (int64_t)min((blk >> 1) * 16 + l16, p.M - 1) * p.lda + kb + (blk & 1) * 32 + g * 8;
+    const int ins = wave * APW + j;  // row group ins / 2, rows 8 (ins % 2) ..
+    ga[j] = A + (int64_t)min((ins >> 1) * 16 + (ins & 1) * 8 + lr, p.M - 1) * p.lda + kb + chunk(ins & 1);
   }
-  const uint16_t* gb = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + kb + g * 8;
+  const uint16_t* gb[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) gb[q] = B + (int64_t)min(n0 + q * 8 + lr, p.N - 1) * p.ldb + kb + chunk(q);
 
   // Fetch stage st into ring slot buf. Callers clamp st to the last stage: in the tail the
   // re-fetch goes to the slot of a stage already consumed, so every iteration issues the same
@@ -707,8 +714,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs p, int ks
 #pragma unroll
     for (int j = 0; j < APW; ++j) gl2lds16(ga[j] + st * 64, base + (wave * APW + j) * 512);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) gl2lds16(gb + st * 64 + h * 32, base + (ABLK + wave * 2 + h) * 512);
+    for (int q = 0; q < 2; ++q) gl2lds16(gb[q] + st * 64, base + (ABLK + wave * 2 + q) * 512);
   };
+  // this lane's operand positions: row l16 of a 16-row group, chunk 4h + g for feature half h
+  const int swz = (l16 >> 1) & 7;
+  const uint32_t o0 = l16 * 128 + ((g ^ swz) << 4), o1 = l16 * 128 + (((4 + g) ^ swz) << 4);
 
   f32x4_t acc[MT];
 #pragma unroll
@@ -721,9 +731,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs p, int ks
     // release fence would wait for every load in flight, collapsing the ring to one stage.
     asm volatile("s_barrier" ::: "memory");
     issue(min(t + S - 1, nst - 1), (t + S - 1) % S);
-    const uint16_t* base = ring + (t % S) * STAGE + lane * 8;
+    const uint32_t base = lds_addr(ring + (t % S) * STAGE);
+    const uint32_t wb = base + (ABLK + wave * 2) * 1024;
     u32x4_t ra[2 * MT], rb[2];
-    lds_stage_operands<MT>(lds_addr(base), lds_addr(base + (ABLK + wave * 2) * 512), ra, rb);
+    lds_stage_operands<MT>(base + o0, base + o1, wb + o0, wb + o1, ra, rb);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
