@@ -125,8 +125,9 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
       const int key = min(kb + 2 * kp + u, c1 - 1);  // past the split's end: re-read (masked)
       rl[S][u] = ld16(bb + (key - kb) * eb + cc * 16);
     }
-    {  // every thread loads (threads 256..287 keep theirs): the same number of loads in every wave
-      const int key = min(kb + (tid & (DKB - 1)), c1 - 1);
+    {  // every thread loads (threads 256..287 keep theirs): the same number of loads in every wave;
+       // the other waves read one wave-uniform address (one cache line per instruction)
+      const int key = min(kb + (wave == 4 ? (tid & (DKB - 1)) : 0), c1 - 1);
       rs[S] = ld16(bb + (key - kb) * eb + KV_LORA);
     }
     const int key = min(kb + (tid >> 4), c1 - 1);
