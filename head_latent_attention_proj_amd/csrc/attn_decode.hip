@@ -161,7 +161,7 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
   if constexpr (FP8_AHEAD > 2) gload(min(2, nblk - 1), std::integral_constant<int, 2>{});
 
   // ---- query fragments (B operand), fp16: column = head, features lh*288 + ks*32 + g*8 .. +7;
-  // the latent part is the sum of the two float32 absorbed products, features >= 512 are the rotary
+  // the latent part is the absorbed product (or the sum of two float32 parts), features >= 512 are the rotary
   // part, rotated here at the query's position
   f16x8_t qf[9];
   {
@@ -172,13 +172,20 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
       float v[8];
       if (f < KV_LORA) {
         const float* qlf = (const float*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f;
-        const float* qlr = qlf + a.q_lat_lo;
         const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qlf), v1 = *reinterpret_cast<const f32x4_t*>(qlf + 4);
-        const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(qlr), r1 = *reinterpret_cast<const f32x4_t*>(qlr + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[j] = v0[j] + r0[j];
-          v[4 + j] = v1[j] + r1[j];
+          v[j] = v0[j];
+          v[4 + j] = v1[j];
+        }
+        if (a.q_lat_lo != 0) {
+          const float* qlr = qlf + a.q_lat_lo;
+          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(qlr), r1 = *reinterpret_cast<const f32x4_t*>(qlr + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] += r0[j];
+            v[4 + j] += r1[j];
+          }
         }
       } else {
         const int pair0 = (f - KV_LORA) >> 1;

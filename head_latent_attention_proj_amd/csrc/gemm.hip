@@ -575,7 +575,8 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs p, int rw, Norm
 // Workgroup = (head, 16 NWV output columns, 64-row chunk of x); the chunk x_h[m0 .. m0+63] (K =
 // 32 KS) is staged in LDS once and every wave streams 16 weight rows over the whole K with all of
 // its loads issued up front; 16x16x32 MFMA, A fragments from LDS (rows >= M are copies of row
-// M - 1 and never stored).
+// M - 1 and never stored). With pair_rows, a workgroup takes 32 rows and their 32 residual rows
+// (tile rows 0..31 and 32..63) and stores the sums.
 template <int KS, int NWV, int TAG>
 __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
   constexpr int LDX = KS * 32 + 8;  // padded LDS row: consecutive rows in distinct 16-byte bank groups
@@ -585,9 +586,15 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.y * (16 * NWV) + wave * 16;
-  const int m0 = blockIdx.z * 64;
+  const bool pair = p.pair_rows > 0;
+  const int m0 = blockIdx.z * (pair ? 32 : 64);
   const uint16_t* A = (const uint16_t*)p.A + batch * p.sA + (int64_t)m0 * p.lda;
-  const int mrows = min(64, p.M - m0);
+  const int mrows = pair ? min(32, p.pair_rows - m0) : min(64, p.M - m0);
+  // A row (relative to m0) of tile row r
+  auto arow = [&](int r) -> int64_t {
+    if (!pair) return min(r, mrows - 1);
+    return min(r & 31, mrows - 1) + (r >= 32 ? p.pair_rows : 0);
+  };
   const uint16_t* B = (const uint16_t*)p.B + batch * p.sB;
   u32x4_t wb[KS];
   const uint16_t* wr = B + (int64_t)min(n0 + l16, p.N - 1) * p.ldb + 8 * g;
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + NT * i, row = c / CH, ch = c % CH;
-      xv[i] = ld16(A + (int64_t)min(row, mrows - 1) * p.lda + ch * 8);
+      xv[i] = ld16(A + arow(row) * p.lda + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -618,6 +625,22 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       acc[i] = mfma_bf16_16x16x32(as_bf16x8(ld16(xs + (16 * i + l16) * LDX + 32 * ks + 8 * g)), as_bf16x8(wb[ks]), acc[i]);
+  if (pair) {
+    // high part (tile rows 0..31) plus residual part (rows 32..63), each scaled, as two float32
+    // roundings and one float32 addition (no fused multiply-add)
+    const int n = n0 + l16;
+    const float cs = p.c_scale ? p.c_scale[batch * p.cs_stride + (n >> 7)] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * i + 4 * g + e;
+        const float hi = p.c_scale ? __fmul_rn(acc[i][e], cs) : acc[i][e];
+        const float lo = p.c_scale ? __fmul_rn(acc[i + 2][e], cs) : acc[i + 2][e];
+        if (m < mrows && n < p.N) ((float*)p.C)[batch * p.sC + (int64_t)(m0 + m) * p.ldc + n] = __fadd_rn(hi, lo);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -917,7 +940,7 @@ void launch_rows(const GemmArgs& a, const Plan& pl, dim3 grid, size_t lds, hipSt
 template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   if (pl.kind == 4) {
-    dim3 grid(a.batch, pl.tiles, cdiv(a.M, 64));
+    dim3 grid(a.batch, pl.tiles, a.pair_rows > 0 ? cdiv(a.pair_rows, 32) : cdiv(a.M, 64));
     if (pl.nw == 8) {
       if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 8, TAG>), grid, dim3(512), 0, s, a);
       else hipLaunchKernelGGL((gemm_head_kernel<16, 8, TAG>), grid, dim3(512), 0, s, a);
@@ -999,9 +1022,15 @@ hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s)
   return hipGetLastError();
 }
 
+bool gemm_bf16_pairs(const GemmArgs& a) {
+  return a.M == 2 * a.pair_rows && a.epi == EPI_F32 &&
+         plan_gemm(a.M, a.N, a.K, a.batch, a.ysplit_max, rows_ok(a)).kind == 4;
+}
+
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 128 != 0) return hipErrorInvalidValue;
+  if (a.pair_rows > 0 && !gemm_bf16_pairs(a)) return hipErrorInvalidValue;  // only the per-head kernel pairs rows
   const Plan pl = plan_gemm(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, rows_ok(a));
   if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
   switch (a.tag) {

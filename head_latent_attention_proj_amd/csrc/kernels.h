@@ -50,6 +50,11 @@ struct GemmArgs {
   // (batch 1; the decoder block's residual connection fused into o_proj)
   const uint16_t* resid = nullptr;
   int64_t ldr = 0;
+  // Per-head kernel, EPI_F32 only: rows pair_rows .. 2 pair_rows - 1 of A are the residual parts of
+  // rows 0 .. pair_rows - 1, and output row m (< pair_rows) is the sum of the two rows' products,
+  // each multiplied by its c_scale first (high part + residual part, rounded as separate float32
+  // operations). 0: off.
+  int pair_rows = 0;
   // split-K scratch (workspace): fp32 partials, summed by a fixed-order reduction kernel
   float* part = nullptr;
   int64_t part_cap = 0;     // floats available in `part`
@@ -125,6 +130,9 @@ hipError_t norm_rope_append(const NormArgs& a, hipStream_t s);
 // x = q_hat is built from na.cqkv in every workgroup, and the cache entries are written as
 // norm_rope_append would. gemm_bf16_fuses_qnorm() tells whether the shape takes this path.
 bool gemm_bf16_fuses_qnorm(const GemmArgs& a);
+// Whether gemm_bf16 can take these arguments with a.pair_rows set (M = 2 pair_rows, EPI_F32, the
+// per-head kernel's shapes); with pair_rows set on any other shape gemm_bf16 refuses the call.
+bool gemm_bf16_pairs(const GemmArgs& a);
 hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s);
 
 // Byte copy of n ready-made entries to positions pos0 .. pos0 + n - 1 of sequence seq (slots from
@@ -166,7 +174,7 @@ hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 // ---------------------------------------------------------------------------------------------
 struct DecodeAttnArgs {
   const void* q_lat;       // [B][64][512] q_nope absorbed through W_UK (bf16; FP8 mode: float32)
-  int64_t q_lat_lo;        // FP8 mode: q_lat is the sum of two float32 arrays, this many floats apart
+  int64_t q_lat_lo;        // FP8 mode, when not 0: q_lat is the sum of two float32 arrays, this many floats apart
   const void* q;           // [B][64][192] q (bf16; FP8 mode: float32): rotary part rotated on load
   const uint8_t* cache;
   int entry_bytes;

@@ -789,8 +789,9 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   if (fp8 || !mla_k::gemm_bf16_fuses_qnorm(g)) HIP_TRY(run_proj(ctx, g, s));
   // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched). FP8: W_UK as its exact code
   //    values with the block scale of (head, latent block) on the output; q_nope is float32 and
-  //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out, and
-  //    the attention kernel adds the two products.
+  //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out. The
+  //    per-head kernel (up to 128 sequences) adds the two products in its epilogue; otherwise the
+  //    attention kernel adds them when it loads the query.
   g = gemm_common(w, L);
   if (fp8) {
     HIP_TRY(mla_k::split_q_nope((const float*)(w + L.q), B, (uint16_t*)(w + L.qs), s));
@@ -803,10 +804,16 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   g.B = ctx->w_ukT; g.ldb = NOPE; g.sB = (int64_t)KV_LORA * NOPE;
   g.C = w + L.q_lat; g.ldc = HEADS * KV_LORA; g.sC = KV_LORA; g.N = KV_LORA; g.K = NOPE; g.batch = HEADS;
   g.tag = mla_k::TAG_ABSORB;
+  bool absorb_paired = false;
+  if (fp8) {
+    g.pair_rows = B;
+    absorb_paired = mla_k::gemm_bf16_pairs(g);
+    if (!absorb_paired) g.pair_rows = 0;
+  }
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 5. split attention over the latent cache and its merge -> o_lat
   mla_k::DecodeAttnArgs da{};
-  da.q_lat = w + L.q_lat; da.q_lat_lo = (int64_t)B * HEADS * KV_LORA; da.q = w + L.q;
+  da.q_lat = w + L.q_lat; da.q_lat_lo = (fp8 && !absorb_paired) ? (int64_t)B * HEADS * KV_LORA : 0; da.q = w + L.q;
   da.cache = (const uint8_t*)cache->data;
   da.entry_bytes = eb; da.fp8 = fp8; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
   da.seq_ids = seq_ids_d; da.map = slot_map(cache); da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;

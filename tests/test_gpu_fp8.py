@@ -99,6 +99,32 @@ def test_fp8_decode_matches_w8a8_oracle():
         assert_close(y[s:s + 1], ref["y"], f"seq {s} (L={n})")
 
 
+def test_fp8_decode_130_sequences():
+    """More sequences than the per-head absorb kernel pairs (it adds the query's two absorbed
+    products itself for up to 128): here the attention kernel adds them."""
+    import torch
+
+    B = 130
+    lens = [(7 * s) % 41 for s in range(B)]
+    log(f"fp8 decode B={B}, lengths 0..40")
+    wq, w64, L = fp8_setup()
+    cache = binding.Cache(L, [n + 1 for n in lens])
+    lat = {}
+    for s, n in enumerate(lens):
+        if n:
+            e = synth.bf16_bits_to_f64(synth.make_cache_entries(n, seed=5300 + s))
+            raw, c_dq = pack_fp8_entries(e[:, :512], e[:, 512:])
+            lat[s] = (c_dq, e[:, 512:].astype(np.float32).astype(np.float64))
+            L.cache_append(cache, s, torch.from_numpy(raw).cuda())
+    xn = synth.make_hidden(B, seed=5310)
+    y = y_of(L.decode(cache, np.arange(B), binding.bf16_tensor(xn)))
+    torch.cuda.synchronize()
+    for s in (0, 1, 64, 127, 128, 129):
+        kw = {"cache": lat[s]} if lens[s] else {}
+        ref = omla.forward(synth.bf16_bits_to_f64(xn[s:s + 1]), w64, w8a8=True, **kw)
+        assert_close(y[s:s + 1], ref["y"], f"seq {s} (L={lens[s]})")
+
+
 def test_fp8_prefill_then_decode():
     import torch
 
