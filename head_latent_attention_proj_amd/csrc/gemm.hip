@@ -625,6 +625,48 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       acc[i] = mfma_bf16_16x16x32(as_bf16x8(ld16(xs + (16 * i + l16) * LDX + 32 * ks + 8 * g)), as_bf16x8(wb[ks]), acc[i]);
+  if constexpr (NWV == 8) {
+  if (pair && p.q8_codes) {
+    // the row's 128 features (8 waves x 16 columns) are one quantisation group: v = high +
+    // residual (one float32 addition), s = amax / 448 (1 for an all-zero group), code =
+    // RNE-saturating E4M3 of v / s, as the row quantiser computes them
+    __shared__ float red[NWV][32];
+    float v[2][4], mx[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][e] = __fadd_rn(acc[i][e], acc[i + 2][e]);
+        float a = fabsf(v[i][e]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+        mx[i][e] = a;
+      }
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][16 * i + 4 * g + e] = mx[i][e];
+    }
+    __syncthreads();
+    const int col = wave * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * i + 4 * g + e;
+        float amax = red[0][m];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) amax = fmaxf(amax, red[w][m]);
+        const float sc = amax == 0.f ? 1.0f : amax / 448.0f;
+        if (m < mrows) {
+          p.q8_codes[(int64_t)(m0 + m) * p.q8_ld + batch * 128 + col] = (uint8_t)e4m3_rne_sat(v[i][e] / sc);
+          if (wave == 0 && l16 == 0) p.q8_scales[(int64_t)(m0 + m) * p.q8_sld + batch] = sc;
+        }
+      }
+    return;
+  }
+  }
   if (pair) {
     // high part (tile rows 0..31) plus residual part (rows 32..63), each scaled, as two float32
     // roundings and one float32 addition (no fused multiply-add)
@@ -941,7 +983,11 @@ template <int TAG>
 void launch_tagged(const GemmArgs& a, const Plan& pl, hipStream_t s) {
   if (pl.kind == 4) {
     dim3 grid(a.batch, pl.tiles, a.pair_rows > 0 ? cdiv(a.pair_rows, 32) : cdiv(a.M, 64));
-    if (pl.nw == 8) {
+    if (a.pair_rows > 0 && a.q8_codes) {  // the quantiser epilogue: all 128 columns in one workgroup
+      grid.y = 1;
+      if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 8, TAG>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gemm_head_kernel<16, 8, TAG>), grid, dim3(512), 0, s, a);
+    } else if (pl.nw == 8) {
       if (a.K == 128) hipLaunchKernelGGL((gemm_head_kernel<4, 8, TAG>), grid, dim3(512), 0, s, a);
       else hipLaunchKernelGGL((gemm_head_kernel<16, 8, TAG>), grid, dim3(512), 0, s, a);
     } else {
@@ -1023,7 +1069,7 @@ hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s)
 }
 
 bool gemm_bf16_pairs(const GemmArgs& a) {
-  return a.M == 2 * a.pair_rows && a.epi == EPI_F32 &&
+  return a.M == 2 * a.pair_rows && a.epi == EPI_F32 && (!a.q8_codes || (a.N == 128 && !a.c_scale)) &&
          plan_gemm(a.M, a.N, a.K, a.batch, a.ysplit_max, rows_ok(a)).kind == 4;
 }
 

@@ -55,6 +55,12 @@ struct GemmArgs {
   // each multiplied by its c_scale first (high part + residual part, rounded as separate float32
   // operations). 0: off.
   int pair_rows = 0;
+  // With pair_rows and N = 128 (W_UV: one head's 128 features = one quantisation group per row):
+  // instead of the float32 sums, the FP8 activation quantiser's codes (row stride q8_ld bytes, at
+  // column batch * 128) and scales (row stride q8_sld floats, at index batch) of each row.
+  uint8_t* q8_codes = nullptr;
+  float* q8_scales = nullptr;
+  int64_t q8_ld = 0, q8_sld = 0;
   // split-K scratch (workspace): fp32 partials, summed by a fixed-order reduction kernel
   float* part = nullptr;
   int64_t part_cap = 0;     // floats available in `part`

@@ -827,7 +827,8 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   HIP_TRY(mla_k::decode_attention_merge(da, s));
   // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (already
   //    scaled by the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the
-  //    exact code values, two float32 products that the quantiser adds.
+  //    exact code values, two float32 products that are added before o_proj's input quantiser.
+  bool uv_quantised = false;
   if (!fuse_uv) {
     g = gemm_common(w, L);
     g.A = w + L.o_lat; g.lda = HEADS * KV_LORA; g.sA = KV_LORA;
@@ -835,13 +836,20 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.ldc = O_IN; g.sC = VD; g.tag = mla_k::TAG_UV;
     if (fp8) {
       g.M = 2 * B; g.C = w + L.o32; g.epi = mla_k::EPI_F32;
+      // up to 128 sequences the per-head kernel adds the two products and applies o_proj's input
+      // quantiser itself (a head's 128 features are one quantisation group)
+      g.pair_rows = B; g.q8_codes = w + L.o8; g.q8_scales = (float*)(w + L.o8s); g.q8_ld = O_IN; g.q8_sld = O_IN / 128;
+      uv_quantised = mla_k::gemm_bf16_pairs(g);
+      if (!uv_quantised) {
+        g.pair_rows = 0; g.q8_codes = nullptr; g.q8_scales = nullptr;
+      }
     } else {
       g.M = B; g.C = w + L.o; g.epi = mla_k::EPI_BF16;
     }
     HIP_TRY(mla_k::gemm_bf16(g, s));
   }
   // 7. o_proj
-  if (fp8)
+  if (fp8 && !uv_quantised)
     HIP_TRY(mla_k::quantize_rows_f32((const float*)(w + L.o32), (const float*)(w + L.o32) + (int64_t)B * O_IN, O_IN,
                                      B, O_IN, w + L.o8, (float*)(w + L.o8s), s));
   g = gemm_common(w, L);
