@@ -605,10 +605,33 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
     constexpr int NT = 64 * NWV;
     constexpr int PER = 64 * CH / NT;       // chunks per thread
     u32x4_t xv[PER];
+    if (pair && p.a_f32_split) {
+      // both rows of a pair from the token's float32 values: high = bf16(v), residual = bf16(v - high)
+      const float* Af = (const float*)p.A + batch * p.sA + (int64_t)m0 * p.lda;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + NT * i, row = c / CH, ch = c % CH;
-      xv[i] = ld16(A + arow(row) * p.lda + ch * 8);
+      for (int i = 0; i < PER; ++i) {
+        const int c = tid + NT * i, row = c / CH, ch = c % CH;
+        const float* src = Af + (int64_t)min(row & 31, mrows - 1) * p.lda + ch * 8;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(src), v1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint16_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
+          if (row >= 32) {
+            h0 = f2bf(v[2 * j] - bf2f(h0));
+            h1 = f2bf(v[2 * j + 1] - bf2f(h1));
+          }
+          w[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        }
+        xv[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = tid + NT * i, row = c / CH, ch = c % CH;
+        xv[i] = ld16(A + arow(row) * p.lda + ch * 8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {

@@ -58,6 +58,9 @@ struct GemmArgs {
   // With pair_rows and N = 128 (W_UV: one head's 128 features = one quantisation group per row):
   // instead of the float32 sums, the FP8 activation quantiser's codes (row stride q8_ld bytes, at
   // column batch * 128) and scales (row stride q8_sld floats, at index batch) of each row.
+  // With pair_rows: A is float32 (lda, sA in floats) and the kernel forms each pair itself, the
+  // bf16 high part bf16(v) and the residual bf16(v - high) of row m (< pair_rows).
+  bool a_f32_split = false;
   uint8_t* q8_codes = nullptr;
   float* q8_scales = nullptr;
   int64_t q8_ld = 0, q8_sld = 0;

@@ -790,12 +790,11 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   // 4. absorb: q_lat[b,h,:] = q_nope[b,h,:] W_UK,h  (per-head batched). FP8: W_UK as its exact code
   //    values with the block scale of (head, latent block) on the output; q_nope is float32 and
   //    goes in as bf16 high parts (rows 0..B-1) and residuals (rows B..2B-1), float32 out. The
-  //    per-head kernel (up to 128 sequences) adds the two products in its epilogue; otherwise the
-  //    attention kernel adds them when it loads the query.
+  //    per-head kernel (up to 128 sequences) forms the two parts while staging q_nope and adds the
+  //    two products in its epilogue; otherwise the attention kernel adds them when it loads the query.
   g = gemm_common(w, L);
   if (fp8) {
-    HIP_TRY(mla_k::split_q_nope((const float*)(w + L.q), B, (uint16_t*)(w + L.qs), s));
-    g.A = w + L.qs; g.lda = HEADS * NOPE; g.sA = NOPE; g.M = 2 * B; g.epi = mla_k::EPI_F32;
+    g.M = 2 * B; g.epi = mla_k::EPI_F32;
     g.c_scale = ctx->s_kvb;  // kv_b block (2h, c/128) scales W_UK,h
     g.cs_stride = 2 * (KV_LORA / 128);
   } else {
@@ -806,9 +805,15 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   g.tag = mla_k::TAG_ABSORB;
   bool absorb_paired = false;
   if (fp8) {
-    g.pair_rows = B;
+    // paired: the kernel splits q_nope (float32, in q) into high and residual rows while staging
+    g.pair_rows = B; g.a_f32_split = true;
+    g.A = w + L.q; g.lda = QB_N; g.sA = QK;
     absorb_paired = mla_k::gemm_bf16_pairs(g);
-    if (!absorb_paired) g.pair_rows = 0;
+    if (!absorb_paired) {
+      g.pair_rows = 0; g.a_f32_split = false;
+      HIP_TRY(mla_k::split_q_nope((const float*)(w + L.q), B, (uint16_t*)(w + L.qs), s));
+      g.A = w + L.qs; g.lda = HEADS * NOPE; g.sA = NOPE;
+    }
   }
   HIP_TRY(mla_k::gemm_bf16(g, s));
   // 5. split attention over the latent cache and its merge -> o_lat
