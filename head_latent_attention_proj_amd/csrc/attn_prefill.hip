@@ -32,9 +32,9 @@ constexpr float LOG2E = 1.4426950408889634f;
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 MLA_DEV void st8(void* p, const u32x2_t& v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
-// SPLIT (FP8 weights): q and k_pe arrive in float32, K_nope and V^T in fp16 with an fp16 residual
-// plane of V^T. Queries and keys are rounded to fp16 (11 significant bits) and the probabilities
-// too; each score is one fp16 product, each value product two (value and its residual), so the
+// SPLIT (FP8 weights): q arrives in fp16 (q_b's output; the rotary part is rotated here from the fp16
+// values and rounded again), k_pe in float32, K_nope and V^T in fp16 with an fp16 residual plane of
+// V^T. Keys are rounded to fp16 (11 significant bits) and the probabilities too; each score is one fp16 product, each value product two (value and its residual), so the
 // values enter at about 22 bits. Chosen from a CPU emulation of these roundings against the W8A8
 // float64 layer (the FP8 path's o_proj quantiser amplifies any rounding of its input): bf16
 // hi + lo parts on every operand (three products each way) gave 8.0e-3 max-abs on the layer
@@ -86,27 +86,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
       float x[8];
-      if constexpr (SPLIT) {
-        const float* qf32 = (const float*)a.q + qoff + ks * 32 + g * 8;
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qf32), v1 = *reinterpret_cast<const f32x4_t*>(qf32 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[j] = v0[j];
-          x[4 + j] = v1[j];
-        }
-      } else {
-        const u32x4_t raw = ld16((const uint16_t*)a.q + qoff + ks * 32 + g * 8);
-        if (ks < 4) {
-          qf[qt][ks] = as_frag(raw);
-          continue;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[2 * j] = bf_lo(raw[j]);
-          x[2 * j + 1] = bf_hi(raw[j]);
-        }
+      const u32x4_t raw = ld16((const uint16_t*)a.q + qoff + ks * 32 + g * 8);
+      if (ks < 4) {
+        qf[qt][ks] = as_frag(raw);
+        continue;
       }
-      if (ks >= 4) {  // rotary part, rotated at the query's position
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = SPLIT ? f16_lo(raw[j]) : bf_lo(raw[j]);
+        x[2 * j + 1] = SPLIT ? f16_hi(raw[j]) : bf_hi(raw[j]);
+      }
+      {  // rotary part, rotated at the query's position
         const int pair0 = ((ks - 4) * 32 + g * 8) >> 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -59,6 +59,8 @@ MLA_DEV i32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
 MLA_DEV void epi_store8(const GemmArgs& p, int b, int m, int n, float v) {
   if (p.epi == EPI_F32) {
     ((float*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = v;
+  } else if (p.epi == EPI_F16) {
+    ((uint16_t*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = (uint16_t)pack_f16x2(v, 0.f);
   } else if (p.epi == EPI_BF16) {
     if (p.resid) v += bf2f(p.resid[(int64_t)m * p.ldr + n]);
     ((uint16_t*)p.C)[b * p.sC + (int64_t)m * p.ldc + n] = f2bf(v);
@@ -535,7 +537,7 @@ MLA_DEV void ring8_operands(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, 
 }
 
 // Requirements (checked by ring8_ok): K a multiple of 128, 16-byte aligned operand rows, and
-// EPI_F32 or EPI_BF16 with 16-byte aligned C, ldc and N multiples of 8 (bf16) or 4 (f32), for a
+// EPI_F32, EPI_BF16 or EPI_F16 with 16-byte aligned C, ldc and N multiples of 8 (bf16, fp16) or 4 (f32), for a
 // residual 16-byte alignment and ldr a multiple of 8; or EPI_KVB (batch 1) with key_base and vt_ld
 // multiples of 4, N of 8, K_nope 16-byte and V^T planes 8-byte aligned.
 // BN = 256 (prefill sizes: 8 waves, one workgroup per CU), 128 (4 waves, one per CU) or 64 (2 waves,
@@ -780,7 +782,22 @@ __global__ __launch_bounds__(BN / 32 * 64) void gemm_fp8_ring_kernel(GemmArgs p,
 #pragma unroll
       for (int e = 0; e < 4; ++e) sw[(i * 16 + g * 4 + e) * LDW + j * 16 + l16] = acc[i][j][e];
   __syncthreads();
-  if (p.epi == EPI_BF16) {
+  if (p.epi == EPI_F16) {
+    const int lr = lane >> 3, lc = (lane & 7) * 8;
+    const int n = nw + lc;
+    if (n < p.N) {
+      uint16_t* cb = (uint16_t*)p.C + batch * p.sC + n;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = k * 8 + lr, m = mw + r;
+        if (m >= p.M) continue;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(sw + r * LDW + lc + 4);
+        st16(cb + (int64_t)m * p.ldc, u32x4_t{pack_f16x2(v0[0], v0[1]), pack_f16x2(v0[2], v0[3]),
+                                              pack_f16x2(v1[0], v1[1]), pack_f16x2(v1[2], v1[3])});
+      }
+    }
+  } else if (p.epi == EPI_BF16) {
     const int lr = lane >> 3, lc = (lane & 7) * 8;
     const int n = nw + lc;
     if (n < p.N) {
@@ -908,6 +925,7 @@ bool ring8_ok(const GemmArgs& a) {
     return false;
   if (a.epi == EPI_BF16)
     return (a.N & 7) == 0 && (a.ldc & 7) == 0 && (a.sC & 7) == 0 && (!a.resid || (al16(a.resid) && (a.ldr & 7) == 0));
+  if (a.epi == EPI_F16) return (a.N & 7) == 0 && (a.ldc & 7) == 0 && (a.sC & 7) == 0;
   if (a.epi == EPI_KVB) {
     auto al8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; };
     return a.batch == 1 && (a.key_base & 3) == 0 && (a.vt_ld & 3) == 0 && (a.N & 7) == 0 && al16(a.knope) &&

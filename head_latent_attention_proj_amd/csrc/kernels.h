@@ -16,6 +16,7 @@ enum Epilogue : int {
   EPI_KVB = 2,   // kv_b output split per head: content keys -> knope[key][h*128+d] (bf16),
                  // values -> vt[(h*128+d) * vt_ld + key] (bf16, key-contiguous for P.V);
                  // FP8 kernels write fp16 there instead (see vt_lo)
+  EPI_F16 = 3,   // C fp16 (FP8 kernels only: q_b's output at prefill, the attention's fp16 operand)
 };
 
 // Stage tags: one kernel symbol per projection so traces attribute time per stage.
@@ -153,12 +154,12 @@ hipError_t cache_copy_append(uint8_t* cache, const SlotMap& map, const uint8_t* 
 // Prefill attention (rebuilt keys/values, causal): o[row][h*128+d] bf16
 // ---------------------------------------------------------------------------------------------
 struct PrefillAttnArgs {
-  const void* q;           // [n_tok][64][192] bf16 (split: float32), rotary part not yet rotated
+  const void* q;           // [n_tok][64][192] bf16 (split: fp16), rotary part not yet rotated
   const uint16_t* knope;   // [keys][64][128] bf16 (split: fp16)
   const uint16_t* vt;      // [64*128][vt_ld] bf16 (split: fp16)
   int64_t vt_ld;
-  // split precision (FP8 weights): q is float32, k_pe float32 in the entry; queries and keys are
-  // rounded to fp16 and the values carry an fp16 residual plane vt_lo next to vt
+  // split precision (FP8 weights): q is fp16, k_pe float32 in the entry; queries and keys enter as
+  // fp16 and the values carry an fp16 residual plane vt_lo next to vt
   int split;
   const uint16_t* vt_lo;
   const uint8_t* cache;    // for the rotated shared key k_pe of each position

@@ -266,7 +266,7 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
   };
   L.cqkv = take((size_t)ntok * QKVA_N * 4 * qkva_parts_max(ntok));
   L.q_hat = take((size_t)ntok * Q_LORA * 2);  // bf16, or FP8 codes
-  L.q = take((size_t)ntok * QB_N * (fp8 ? 4 : 2));  // FP8: float32 q
+  L.q = take((size_t)ntok * QB_N * (fp8 && decode_splits > 0 ? 4 : 2));  // FP8 decode: float32 q; prefill fp16
   L.o = take((size_t)ntok * O_IN * 2);
   L.meta = take((size_t)nbatch * sizeof(mla_k::SeqMeta));
   L.vt_ld = round_up(nkeys, 64);
@@ -661,7 +661,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   set_a(ctx, g, w + L.q_hat, Q_LORA, w + L.q_hat, (const float*)(w + L.qh8s), Q_LORA / 128);
   g.B = ctx->w_qb; g.ldb = Q_LORA; g.b_scale = ctx->s_qb; g.bs_ld = Q_LORA / 128;
   g.C = w + L.q; g.ldc = QB_N; g.M = ntok; g.N = QB_N; g.K = Q_LORA; g.tag = mla_k::TAG_QB;
-  g.epi = fp8 ? mla_k::EPI_F32 : mla_k::EPI_BF16;
+  g.epi = fp8 ? mla_k::EPI_F16 : mla_k::EPI_BF16;  // FP8: fp16, the attention's operand precision
   HIP_TRY(run_proj(ctx, g, s));
   // 4. kv_b on every latent entry of each sequence (cached prefix + new): content keys, values.
   //    Paged cache: the sequences' entries are gathered into contiguous rows first (kv_b's rows and
