@@ -30,13 +30,21 @@ def deq_rows(codes, scales):
     return ofp8.dequant_1x128(codes, scales)
 
 
+def weight(wq, name):
+    """codes and block scales of one projection; "qkva" is q_a and kv_a stacked as the layer fuses
+    them (N = 2112: the last 128-row scale block and, at 256-column tiles, the last tile partial)"""
+    if name == "qkva":
+        return np.vstack([wq["q_a"], wq["kv_a"]]), np.vstack([wq["q_a_s"], wq["kv_a_s"]])
+    return wq[name], wq[name + "_s"]
+
+
 @pytest.mark.parametrize("name,M", [("q_a", 200), ("q_b", 129), ("kv_b", 300), ("o", 96), ("q_b", 1100), ("o", 1030),
-                                    ("kv_b", 1100), ("q_a", 5600)])
+                                    ("kv_b", 1100), ("q_a", 5600), ("qkva", 200), ("qkva", 4100)])
 def test_fp8_gemm_forms_against_float64(name, M):
     import torch
 
     wq = synth.make_weights_fp8(seed=0)
-    b_codes, b_scales = wq[name], wq[name + "_s"]
+    b_codes, b_scales = weight(wq, name)
     N, K = b_codes.shape
     rng = np.random.default_rng(7100 + M)
     a_codes, a_scales = ofp8.quantize_1x128(rng.standard_normal((M, K)))
