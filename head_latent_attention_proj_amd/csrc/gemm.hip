@@ -7,16 +7,19 @@
 //
 // Kernels:
 //   * gemm_tile   -- prefill-sized M: BM x BN workgroup tile staged through LDS (double
-//                    buffered, padded rows so 16-byte fragment reads are bank-conflict free),
-//                    16x16x32 bf16 MFMA, XCD-aware grouped tile order. Optional split-K.
-//   * gemm_skinny -- 16 < M <= 64 with K >= 512: a ring of LDS stages filled by direct-to-LDS
-//                    loads in MFMA operand order, several stages in flight per workgroup.
+//                    buffered, XOR-swizzled 128-byte rows so stores and 16-byte fragment reads
+//                    are bank-conflict free), 16x16x32 bf16 MFMA, XCD-aware grouped tile order.
+//                    Optional split-K.
+//   * gemm_skinny -- 16 < M <= 64 with K >= 512: a ring of LDS stages filled by whole-row
+//                    direct-to-LDS loads into swizzled rows, several stages in flight per workgroup.
 //   * gemm_wsplit -- other decode-sized M (<= 64): operands go straight from global memory into
 //                    MFMA fragments; the K range of a 16*NT-column tile is split across the waves
 //                    of one workgroup (each wave streams its own contiguous slice of the weight
 //                    rows), and the waves' partial tiles are summed through LDS in a fixed order.
 //                    No cross-workgroup synchronisation, no float atomics: deterministic.
-//   * gemm_head   -- per-head batched products at M <= 64 with K of 128 or 512.
+//   * gemm_head   -- per-head batched products up to 256 rows with K of 128 or 512 (optionally
+//                    paired high / residual rows summed in the epilogue, with o_proj's FP8
+//                    input quantiser applied there).
 //   * gemm_rows   -- one or two rows of A: each load of a wave reads 1 KB (or 256 B) runs of
 //                    single weight rows, dot products on the VALU with x staged in LDS.
 //   Split-K of the tile kernel (few tiles, small M) writes fp32 partials and a separate

@@ -487,17 +487,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 }
 
 // ------------------------------------------------------------------------------------------
-// Prefill-sized M, native form: K groups streamed through a ring of LDS stages
+// K groups streamed through a ring of LDS stages (both forms; prefill and decode sizes)
 // ------------------------------------------------------------------------------------------
-// 128 x 256 output tile, 8 waves of 64 x 64 (2 x 4). A stage is one K group: the A tile as 8 and
-// the B tile as 16 blocks of 16 rows x 128 codes, and the tile's 128 A scales. Every piece is
-// fetched by direct-to-LDS loads, which hold no registers: two stages are in flight while the
-// third is multiplied (the register-staged tile kernel has one stage of compute to cover each
-// load). One wave instruction fetches 8 whole rows of a block (lane l: row l / 8, one 16-byte
-// chunk), so it touches 8 cache lines; a block lands row-major, chunk c of row r at position
-// c ^ ((r / 2) % 8): a lane's operand halves (row l16, chunks 2g and 2g + 1) are then read with
-// the 16 lanes of one g on distinct banks. The row scales are fetched by one wave per 64 rows.
-// Three stages of 48.5 KB: one workgroup per CU.
+// 128 x BN output tile (BN = 256, 128 or 64), waves of 64 x 64 (2 x BN/64). A stage is one K
+// group: the A tile as 8 and the B tile as BN/16 blocks of 16 rows x 128 codes, and the tile's
+// 128 A scales. Every piece is fetched by direct-to-LDS loads, which hold no registers: two stages
+// are in flight while the third is multiplied (the register-staged tile kernel has one stage of
+// compute to cover each load). One wave instruction fetches 8 whole rows of a block (lane l: row
+// l / 8, one 16-byte chunk), so it touches 8 cache lines; a block lands row-major, chunk c of row r
+// at position c ^ ((r / 2) % 8): a lane's operand halves (row l16, chunks 2g and 2g + 1) are then
+// read with the 16 lanes of one g on distinct banks. The row scales are fetched by one wave per 64
+// rows. Three stages of 48.5 KB at BN = 256 (one workgroup per CU), 24.5 KB at BN = 64 (two).
 namespace ring8 {
 constexpr int BM = 128, S = 3;
 constexpr int A_BYTES = BM * 128;
