@@ -19,6 +19,10 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary vector registers: the FP8 GEMMs scale each K group's sums
+    # with plain FMAs instead of first copying them out of accumulation registers (decode-sized
+    # o_proj 28.2 -> 26.6 us, q_b 13.5 -> 12.3 us)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
