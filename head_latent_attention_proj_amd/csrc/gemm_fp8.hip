@@ -858,7 +858,7 @@ bool tag_precise(int tag) { return tag == TAG_QKVA || tag == TAG_KVB; }
 
 // prec: the precise form keeps 128 x 128 tiles (two accumulator sets per lane do not fit the
 // 128 x 256 tile's registers)
-Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
+Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec, int parts_max) {
   Plan8 pl{};
   pl.splits = 1;
   pl.ksplit = K;
@@ -899,7 +899,16 @@ Plan8 plan_fp8(int M, int N, int K, int batch, int ysplit_max, bool prec) {
   const int per = cdiv(ngroups, splits);
   pl.ksplit = per * 128;
   pl.splits = cdiv(ngroups, per);
+  // a consumer that adds up to parts_max parts takes the split partials straight from C: no
+  // reduction launch (the sums are the reduction's: parts added in split order)
+  if (pl.splits > 1 && pl.splits <= parts_max) pl.ysplit = pl.splits;
   return pl;
+}
+
+// The parts a call's consumer adds, for the K-split tile kernels: float32 output of one batch with
+// its parts packed (C rows N floats apart, parts M N floats apart); otherwise none.
+int parts_max_of(const GemmArgs& a) {
+  return a.epi == EPI_F32 && a.batch == 1 && a.ldc == a.N && a.c_split_stride == (int64_t)a.M * a.N ? a.ysplit_max : 1;
 }
 
 template <int MT, int TAG, bool PREC>
@@ -979,7 +988,7 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
   else if constexpr (!PREC)
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 256, 2, 4, TAG, PREC>), grid, dim3(512), 0, s, a, pl.splits,
                        pl.ksplit);
-  if (pl.splits > 1) {
+  if (pl.splits > 1 && pl.ysplit == 1) {
     dim3 rgrid((unsigned)(((int64_t)a.M * a.N + 255) / 256), a.batch);
     hipLaunchKernelGGL((splitk_reduce8_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
   }
@@ -990,28 +999,32 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
 int64_t gemm_fp8_part_floats(int M, int N, int K, int batch) {
   int64_t mx = 0;
   for (bool prec : {false, true}) {
-    const Plan8 pl = plan_fp8(M, N, K, batch, 1, prec);
+    const Plan8 pl = plan_fp8(M, N, K, batch, 1, prec, 1);
     if (pl.splits > 1) mx = std::max(mx, (int64_t)pl.splits * batch * M * N);
   }
   return mx;
 }
 
 int gemm_fp8_ysplit(const GemmArgs& a) {
-  return plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag)).ysplit;
+  return plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag), parts_max_of(a)).ysplit;
 }
 
 hipError_t gemm_fp8(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 128 != 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
-  const Plan8 pl = plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag));
-  if (pl.splits > 1 && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
+  const Plan8 pl =
+      plan_fp8(a.M, a.N, a.K, a.batch, a.epi == EPI_F32 ? a.ysplit_max : 1, tag_precise(a.tag), parts_max_of(a));
+  const bool parts_in_c = pl.kind != 0 && pl.ysplit > 1;
+  if (pl.splits > 1 && !parts_in_c && (int64_t)pl.splits * a.batch * a.M * a.N > a.part_cap) return hipErrorInvalidValue;
+  GemmArgs b = a;
+  if (parts_in_c) b.part = (float*)a.C;  // split s writes part s of C
   // q_a|kv_a and kv_b: precise; q_b, o_proj (and untagged test calls): native
   switch (a.tag) {
-    case TAG_QKVA: launch_fp8_tagged<TAG_QKVA, true>(a, pl, s); break;
-    case TAG_QB: launch_fp8_tagged<TAG_QB, false>(a, pl, s); break;
-    case TAG_KVB: launch_fp8_tagged<TAG_KVB, true>(a, pl, s); break;
-    case TAG_OPROJ: launch_fp8_tagged<TAG_OPROJ, false>(a, pl, s); break;
-    default: launch_fp8_tagged<TAG_NONE, false>(a, pl, s); break;
+    case TAG_QKVA: launch_fp8_tagged<TAG_QKVA, true>(b, pl, s); break;
+    case TAG_QB: launch_fp8_tagged<TAG_QB, false>(b, pl, s); break;
+    case TAG_KVB: launch_fp8_tagged<TAG_KVB, true>(b, pl, s); break;
+    case TAG_OPROJ: launch_fp8_tagged<TAG_OPROJ, false>(b, pl, s); break;
+    default: launch_fp8_tagged<TAG_NONE, false>(b, pl, s); break;
   }
   return hipGetLastError();
 }

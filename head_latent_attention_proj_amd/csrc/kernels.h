@@ -112,7 +112,7 @@ hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, in
 // and len[seq] is advanced by one after the entry is written.
 struct NormArgs {
   const float* cqkv;     // [n_part][n][2112] partial sums (added here)
-  int n_part;            // 1 .. 4
+  int n_part;            // 1 .. 8
   int64_t part_stride;   // floats between parts
   const uint16_t* g_q;
   const uint16_t* g_kv;

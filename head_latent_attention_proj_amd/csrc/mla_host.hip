@@ -190,10 +190,11 @@ PackedLayout packed_layout(const mla_config* c) {
 }
 
 // ---- workspace planning ----------------------------------------------------------------------
-// K-split parts of the fused q_a|kv_a projection that the norm kernel adds: up to 4 at decode sizes,
-// none above 64 rows (no projection kernel splits K into its consumer's parts there), so a prefill's
-// workspace holds one copy of the sums
-int qkva_parts_max(int ntok) { return ntok <= 64 ? 4 : 1; }
+// K-split parts of the fused q_a|kv_a projection that the norm kernel adds: up to 4 at decode sizes;
+// with FP8 weights up to 128 rows, 8 (the precise FP8 tile kernel splits K 7 ways at 65 .. 128 rows
+// and then needs no reduction launch); none above (no projection kernel splits K there), so a
+// prefill's workspace holds one copy of the sums
+int qkva_parts_max(int ntok, bool fp8) { return ntok <= 64 ? 4 : (fp8 && ntok <= 128 ? 8 : 1); }
 constexpr int DECODE_MAX_WG = 2048;
 constexpr int MAX_BATCH = 4096;  // sequences per prefill or decode call (MLA_E_UNSUPPORTED above)
 
@@ -264,7 +265,7 @@ WsLayout ws_layout(int ntok, int nbatch, int64_t nkeys, int decode_splits, int64
     off = round_up(off + bytes, 256);
     return o;
   };
-  L.cqkv = take((size_t)ntok * QKVA_N * 4 * qkva_parts_max(ntok));
+  L.cqkv = take((size_t)ntok * QKVA_N * 4 * qkva_parts_max(ntok, fp8));
   L.q_hat = take((size_t)ntok * Q_LORA * 2);  // bf16, or FP8 codes
   L.q = take((size_t)ntok * QB_N * (fp8 && decode_splits > 0 ? 4 : 2));  // FP8 decode: float32 q; prefill fp16
   L.o = take((size_t)ntok * O_IN * 2);
@@ -643,7 +644,7 @@ mla_status prefill_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h
   set_a(ctx, g, x, HIDDEN, w + L.x8, (const float*)(w + L.x8s), HIDDEN / 128);
   g.B = ctx->w_qkva; g.ldb = HIDDEN; g.b_scale = ctx->s_qkva; g.bs_ld = HIDDEN / 128;
   g.C = w + L.cqkv; g.ldc = QKVA_N; g.M = ntok; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
-  g.tag = mla_k::TAG_QKVA; g.ysplit_max = qkva_parts_max(ntok); g.c_split_stride = (int64_t)ntok * QKVA_N;
+  g.tag = mla_k::TAG_QKVA; g.ysplit_max = qkva_parts_max(ntok, ctx->fp8); g.c_split_stride = (int64_t)ntok * QKVA_N;
   const int qkva_parts = proj_ysplit(ctx, g);  // > 1 only at short prefills: the norm kernel adds them
   HIP_TRY(run_proj(ctx, g, s));
   // 2. RMSNorms, RoPE of the shared key, latent entries into the cache (FP8: quantised q_hat, c_hat)
@@ -763,7 +764,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   set_a(ctx, g, x, HIDDEN, w + L.x8, (const float*)(w + L.x8s), HIDDEN / 128);
   g.B = ctx->w_qkva; g.ldb = HIDDEN; g.b_scale = ctx->s_qkva; g.bs_ld = HIDDEN / 128;
   g.C = w + L.cqkv; g.ldc = QKVA_N; g.M = B; g.N = QKVA_N; g.K = HIDDEN; g.epi = mla_k::EPI_F32;
-  g.tag = mla_k::TAG_QKVA; g.ysplit_max = qkva_parts_max(B); g.c_split_stride = (int64_t)B * QKVA_N;
+  g.tag = mla_k::TAG_QKVA; g.ysplit_max = qkva_parts_max(B, ctx->fp8); g.c_split_stride = (int64_t)B * QKVA_N;
   const int qkva_parts = proj_ysplit(ctx, g);
   HIP_TRY(run_proj(ctx, g, s));
   // 2. norms + shared-key RoPE + append at position len; len_d advances by one here

@@ -22,7 +22,8 @@ MLA_DEV float block_sum256(float v, float* red) {
 }
 
 // q_hat of decode token `tok` (the 1536 query-latent features of the fused q_a | kv_a sums,
-// a.n_part parts added in part order) as bf16 into dst[0 .. 1536).
+// a.n_part parts added in part order, at most 4: bf16 weights at one or two tokens) as bf16 into
+// dst[0 .. 1536).
 MLA_DEV void q_norm_bf16(const NormArgs& a, int tok, uint16_t* dst, float* red) {
   using namespace mla_dims;
   const int tid = threadIdx.x;

@@ -46,6 +46,7 @@ __global__ void commit_kernel(const int32_t* seq_ids, const int32_t* q_start, in
 }
 
 // One workgroup (256 threads) per token.
+template <int MAX_PARTS>
 __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   using namespace mla_dims;
   __shared__ float red[4];
@@ -75,7 +76,6 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormArgs a) {
   // Every load of the token's row (all K-split parts, up to MAX_PARTS) is issued before any is
   // used: at decode this kernel is one workgroup per token and runs at load latency. The parts
   // are then added in part order.
-  constexpr int MAX_PARTS = 4;
   float pv[MAX_PARTS][9];
 #pragma unroll
   for (int p = 0; p < MAX_PARTS; ++p) {
@@ -350,7 +350,14 @@ hipError_t commit_lengths(const int32_t* seq_ids_d, const int32_t* q_start_d, in
 
 hipError_t norm_rope_append(const NormArgs& a, hipStream_t s) {
   if (a.n_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(norm_rope_append_kernel, dim3(a.n_tokens), dim3(256), 0, s, a);
+  if (a.n_part < 1 || a.n_part > 8) return hipErrorInvalidValue;
+  // one load per part and element, so the part capacity follows the call's part count
+  if (a.n_part == 1)
+    hipLaunchKernelGGL(norm_rope_append_kernel<1>, dim3(a.n_tokens), dim3(256), 0, s, a);
+  else if (a.n_part <= 4)
+    hipLaunchKernelGGL(norm_rope_append_kernel<4>, dim3(a.n_tokens), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(norm_rope_append_kernel<8>, dim3(a.n_tokens), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

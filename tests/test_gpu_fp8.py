@@ -52,7 +52,7 @@ def unpack_fp8_entries(raw: np.ndarray):
     return ofp8.dequant_1x128(codes, scales), kpe
 
 
-@pytest.mark.parametrize("lens_t", [[64], [300], [50, 129]])
+@pytest.mark.parametrize("lens_t", [[64], [100], [300], [50, 129]])
 def test_fp8_prefill_matches_w8a8_oracle(lens_t):
     import torch
 
@@ -99,12 +99,14 @@ def test_fp8_decode_matches_w8a8_oracle():
         assert_close(y[s:s + 1], ref["y"], f"seq {s} (L={n})")
 
 
-def test_fp8_decode_130_sequences():
-    """More sequences than the per-head absorb kernel pairs (it adds the query's two absorbed
-    products itself for up to 128): here the attention kernel adds them."""
+@pytest.mark.parametrize("B", [100, 130])
+def test_fp8_decode_many_sequences(B):
+    """100 sequences: the q_a|kv_a partial sums of the K-split projection go to the norm kernel as
+    parts (up to 128 rows). 130: more sequences than the per-head absorb kernel pairs (it adds the
+    query's two absorbed products itself for up to 128), so the attention kernel adds them, and the
+    projection's partial sums go through its own reduction."""
     import torch
 
-    B = 130
     lens = [(7 * s) % 41 for s in range(B)]
     log(f"fp8 decode B={B}, lengths 0..40")
     wq, w64, L = fp8_setup()
@@ -119,7 +121,7 @@ def test_fp8_decode_130_sequences():
     xn = synth.make_hidden(B, seed=5310)
     y = y_of(L.decode(cache, np.arange(B), binding.bf16_tensor(xn)))
     torch.cuda.synchronize()
-    for s in (0, 1, 64, 127, 128, 129):
+    for s in (0, 1, 64, B - 3, B - 2, B - 1):
         kw = {"cache": lat[s]} if lens[s] else {}
         ref = omla.forward(synth.bf16_bits_to_f64(xn[s:s + 1]), w64, w8a8=True, **kw)
         assert_close(y[s:s + 1], ref["y"], f"seq {s} (L={lens[s]})")
