@@ -608,7 +608,57 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
     constexpr int NT = 64 * NWV;
     constexpr int PER = 64 * CH / NT;       // chunks per thread
     u32x4_t xv[PER];
-    if (pair && p.a_f32_split) {
+    // both rows of a pair as bf16 high = bf16(v) and residual = bf16(v - high) of a float32 v
+    auto split8 = [&](const float (&v)[8], u32x4_t& hi, u32x4_t& lo) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
+        wh[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        wl[j] = (uint32_t)f2bf(v[2 * j] - bf2f(h0)) | ((uint32_t)f2bf(v[2 * j + 1] - bf2f(h1)) << 16);
+      }
+      hi = u32x4_t{wh[0], wh[1], wh[2], wh[3]};
+      lo = u32x4_t{wl[0], wl[1], wl[2], wl[3]};
+    };
+    bool staged = false;
+    if constexpr (KS == 16 && NWV == 8) {
+      if (pair && p.a_f32_split && p.mg_ml) {
+        // merge the attention splits of row b for this head (batch) while staging: this thread's
+        // chunks i = 0 .. 3 are rows tid / 64 + 8 i (< 32), chunks i + 4 their residual rows
+        static_assert(PER == 8 && CH == 64, "merge staging layout");
+        const float* Po = (const float*)p.A;
+#pragma unroll
+        for (int i = 0; i < PER / 2; ++i) {
+          const int c = tid + NT * i, row = c / CH, ch = c % CH;
+          const int b = m0 + min(row, mrows - 1);
+          const int ns = cdiv(p.mg_len[p.mg_seq[b]], p.mg_chunk);
+          const int64_t q0 = (int64_t)b * p.mg_max_splits * 64 + batch;  // (b, split 0, head)
+          float mx = -INFINITY;
+          for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, p.mg_ml[(q0 + (int64_t)sp * 64) * 2]);
+          float l = 0.f;
+          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+          for (int sp = 0; sp < ns; ++sp) {
+            const int64_t q = q0 + (int64_t)sp * 64;
+            const float w = exp2f(p.mg_ml[q * 2] - mx);
+            l += w * p.mg_ml[q * 2 + 1];
+            const float* src = Po + q * 512 + ch * 8;
+            a0 += *reinterpret_cast<const f32x4_t*>(src) * w;
+            a1 += *reinterpret_cast<const f32x4_t*>(src + 4) * w;
+          }
+          const float inv = 1.0f / l, sc = p.mg_scale[(2 * batch + 1) * 4 + (ch >> 4)];
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = a0[e] * inv * sc;
+            v[4 + e] = a1[e] * inv * sc;
+          }
+          split8(v, xv[i], xv[i + PER / 2]);
+        }
+        staged = true;
+      }
+    }
+    if (staged) {
+    } else if (pair && p.a_f32_split) {
       // both rows of a pair from the token's float32 values: high = bf16(v), residual = bf16(v - high)
       const float* Af = (const float*)p.A + batch * p.sA + (int64_t)m0 * p.lda;
 #pragma unroll
@@ -617,17 +667,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
         const float* src = Af + (int64_t)min(row & 31, mrows - 1) * p.lda + ch * 8;
         const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(src), v1 = *reinterpret_cast<const f32x4_t*>(src + 4);
         const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint16_t h0 = f2bf(v[2 * j]), h1 = f2bf(v[2 * j + 1]);
-          if (row >= 32) {
-            h0 = f2bf(v[2 * j] - bf2f(h0));
-            h1 = f2bf(v[2 * j + 1] - bf2f(h1));
-          }
-          w[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        }
-        xv[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+        u32x4_t hi, lo;
+        split8(v, hi, lo);
+        xv[i] = row >= 32 ? lo : hi;
       }
     } else {
 #pragma unroll
@@ -1096,6 +1138,7 @@ hipError_t gemm_bf16_qnorm(const GemmArgs& a, const NormArgs& na, hipStream_t s)
 
 bool gemm_bf16_pairs(const GemmArgs& a) {
   return a.M == 2 * a.pair_rows && a.epi == EPI_F32 && (!a.q8_codes || (a.N == 128 && !a.c_scale)) &&
+         (!a.mg_ml || (a.a_f32_split && a.q8_codes && a.K == 512 && a.mg_chunk > 0 && a.mg_max_splits > 0)) &&
          plan_gemm(a.M, a.N, a.K, a.batch, a.ysplit_max, rows_ok(a)).kind == 4;
 }
 

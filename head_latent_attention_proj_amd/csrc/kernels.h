@@ -62,6 +62,17 @@ struct GemmArgs {
   // With pair_rows: A is float32 (lda, sA in floats) and the kernel forms each pair itself, the
   // bf16 high part bf16(v) and the residual bf16(v - high) of row m (< pair_rows).
   bool a_f32_split = false;
+  // With a_f32_split and mg_ml (W_UV after the split decode attention; K = 512, N = 128): A is the
+  // attention's partial outputs [b][mg_max_splits][64 heads][512] (unnormalised float32 sums, head
+  // = batch), merged while staging with their (max, sum) pairs mg_ml (same index, log2 units; the
+  // split count of row b is cdiv(mg_len[mg_seq[b]], mg_chunk)) and multiplied by mg_scale[(2 h + 1)
+  // * 4 + k / 128]: row b's value is that scale times sum_s w_s o_s / sum_s w_s l_s, w_s =
+  // 2^(m_s - max_s m_s).
+  const float* mg_ml = nullptr;
+  const int32_t* mg_seq = nullptr;
+  const int32_t* mg_len = nullptr;
+  int mg_chunk = 0, mg_max_splits = 0;
+  const float* mg_scale = nullptr;
   uint8_t* q8_codes = nullptr;
   float* q8_scales = nullptr;
   int64_t q8_ld = 0, q8_sld = 0;

@@ -833,10 +833,12 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     da.w_uv = (const uint16_t*)ctx->w_uv; da.uv_head_stride = ctx->uv_head_stride; da.o = (uint16_t*)(w + L.o);
   }
   PROBED(MLA_STAGE_DECODE_ATTN, mla_k::decode_attention_splits(da, s));
-  HIP_TRY(mla_k::decode_attention_merge(da, s));
-  // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (already
-  //    scaled by the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the
-  //    exact code values, two float32 products that are added before o_proj's input quantiser.
+  // 6. W_UV per head: o[b][h*128 + d] = sum_c W_UV,h[d][c] o_lat[b][h][c]. FP8: o_lat (scaled by
+  //    the blocks' scales) as high rows 0..B-1 and residual rows B..2B-1 against the exact code
+  //    values, two float32 products that are added before o_proj's input quantiser. Up to 128
+  //    sequences the per-head kernel merges the attention's splits itself while staging o_lat,
+  //    forms the two rows, adds the two products and applies o_proj's input quantiser (a head's
+  //    128 features are one quantisation group); otherwise the merge kernel writes o_lat first.
   bool uv_quantised = false;
   if (!fuse_uv) {
     g = gemm_common(w, L);
@@ -845,17 +847,21 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
     g.N = VD; g.K = KV_LORA; g.batch = HEADS; g.ldc = O_IN; g.sC = VD; g.tag = mla_k::TAG_UV;
     if (fp8) {
       g.M = 2 * B; g.C = w + L.o32; g.epi = mla_k::EPI_F32;
-      // up to 128 sequences the per-head kernel adds the two products and applies o_proj's input
-      // quantiser itself (a head's 128 features are one quantisation group)
-      g.pair_rows = B; g.q8_codes = w + L.o8; g.q8_scales = (float*)(w + L.o8s); g.q8_ld = O_IN; g.q8_sld = O_IN / 128;
-      uv_quantised = mla_k::gemm_bf16_pairs(g);
-      if (!uv_quantised) {
-        g.pair_rows = 0; g.q8_codes = nullptr; g.q8_scales = nullptr;
-      }
+      mla_k::GemmArgs gm = g;
+      gm.pair_rows = B; gm.q8_codes = w + L.o8; gm.q8_scales = (float*)(w + L.o8s); gm.q8_ld = O_IN;
+      gm.q8_sld = O_IN / 128;
+      gm.A = da.part_o; gm.lda = KV_LORA; gm.sA = KV_LORA; gm.a_f32_split = true;
+      gm.mg_ml = da.part_ml; gm.mg_seq = seq_ids_d; gm.mg_len = cache->len_d; gm.mg_chunk = da.chunk;
+      gm.mg_max_splits = da.max_splits; gm.mg_scale = ctx->s_kvb;
+      uv_quantised = mla_k::gemm_bf16_pairs(gm);
+      if (uv_quantised) g = gm;
     } else {
       g.M = B; g.C = w + L.o; g.epi = mla_k::EPI_BF16;
     }
+    if (!uv_quantised) HIP_TRY(mla_k::decode_attention_merge(da, s));
     HIP_TRY(mla_k::gemm_bf16(g, s));
+  } else {
+    HIP_TRY(mla_k::decode_attention_merge(da, s));
   }
   // 7. o_proj
   if (fp8 && !uv_quantised)
