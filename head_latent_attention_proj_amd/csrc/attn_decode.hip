@@ -170,6 +170,10 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
     for (int ks = 0; ks < 9; ++ks) {
       const int f = lh * HALF + ks * 32 + g * 8;
       float v[8];
+      if (f < KV_LORA && a.q_lat_f16) {
+        qf[ks] = as_f16x8(ld16((const uint16_t*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f));
+        continue;
+      }
       if (f < KV_LORA) {
         const float* qlf = (const float*)a.q_lat + ((int64_t)b * 64 + head) * KV_LORA + f;
         const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qlf), v1 = *reinterpret_cast<const f32x4_t*>(qlf + 4);

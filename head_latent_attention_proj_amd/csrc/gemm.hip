@@ -747,7 +747,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
         const int m = 16 * i + 4 * g + e;
         const float hi = p.c_scale ? __fmul_rn(acc[i][e], cs) : acc[i][e];
         const float lo = p.c_scale ? __fmul_rn(acc[i + 2][e], cs) : acc[i + 2][e];
-        if (m < mrows && n < p.N) ((float*)p.C)[batch * p.sC + (int64_t)(m0 + m) * p.ldc + n] = __fadd_rn(hi, lo);
+        const int64_t ci = batch * p.sC + (int64_t)(m0 + m) * p.ldc + n;
+        if (m < mrows && n < p.N) {
+          if (p.c_f16) ((_Float16*)p.C)[ci] = (_Float16)__fadd_rn(hi, lo);
+          else ((float*)p.C)[ci] = __fadd_rn(hi, lo);
+        }
       }
     return;
   }

@@ -56,6 +56,9 @@ struct GemmArgs {
   // each multiplied by its c_scale first (high part + residual part, rounded as separate float32
   // operations). 0: off.
   int pair_rows = 0;
+  // With pair_rows, without q8_codes: the sums stored as fp16 (round to nearest even; C in
+  // 16-bit elements) instead of float32
+  bool c_f16 = false;
   // With pair_rows and N = 128 (W_UV: one head's 128 features = one quantisation group per row):
   // instead of the float32 sums, the FP8 activation quantiser's codes (row stride q8_ld bytes, at
   // column batch * 128) and scales (row stride q8_sld floats, at index batch) of each row.
@@ -194,8 +197,9 @@ hipError_t prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 // Decode attention in the latent space, split over positions, then merged
 // ---------------------------------------------------------------------------------------------
 struct DecodeAttnArgs {
-  const void* q_lat;       // [B][64][512] q_nope absorbed through W_UK (bf16; FP8 mode: float32)
+  const void* q_lat;       // [B][64][512] q_nope absorbed through W_UK (bf16; FP8 mode: float32, or fp16)
   int64_t q_lat_lo;        // FP8 mode, when not 0: q_lat is the sum of two float32 arrays, this many floats apart
+  bool q_lat_f16;          // FP8 mode: q_lat holds fp16 values (the attention's query precision)
   const void* q;           // [B][64][192] q (bf16; FP8 mode: float32): rotary part rotated on load
   const uint8_t* cache;
   int entry_bytes;

@@ -810,11 +810,11 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   bool absorb_paired = false;
   if (fp8) {
     // paired: the kernel splits q_nope (float32, in q) into high and residual rows while staging
-    g.pair_rows = B; g.a_f32_split = true;
+    g.pair_rows = B; g.a_f32_split = true; g.c_f16 = true;  // q_lat in the attention's fp16
     g.A = w + L.q; g.lda = QB_N; g.sA = QK;
     absorb_paired = mla_k::gemm_bf16_pairs(g);
     if (!absorb_paired) {
-      g.pair_rows = 0; g.a_f32_split = false;
+      g.pair_rows = 0; g.a_f32_split = false; g.c_f16 = false;
       HIP_TRY(mla_k::split_q_nope((const float*)(w + L.q), B, (uint16_t*)(w + L.qs), s));
       g.A = w + L.qs; g.lda = HEADS * NOPE; g.sA = NOPE;
     }
@@ -823,6 +823,7 @@ mla_status decode_impl(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h,
   // 5. split attention over the latent cache and its merge -> o_lat
   mla_k::DecodeAttnArgs da{};
   da.q_lat = w + L.q_lat; da.q_lat_lo = (fp8 && !absorb_paired) ? (int64_t)B * HEADS * KV_LORA : 0; da.q = w + L.q;
+  da.q_lat_f16 = fp8 && absorb_paired;
   da.cache = (const uint8_t*)cache->data;
   da.entry_bytes = eb; da.fp8 = fp8; da.rope_cs = ctx->rope_cs; da.max_pos = ctx->cfg.max_positions;
   da.seq_ids = seq_ids_d; da.map = slot_map(cache); da.len = cache->len_d; da.B = B; da.chunk = dp.chunk;
