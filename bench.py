@@ -115,7 +115,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the headline's attention launches settle over the first ~40 steps of a fresh process (a kernel
+    # trace shows 825 -> 585 us per launch: the GPU's clocks and power, not the work, change), so the
+    # default warm-up puts the timed steps in the steady state the probed launches are measured in
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--copies", type=int, default=3, help="bf16 layer copies stepped in turn")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
@@ -610,10 +613,11 @@ def cpu_decode_varlen(bits, seconds):
 
 
 def cpu_prefill(wbits, T, seconds, batch=1):
-    """Prefill of T tokens (per sequence; `batch` sequences): the oracle's latent path over all T tokens
-    and its rebuilt keys and values (one call with the last row, timed), then query rows at evenly
-    spaced positions (as many as fit in `seconds`, each seeing position + 1 keys); the estimate adds the
-    rows' mean cost per key times the T(T+1)/2 causal pairs of the sequence, times `batch`."""
+    """Prefill of T tokens (per sequence; `batch` sequences): the oracle's latent path and rebuilt keys
+    and values over all T tokens with the last row's output (one call, timed), then one call for n
+    evenly spaced query rows up to the last (n doubled until that call takes half of `seconds`): the
+    difference of the two calls is the attention of n - 1 more rows over T keys, and the estimate adds
+    that cost per (row, key) pair times the T(T+1)/2 causal pairs of the sequence, times `batch`."""
     from head_latent_attention_proj_amd import synth
     from oracle import mla as omla
 
@@ -631,25 +635,22 @@ def cpu_prefill(wbits, T, seconds, batch=1):
     t0 = time.perf_counter()
     omla.forward(x, w, rows=np.array([T - 1]), w8a8=fp8)
     t_base = time.perf_counter() - t0
-    rows = np.linspace(T // 8, T - 2, 64).astype(int)
-    n, keys, t1 = 0, 0, time.perf_counter()
-    for r in rows:
-        omla.forward(x[: r + 1], w, rows=np.array([r]), w8a8=fp8)
-        n += 1
-        keys += r + 1
-        if time.perf_counter() - t1 >= seconds:
+    n = 8
+    while True:
+        rows = np.linspace(T // 8, T - 1, n).astype(int)
+        t0 = time.perf_counter()
+        omla.forward(x, w, rows=rows, w8a8=fp8)
+        t_rows = time.perf_counter() - t0
+        if t_rows - t_base >= seconds / 2 or n >= 512:
             break
-    dt = time.perf_counter() - t1
-    # each sampled call also re-ran the latent path and kv rebuild of its r + 1 tokens: take that part
-    # out at the base call's per-token rate before estimating the per-key attention cost
-    per_tok = t_base / T
-    per_key = max(dt - per_tok * keys, 0.0) / keys
-    est = batch * (t_base + per_key * T * (T + 1) / 2)
+        n *= 2
+    per_pair = max(t_rows - t_base, 0.0) / ((n - 1) * T)
+    est = batch * (t_base + per_pair * T * (T + 1) / 2)
     what = "W8A8 " if fp8 else ""
     return _rec(batch * T / est, "tokens/s",
                 f"float64 {what}prefill of {T} tokens estimated from one call computing the kv path of all {T} "
-                f"({t_base:.1f} s) and {n} query rows sampled over positions ({dt:.1f} s), x{batch} sequences")
-
+                f"with one query row ({t_base:.1f} s) and one with {n} query rows over all {T} keys "
+                f"({t_rows:.1f} s), x{batch} sequences")
 
 if __name__ == "__main__":
     main()
