@@ -189,12 +189,21 @@ __global__ __launch_bounds__(KW * 64) void gemm_fp8_wsplit_kernel(GemmArgs p) {
 // through LDS (144-byte
 // rows: 8 consecutive rows hit 8 distinct 16-byte bank groups), double buffered.
 // ------------------------------------------------------------------------------------------
+// Stage rows of 128 bytes (one K group of codes) keep 16-byte chunk c of row r at position
+// c ^ chunk_swz(r). A lane's operand halves are chunks 2g and 2g + 1 of row l16; gfx950 serves a
+// 16-byte LDS read 16 lanes per cycle from 64 four-byte banks, those 16 lanes being the four quads
+// (lane / 4) of one half-wave whose index has one parity of its low three bits, i.e. 8 rows of each
+// of two values of g. With r's bits b1 and b3, chunk_swz = (b3, b3, b1) puts such 16 lanes on
+// distinct banks (the plain (r / 2) % 8 left every read 2-way conflicted, as the bank-conflict counter
+// showed); the stores of a row (8 consecutive lanes, 8 distinct chunks) stay conflict-free with any
+// per-row swizzle.
+MLA_DEV int chunk_swz(int r) { return (((r >> 3) & 1) * 6) | ((r >> 1) & 1); }
+
 template <int BM, int BN, int WM, int WN, int TAG, bool PREC>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, int splits, int ksplit) {
   constexpr int NT = WM * WN * 64;
   constexpr int BK = 128;  // bytes (= codes) per row per stage: one K group
-  // unpadded 128-byte stage rows, 16-byte chunk c of row r at position c ^ ((r / 2) % 8): the
-  // stores (8 lanes per row) and the operand reads meet distinct banks in every 16 lanes
+  // unpadded 128-byte stage rows, 16-byte chunk c of row r at position c ^ chunk_swz(r)
   constexpr int LDK = BK;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 
   const int lr = tid / CPR, lc = (tid % CPR) * 16;
   static_assert(CPR == 8 && RPP % 16 == 0, "swizzle: 8 chunks per row, passes of whole 16-row groups");
-  const int lcs = ((tid % CPR) ^ ((lr >> 1) & 7)) << 4;  // this thread's chunk, swizzled
+  const int lcs = ((tid % CPR) ^ chunk_swz(lr)) << 4;  // this thread's chunk, swizzled
   const uint8_t* ga[AP];
   const uint8_t* gb[BP];
 #pragma unroll
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
     // chunks 2g and 2g + 1
     const uint8_t* sA = smem + cur * (BM + BN) * LDK + (wm * WTM + l16) * LDK;
     const uint8_t* sB = smem + cur * (BM + BN) * LDK + BM * LDK + (wn * WTN + l16) * LDK;
-    const int swz = (l16 >> 1) & 7;
+    const int swz = chunk_swz(l16);
     const int c0 = ((2 * g) ^ swz) << 4, c1 = ((2 * g + 1) ^ swz) << 4;
     if constexpr (PREC) {
       // four steps of eight codes (k = g*32 + st*8 ..) widened to bf16 as they are read
@@ -495,8 +504,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fp8_tile_kernel(GemmArgs p, 
 // are in flight while the third is multiplied (the register-staged tile kernel has one stage of
 // compute to cover each load). One wave instruction fetches 8 whole rows of a block (lane l: row
 // l / 8, one 16-byte chunk), so it touches 8 cache lines; a block lands row-major, chunk c of row r
-// at position c ^ ((r / 2) % 8): a lane's operand halves (row l16, chunks 2g and 2g + 1) are then
-// read with the 16 lanes of one g on distinct banks. The row scales are fetched by one wave per 64
+// at position c ^ chunk_swz(r), where a lane's operand halves (row l16, chunks 2g and 2g + 1) are
+// read on distinct banks. The row scales are fetched by one wave per 64
 // rows. Three stages of 48.5 KB at BN = 256 (one workgroup per CU), 24.5 KB at BN = 64 (two).
 namespace ring8 {
 constexpr int BM = 128, S = 3;
@@ -578,7 +587,7 @@ __global__ __launch_bounds__(BN / 32 * 64) void gemm_fp8_ring_kernel(GemmArgs p,
   const int lr = lane >> 3;
   auto src = [&](const uint8_t* base, int64_t ld, int r0, int lim, int q) {
     const int r = q * 8 + lr;
-    return base + (int64_t)min(r0 + r, lim - 1) * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 4) + (int64_t)kg0 * 128;
+    return base + (int64_t)min(r0 + r, lim - 1) * ld + (((lane & 7) ^ chunk_swz(r)) << 4) + (int64_t)kg0 * 128;
   };
   const uint8_t* ga[APW][2];
 #pragma unroll
@@ -609,7 +618,7 @@ __global__ __launch_bounds__(BN / 32 * 64) void gemm_fp8_ring_kernel(GemmArgs p,
   // the wave's weight scales: its 64 columns lie in one 128-column block
   const float* gsb = p.b_scale + (int64_t)(min(n0 + wn * 64, p.N - 1) >> 7) * p.bs_ld + kg0;
   // operand addresses within a stage: row l16 of a block, chunk halves 2g and 2g + 1
-  const int swz = (l16 >> 1) & 7;
+  const int swz = chunk_swz(l16);
   const uint32_t oa0 = wm * 8192 + l16 * 128 + (((2 * g) ^ swz) << 4);
   const uint32_t oa1 = wm * 8192 + l16 * 128 + (((2 * g + 1) ^ swz) << 4);
   const uint32_t ob0 = A_BYTES + wn * 8192 + l16 * 128 + (((2 * g) ^ swz) << 4);
