@@ -25,8 +25,13 @@ namespace {
 
 constexpr int PQ = 128;   // queries per workgroup
 constexpr int PKB = 64;   // keys per block
-constexpr int LDK = 200;  // sK row: 192 features + pad (400 B: 8 rows -> 8 distinct bank groups)
-constexpr int LDV = 68;   // sV row: 64 keys + pad (136 B: 16 rows -> 16 distinct 8-byte slots)
+// Padded LDS rows, sized for gfx950's LDS: a 16-byte read serves 16 lanes per cycle from 64 four-byte
+// banks, namely the quads (lane / 4) of one half-wave whose index has one parity of its low three bits
+// (8 rows l16 of each of two lane groups g); an 8-byte read serves a half-wave (16 rows x 2 g) per
+// cycle. The key reads (row l16, 16 bytes at 16 g) meet distinct banks with 416-byte rows (400 left
+// them 2-way conflicted), the value reads (row l16, 8 bytes at 8 g) with 144-byte rows (136: 2-way).
+constexpr int LDK = 208;  // sK row: 192 features + pad (416 B)
+constexpr int LDV = 72;   // sV row: 64 keys + pad (144 B)
 constexpr float LOG2E = 1.4426950408889634f;
 
 MLA_DEV u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
