@@ -438,7 +438,13 @@ MLA_DEV f32x16_t mfma_bf16_32x32x16(const bf16x8_t& a, const bf16x8_t& b, const 
 // The running maximum is raised only when a block's maximum exceeds it by more than 8 (log2
 // units), so probabilities stay <= 256 and the output accumulators are rescaled rarely; the
 // decision is taken for the whole wave.
-constexpr int LDC2 = 584;  // 1168-byte rows: 16 consecutive rows start in distinct 4-bank groups
+// Staged bf16 block: unpadded 1152-byte rows, 16-byte chunk c of row r at c ^ swz2(r) (low three bits).
+// With r's bits b1..b3, swz2 = (b1 ^ b3, b2, b1) puts the score reads (rows l32 at one chunk per lane
+// half), the transposed value reads (rows 4 kg + l16 / 4 + 8 h, two chunks) and the staging writes (8
+// consecutive chunks of a row) on distinct banks under gfx950's LDS grouping (see swz); 1168-byte
+// padded rows left the value reads 2-way conflicted.
+constexpr int LDC2 = 576;
+MLA_DEV int swz2(int r) { return ((((r >> 1) ^ (r >> 3)) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 1) & 1); }
 
 __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs a) {
   using namespace mla_dims;
@@ -498,7 +504,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
 #pragma unroll
     for (int i = 0; i < 5; ++i) {  // chunks past the block go to a scratch row (no branch)
       const int c = tid + 512 * i;
-      st16(c < DKB * 72 ? sCb + (c / 72) * LDC2 + (c % 72) * 8 : sCb + DKB * LDC2 + (tid & 63) * 8, rs[i]);
+      const int row = c / 72;
+      st16(c < DKB * 72 ? sCb + row * LDC2 + (((c % 72) ^ swz2(row)) << 3) : sCb + DKB * LDC2 + (tid & 63) * 8, rs[i]);
     }
   };
   u32x4_t rA[5], rB[5];
@@ -558,11 +565,16 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     // partial S^T[pos][head] over this wave's 144 features (two chains, added at the end)
     f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
     {
-      const uint16_t* ap = sCb + l32 * LDC2 + 144 * fq + 8 * kg;
+      // step ks reads chunk 18 fq + kg + 2 ks of row l32: one per-lane base for each ks mod 4 (the
+      // swizzle changes the low three bits only) plus 8 chunks per 4 steps
+      const int sw = swz2(l32);
+      const uint16_t* ap[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ap[m] = sCb + l32 * LDC2 + (((18 * fq + kg + 2 * m) ^ sw) << 3);
 #pragma unroll
       for (int ks = 0; ks < 9; ks += 2) {
-        s0 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap + 16 * ks)), qf[ks], s0);
-        if (ks + 1 < 9) s1 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap + 16 * ks + 16)), qf[ks + 1], s1);
+        s0 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap[ks & 3] + 64 * (ks >> 2))), qf[ks], s0);
+        if (ks + 1 < 9) s1 = mfma_bf16_32x32x16(as_bf16x8(ld16(ap[(ks + 1) & 3] + 64 * ((ks + 1) >> 2))), qf[ks + 1], s1);
       }
     }
     const f32x16_t sacc = s0 + s1;
@@ -616,14 +628,24 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
                                  pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]), pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7])});
 
     // O^T[feature][head] over this wave's 128 latent features: 4 tiles x 2 position steps
+    // lane (r, cc, kg) reads row 4 kg + r / 4 (+ 8, + 16 ks), feature 128 fq + cc + 4 (r % 4) + 32 t: chunk
+    // 16 fq + cc / 8 + (r % 4) / 2 + 4 t at element 4 (r % 2) of it. Bases per (t mod 2, +8 rows): the
+    // swizzle of row + 16 ks is that of row, t / 2 moves by 8 chunks.
     const int r = lane & 15, cc = 16 * ((lane >> 4) & 1);
-    const uint16_t* tp = sCb + (4 * kg + (r >> 2)) * LDC2 + 128 * fq + cc + 4 * (r & 3);
+    const uint16_t* tp[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 4 * kg + (r >> 2) + 8 * h;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        tp[tt][h] = sCb + row * LDC2 + 128 * fq + ((((cc >> 3) + ((r & 3) >> 1) + 4 * tt) ^ swz2(row)) << 3) + 4 * (r & 1);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t* p0 = tp + 16 * ks * LDC2 + 32 * t;
-        const u32x2_t w0 = ds_read_tr16(p0), w1 = ds_read_tr16(p0 + 8 * LDC2);
+        const u32x2_t w0 = ds_read_tr16(tp[t & 1][0] + 16 * ks * LDC2 + 64 * (t >> 1));
+        const u32x2_t w1 = ds_read_tr16(tp[t & 1][1] + 16 * ks * LDC2 + 64 * (t >> 1));
         o[t] = mfma_bf16_32x32x16(as_bf16x8(u32x4_t{w0[0], w0[1], w1[0], w1[1]}), pf[ks], o[t]);
       }
   };
