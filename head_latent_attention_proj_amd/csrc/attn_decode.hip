@@ -285,7 +285,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
       else qk_half(std::integral_constant<int, 1>{});
     }
     // add the other half's partial scores (same order in both waves of a pair)
-    // 16-byte LDS accesses on 48-byte lane rows (eight lanes of one LDS cycle in distinct banks)
+    // 16-byte LDS accesses on 48-byte lane rows: distinct banks for the writes (8 consecutive lanes
+    // per cycle) and the reads (16 lanes per cycle)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) *reinterpret_cast<f32x4_t*>(&xS[wave][lane][4 * kt]) = sacc[kt];
     __syncthreads();
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
   // the same bytes stage the output rows
   constexpr int SC_ELEMS = (DKB + 1) * LDC2;
   constexpr int SC_BYTES = 2 * SC_ELEMS * 2;
-  constexpr int XSL = 20;  // floats per lane in the score exchange: 16 + 4 (80-byte rows: the
-                           // eight lanes of one 128-byte LDS cycle hit distinct banks)
+  constexpr int XSL = 20;  // floats per lane in the score exchange: 16 + 4 (80-byte rows: distinct
+                           // banks for the 16-byte writes and reads)
   constexpr int XS_BYTES = 8 * 64 * XSL * 4;
   constexpr int ST_LD = 256 + 4;  // staged half row: 256 floats + 16 bytes
   static_assert(SC_BYTES % 16 == 0 && 64 * ST_LD * 4 <= SC_BYTES + XS_BYTES, "LDS carve-up");
