@@ -630,18 +630,47 @@ __global__ __launch_bounds__(64 * NWV) void gemm_head_kernel(GemmArgs p) {
         // chunks i = 0 .. 3 are rows tid / 64 + 8 i (< 32), chunks i + 4 their residual rows
         static_assert(PER == 8 && CH == 64, "merge staging layout");
         const float* Po = (const float*)p.A;
+        // the first two splits of every row are loaded at once (split 1 clamped to the array; its
+        // values are used only where the row has it), further splits afterwards (rare): the common
+        // case costs the sequence-length lookup and one round of loads instead of a chain per split
+        const int sp1 = min(1, p.mg_max_splits - 1);
+        int ns[PER / 2];
+        int64_t q0[PER / 2];
+        f32x2_t ml[PER / 2][2];
+        f32x4_t ov[PER / 2][2][2];
 #pragma unroll
         for (int i = 0; i < PER / 2; ++i) {
           const int c = tid + NT * i, row = c / CH, ch = c % CH;
           const int b = m0 + min(row, mrows - 1);
-          const int ns = cdiv(p.mg_len[p.mg_seq[b]], p.mg_chunk);
-          const int64_t q0 = (int64_t)b * p.mg_max_splits * 64 + batch;  // (b, split 0, head)
-          float mx = -INFINITY;
-          for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, p.mg_ml[(q0 + (int64_t)sp * 64) * 2]);
-          float l = 0.f;
-          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-          for (int sp = 0; sp < ns; ++sp) {
-            const int64_t q = q0 + (int64_t)sp * 64;
+          ns[i] = cdiv(p.mg_len[p.mg_seq[b]], p.mg_chunk);
+          q0[i] = (int64_t)b * p.mg_max_splits * 64 + batch;  // (b, split 0, head)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int64_t q = q0[i] + (int64_t)(u ? sp1 : 0) * 64;
+            ml[i][u] = *reinterpret_cast<const f32x2_t*>(p.mg_ml + q * 2);
+            const float* src = Po + q * 512 + ch * 8;
+            ov[i][u][0] = *reinterpret_cast<const f32x4_t*>(src);
+            ov[i][u][1] = *reinterpret_cast<const f32x4_t*>(src + 4);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < PER / 2; ++i) {
+          const int ch = (tid + NT * i) % CH;
+          float mx = ml[i][0][0];
+          if (ns[i] > 1) mx = fmaxf(mx, ml[i][1][0]);
+          for (int sp = 2; sp < ns[i]; ++sp) mx = fmaxf(mx, p.mg_ml[(q0[i] + (int64_t)sp * 64) * 2]);
+          // splits added in order: 0, 1, then the rest
+          const float w0 = exp2f(ml[i][0][0] - mx);
+          float l = w0 * ml[i][0][1];
+          f32x4_t a0 = ov[i][0][0] * w0, a1 = ov[i][0][1] * w0;
+          if (ns[i] > 1) {
+            const float w1 = exp2f(ml[i][1][0] - mx);
+            l += w1 * ml[i][1][1];
+            a0 += ov[i][1][0] * w1;
+            a1 += ov[i][1][1] * w1;
+          }
+          for (int sp = 2; sp < ns[i]; ++sp) {
+            const int64_t q = q0[i] + (int64_t)sp * 64;
             const float w = exp2f(p.mg_ml[q * 2] - mx);
             l += w * p.mg_ml[q * 2 + 1];
             const float* src = Po + q * 512 + ch * 8;
