@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "splitk.h"
 
 namespace mla_k {
 
@@ -856,41 +857,6 @@ __global__ __launch_bounds__(256) void splitk_reduce8_kernel(GemmArgs p, int spl
   epi_store8(p, b, (int)(idx / p.N), (int)(idx % p.N), s);
 }
 
-// The same reduction four columns per thread (float32 or bf16 output, aligned rows; see reduce8_vec_ok):
-// 16-byte loads of every part, one vector store.
-template <int TAG>
-__global__ __launch_bounds__(256) void splitk_reduce8_vec_kernel(GemmArgs p, int splits) {
-  const int64_t mn = (int64_t)p.M * p.N;
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const int b = blockIdx.y;
-  if (idx >= mn) return;
-  const float* base = p.part + (int64_t)b * splits * mn + idx;
-  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(base + sp * mn);
-  const int m = (int)(idx / p.N), n = (int)(idx % p.N);
-  const int64_t ci = b * p.sC + (int64_t)m * p.ldc + n;
-  if (p.epi == EPI_F32) {
-    *reinterpret_cast<f32x4_t*>((float*)p.C + ci) = s;
-  } else {
-    if (p.resid) {
-      const u32x2_t r = *reinterpret_cast<const u32x2_t*>(p.resid + (int64_t)m * p.ldr + n);
-      s[0] += __uint_as_float(r[0] << 16);
-      s[1] += __uint_as_float(r[0] & 0xffff0000u);
-      s[2] += __uint_as_float(r[1] << 16);
-      s[3] += __uint_as_float(r[1] & 0xffff0000u);
-    }
-    *reinterpret_cast<u32x2_t*>((uint16_t*)p.C + ci) = u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-  }
-}
-
-bool reduce8_vec_ok(const GemmArgs& a) {
-  auto al = [](const void* q, uintptr_t n) { return (reinterpret_cast<uintptr_t>(q) & (n - 1)) == 0; };
-  if ((a.N & 3) || (a.ldc & 3) || (a.sC & 3)) return false;
-  if (a.epi == EPI_F32) return al(a.C, 16);
-  if (a.epi == EPI_BF16) return al(a.C, 8) && (!a.resid || (al(a.resid, 8) && (a.ldr & 3) == 0));
-  return false;
-}
-
 struct Plan8 {
   int kind;  // 0 wsplit, 1 tile 128 x 128, 2 tile 128 x 256, 3 tile 128 x 64
   int mt, kw, ysplit;
@@ -1033,9 +999,9 @@ void launch_fp8_tagged(const GemmArgs& a, const Plan8& pl, hipStream_t s) {
     hipLaunchKernelGGL((gemm_fp8_tile_kernel<128, 256, 2, 4, TAG, PREC>), grid, dim3(512), 0, s, a, pl.splits,
                        pl.ksplit);
   if (pl.splits > 1 && pl.ysplit == 1) {
-    if (reduce8_vec_ok(a)) {
+    if (reduce_vec_ok(a)) {
       dim3 rgrid((unsigned)(((int64_t)a.M * a.N / 4 + 255) / 256), a.batch);
-      hipLaunchKernelGGL((splitk_reduce8_vec_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
+      hipLaunchKernelGGL((splitk_reduce_vec_kernel<TAG, false>), rgrid, dim3(256), 0, s, a, pl.splits);
     } else {
       dim3 rgrid((unsigned)(((int64_t)a.M * a.N + 255) / 256), a.batch);
       hipLaunchKernelGGL((splitk_reduce8_kernel<TAG>), rgrid, dim3(256), 0, s, a, pl.splits);
