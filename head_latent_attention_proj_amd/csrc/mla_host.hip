@@ -23,7 +23,7 @@ using namespace mla_dims;
 // array, one copy per GPU the library runs on, held until the process ends. In host code the
 // name `scratch` is only a host-side stand-in; kernels receive the device address obtained from
 // hipGetSymbolAddress for the current device.
-constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)128 << 20;
 static_assert(STATIC_SCRATCH_BYTES == MLA_STATIC_SCRATCH_BYTES, "header and library agree on the size");
 static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
 

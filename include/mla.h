@@ -211,17 +211,19 @@ mla_status mla_decode(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, 
 /* ---- Decode without any allocation, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments,
  * semantics, validation and errors as mla_decode, minus the workspace: the call uses a
- * workspace inside the library, a static device array of MLA_STATIC_SCRATCH_BYTES (64 MiB) that
+ * workspace inside the library, a static device array of MLA_STATIC_SCRATCH_BYTES (128 MiB) that
  * every GPU the library runs on holds once, from the first call on that device (or
  * mla_init_weights there) until the process ends. It calls no hipMalloc/hipFree and no
  * allocating routine.
- * Limit: a step whose workspace would exceed MLA_STATIC_SCRATCH_BYTES (what
- * mla_decode_workspace_bytes reports for its B and positions, e.g. more than about 400 bf16
- * splits of 64 heads x 512 features) returns MLA_E_WORKSPACE before anything is enqueued.
+ * Limit: the step's own workspace, from its B and the lengths its sequences reach (at most what
+ * mla_decode_workspace_bytes reports, which bounds every split plan), must fit
+ * MLA_STATIC_SCRATCH_BYTES, else the call returns MLA_E_WORKSPACE before anything is enqueued.
+ * Measured needs: FP8, 128 sequences of 16384 positions: 124.7 MiB (fits); bf16, 64 sequences of
+ * 1024..8192: 116.8 MiB (fits); bf16, 1000 sequences of one position: more (rejected).
  * All calls on one GPU share that GPU's array and it keeps the last call's values: two calls that
  * may overlap on one GPU (different streams or threads without ordering) race and must not be
  * issued; calls in stream order are safe. Nothing in the array needs clearing between calls. */
-#define MLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 mla_status mla_decode_static(mla_ctx* ctx, mla_cache* cache, const int32_t* seq_ids_h, const int32_t* seq_ids_d,
                              int32_t B, const void* x, void* y, mla_stream stream);
 

@@ -4,7 +4,8 @@ cannot allocate) against mla_decode on identical caches, through the C ABI.
 Two calls in a row on the same caches, the second with fewer sequences and a shorter step
 (so the scratch still holds the first call's larger values): outputs bit-identical to
 mla_decode's and within the parity bar of the float64 oracle, cache bytes and lengths identical.
-Also the FP8 layer, and a step too large for the scratch, which is rejected before anything runs.
+Also the FP8 layer (at 128 sequences of 16384 positions too), and a step too large for the scratch,
+which is rejected before anything runs.
 """
 import numpy as np
 import pytest
@@ -80,14 +81,42 @@ def test_static_decode_matches_decode_fp8():
         assert torch.equal(ca.data, cb.data) and ca.len_h.tolist() == cb.len_h.tolist()
 
 
+def test_static_decode_fp8_128_sequences_of_16384():
+    """The FP8 decode step at its full size (128 sequences of 16384 cached positions, 124.7 MiB of
+    workspace) fits the scratch; then 64 of those sequences in another order."""
+    import torch
+
+    from test_gpu_fp8 import fp8_setup
+
+    B, P = 128, 16384
+    log(f"static-scratch decode vs mla_decode, FP8, {B} x {P}, then 64 sequences")
+    wq, _, _ = fp8_setup()
+    L = binding.Layer(binding.weights_to_device(wq), max_positions=P + 8, wdtype=binding.WDTYPE_FP8)
+    base = torch.from_numpy(synth.make_cache_entries_fp8(P, seed=8500)).cuda()
+    ca, cb = (binding.Cache(L, [P + 3] * B, fill_byte=0x55) for _ in range(2))
+    for s in range(B):
+        ents = torch.roll(base, shifts=97 * s, dims=0).contiguous()  # a different cache per sequence
+        for c in (ca, cb):
+            L.cache_append(c, s, ents)
+    del base
+    for k, order in enumerate([np.arange(B, dtype=np.int32), np.arange(B - 1, -1, -2, dtype=np.int32)]):
+        x = binding.bf16_tensor(synth.make_hidden(len(order), seed=8600 + k))
+        ya = L.decode(ca, order, x)
+        yb = L.decode_static(cb, order, x)
+        torch.cuda.synchronize()
+        assert np.array_equal(binding.tensor_to_bf16_bits(ya), binding.tensor_to_bf16_bits(yb)), f"call {k}: outputs differ"
+        assert torch.equal(ca.data, cb.data) and ca.len_h.tolist() == cb.len_h.tolist(), f"call {k}: caches differ"
+        assert bool(torch.isfinite(yb.float()).all())
+
+
 def test_static_decode_rejects_a_step_larger_than_its_scratch():
     import torch
 
     B = 1000
-    log(f"static-scratch decode: {B} sequences need more than the 64 MiB scratch")
+    log(f"static-scratch decode: {B} sequences need more than the 128 MiB scratch")
     L = layer()
     need = L.decode_workspace_bytes(B, B)
-    assert need > 64 << 20
+    assert need > 128 << 20
     cache = binding.Cache(L, [1] * B, fill_byte=0x3C)
     x = binding.bf16_tensor(synth.make_hidden(B, seed=8400))
     with pytest.raises(binding.MlaError) as ei:
