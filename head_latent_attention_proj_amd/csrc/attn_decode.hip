@@ -161,8 +161,8 @@ __global__ __launch_bounds__(512, 1) void decode_attn_fp8_kernel(DecodeAttnArgs 
   // block re-read the last block (never staged): every loop trip then issues the same loads, so the
   // compiler's wait before a set is used covers that set only, not the sets issued after it.
   gload(0, std::integral_constant<int, 0>{});
-  if constexpr (FP8_AHEAD > 1) gload(min(1, nblk - 1), std::integral_constant<int, 1>{});
-  if constexpr (FP8_AHEAD > 2) gload(min(2, nblk - 1), std::integral_constant<int, 2>{});
+  if constexpr (FP8_AHEAD > 1) gload(min(1, nblk - 1), std::integral_constant<int, 1 % FP8_AHEAD>{});
+  if constexpr (FP8_AHEAD > 2) gload(min(2, nblk - 1), std::integral_constant<int, 2 % FP8_AHEAD>{});
 
   // ---- query fragments (B operand), fp16: column = head, features lh*288 + ks*32 + g*8 .. +7;
   // the latent part is the absorbed product (or the sum of two float32 parts), features >= 512 are the rotary
